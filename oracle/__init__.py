@@ -1,0 +1,9 @@
+"""CPU oracle for the paged KV cache hot path (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python
+binding) never does, and this package imports nothing from it.
+"""
+from .attention import (widen, kv_cache_write, gather_kv, attention_seq_kvhead,  # noqa: F401
+                        paged_attention, merge_partials, split_attention, block_bytes,
+                        blocks_for_tokens)

@@ -1,0 +1,385 @@
+"""Seeded synthetic inputs for paged attention.
+
+This module only builds inputs: sequence lengths, a shuffled pool of KV
+blocks, block tables, slot mappings and normally distributed q/K/V values.
+It performs none of the attention arithmetic, so both the CPU oracle and the
+GPU path can consume the same arrays.
+
+Conventions (taken from the vLLM pages):
+  * KV cache per layer: separate K and V tensors shaped
+    [num_blocks, block_size, num_kv_heads, head_size]
+    (vLLM book, ch. 6, "Transformation de la disposition mémoire du KV cache").
+  * A block table row lists a sequence's physical block ids; padding entries
+    hold the null block id 0, and block 0 is reserved and never holds data
+    (vLLM book, ch. 5.2, "slot_mapping et la block table"; ch. 4.1).
+  * A sequence of L tokens owns ceil(L / block_size) blocks
+    ("Khám phá vLLM", "Scheduler", the allocate_slots example).
+  * slot_mapping[t] = physical_block * block_size + offset, int64, -1 marks a
+    padded token that must not be written (vLLM book, ch. 5.2).
+
+Random recipe (all integer draws inclusive):
+  root = SeedSequence(seed); one metadata stream drawn from root draws the
+  lengths and then the block permutation; spawned child streams draw q and,
+  per sequence, that sequence's K then V values; C5 uses one more child for
+  the new tokens' K, V and q. Values are standard_normal(float32) * sigma,
+  rounded to bfloat16 by round-to-nearest-even for bf16 workloads.
+Every cache slot that holds no valid token (block 0, spare pool blocks, the
+tail of each sequence's last block) is filled with a quiet NaN.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import numpy as np
+
+BF16_QNAN = np.uint16(0x7FC0)
+F32_QNAN_BITS = np.uint32(0x7FC00000)
+
+# Threads used to draw the per-sequence K/V streams.  The result does not
+# depend on this number: every sequence has its own stream.
+_GEN_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16 high bits as uint16.  NaN inputs map to a quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = BF16_QNAN
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One attention-layer step: cache contents, metadata and queries.
+
+    Floating-point arrays are float32 for dtype 'f32' and raw bfloat16 bits
+    (uint16) for dtype 'bf16'.
+    """
+    name: str
+    dtype: str                       # 'f32' | 'bf16'
+    num_heads: int
+    num_kv_heads: int
+    head_size: int
+    block_size: int
+    scale: float
+    causal: bool
+    q: np.ndarray                    # [num_q_rows, num_heads, head_size]
+    k_cache: np.ndarray              # [num_blocks, block_size, num_kv_heads, head_size]
+    v_cache: np.ndarray
+    block_tables: np.ndarray         # int32 [num_seqs, max_blocks]
+    seq_lens: np.ndarray             # int32 [num_seqs], context + query tokens
+    cu_seqlens_q: Optional[np.ndarray] = None   # int32 [num_seqs + 1]; None = decode (one row per seq)
+    key_new: Optional[np.ndarray] = None        # [num_new, num_kv_heads, head_size]
+    value_new: Optional[np.ndarray] = None
+    slot_mapping: Optional[np.ndarray] = None   # int64 [num_new]
+    partition_size: int = 0          # 0 = library default
+    sigma: float = 1.0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        if self.cu_seqlens_q is None:
+            return np.ones(self.num_seqs, dtype=np.int32)
+        return np.diff(self.cu_seqlens_q).astype(np.int32)
+
+    @property
+    def max_query_len(self) -> int:
+        ql = self.query_lens
+        return int(ql.max()) if ql.size else 0
+
+    @property
+    def num_q_rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def kv_block_bytes(self) -> int:
+        """Bytes of one block of one layer, K and V together (2 * bs * Hkv * D * e)."""
+        return 2 * self.block_size * self.num_kv_heads * self.head_size * self.elem_bytes
+
+    def valid_slot_mask(self) -> np.ndarray:
+        """bool [num_blocks, block_size]: True where the cache holds a token that
+        attention may read after the new tokens (if any) have been written."""
+        m = np.zeros((self.num_blocks, self.block_size), dtype=bool)
+        bs = self.block_size
+        for s in range(self.num_seqs):
+            L = int(self.seq_lens[s])
+            pos = np.arange(L)
+            m[self.block_tables[s, pos // bs], pos % bs] = True
+        return m
+
+
+def _poison(shape, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.full(shape, F32_QNAN_BITS, dtype=np.uint32).view(np.float32)
+    return np.full(shape, BF16_QNAN, dtype=np.uint16)
+
+
+def _draw(rng: np.random.Generator, n: int, sigma: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(n, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def blocks_needed(seq_len: int, block_size: int) -> int:
+    return -(-int(seq_len) // int(block_size))
+
+
+def build_pool(seq_lens, block_size: int, rng: np.random.Generator,
+               num_blocks: Optional[int] = None, extra_frac: float = 0.10):
+    """Shuffle physical block ids 1..num_blocks-1 and hand them out to the
+    sequences in order.  Returns (num_blocks, block_tables int32)."""
+    nb = [blocks_needed(L, block_size) for L in seq_lens]
+    total = int(sum(nb))
+    if num_blocks is None:
+        num_blocks = 1 + int(math.ceil((1.0 + extra_frac) * total))
+    if num_blocks - 1 < total:
+        raise ValueError(f"pool of {num_blocks} blocks cannot hold {total} blocks")
+    perm = rng.permutation(np.arange(1, num_blocks, dtype=np.int64))
+    max_blocks = max(nb) if nb else 0
+    bt = np.zeros((len(seq_lens), max(max_blocks, 1)), dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(nb):
+        bt[s, :n] = perm[pos:pos + n]
+        pos += n
+    return num_blocks, bt
+
+
+def slots_of(block_table_row: np.ndarray, positions: np.ndarray, block_size: int) -> np.ndarray:
+    """Flat slot ids (block * block_size + offset) of token positions."""
+    positions = np.asarray(positions, dtype=np.int64)
+    return block_table_row[positions // block_size].astype(np.int64) * block_size + positions % block_size
+
+
+def _fill_cache(k_cache, v_cache, block_tables, fill_lens, block_size, child_seeds, sigma, dtype):
+    """Write fill_lens[s] leading tokens of every sequence into the pool,
+    K then V, each sequence from its own stream."""
+    Hkv, D = k_cache.shape[2], k_cache.shape[3]
+    kf = k_cache.reshape(-1, Hkv, D)
+    vf = v_cache.reshape(-1, Hkv, D)
+    chunk_tokens = max(1, (1 << 22) // (Hkv * D))
+
+    def one(s):
+        L = int(fill_lens[s])
+        if L <= 0:
+            return
+        rng = np.random.Generator(np.random.PCG64(child_seeds[s]))
+        for cache in (kf, vf):
+            for t0 in range(0, L, chunk_tokens):
+                t1 = min(L, t0 + chunk_tokens)
+                vals = _draw(rng, (t1 - t0) * Hkv * D, sigma, dtype).reshape(t1 - t0, Hkv, D)
+                cache[slots_of(block_tables[s], np.arange(t0, t1), block_size)] = vals
+
+    if len(fill_lens) > 1 and _GEN_THREADS > 1:
+        with _cf.ThreadPoolExecutor(_GEN_THREADS) as ex:
+            list(ex.map(one, range(len(fill_lens))))
+    else:
+        for s in range(len(fill_lens)):
+            one(s)
+
+
+def make_decode(name, seq_lens, num_heads, num_kv_heads, head_size, block_size, dtype,
+                seed, sigma=1.0, num_blocks=None, partition_size=0, meta_rng=None,
+                root=None) -> Workload:
+    """Decode step: one query row per sequence; the cache already holds all
+    seq_lens[s] tokens (the current token included)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    if root is None:
+        root = np.random.SeedSequence(seed)
+    if meta_rng is None:
+        meta_rng = np.random.Generator(np.random.PCG64(root))
+    num_blocks, bt = build_pool(seq_lens, block_size, meta_rng, num_blocks)
+    children = root.spawn(1 + len(seq_lens))
+    q_rng = np.random.Generator(np.random.PCG64(children[0]))
+    q = _draw(q_rng, len(seq_lens) * num_heads * head_size, sigma, dtype).reshape(
+        len(seq_lens), num_heads, head_size)
+    shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_cache = _poison(shape, dtype)
+    v_cache = _poison(shape, dtype)
+    _fill_cache(k_cache, v_cache, bt, seq_lens, block_size, children[1:], sigma, dtype)
+    return Workload(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                    head_size=head_size, block_size=block_size, scale=1.0 / math.sqrt(head_size),
+                    causal=False, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=bt,
+                    seq_lens=seq_lens, partition_size=partition_size, sigma=sigma)
+
+
+def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_size, block_size,
+                dtype, seed, sigma=1.0, causal=True, num_blocks=None, partition_size=0,
+                meta_rng=None, root=None) -> Workload:
+    """Mixed step: sequence s has context_lens[s] tokens already cached and
+    query_lens[s] new tokens whose K/V must first be scattered through
+    slot_mapping; seq_lens = context + query."""
+    context_lens = np.asarray(context_lens, dtype=np.int64)
+    query_lens = np.asarray(query_lens, dtype=np.int64)
+    seq_lens = (context_lens + query_lens).astype(np.int32)
+    if root is None:
+        root = np.random.SeedSequence(seed)
+    if meta_rng is None:
+        meta_rng = np.random.Generator(np.random.PCG64(root))
+    num_blocks, bt = build_pool(seq_lens, block_size, meta_rng, num_blocks)
+    S = len(seq_lens)
+    children = root.spawn(2 + S)
+    shape = (num_blocks, block_size, num_kv_heads, head_size)
+    k_cache = _poison(shape, dtype)
+    v_cache = _poison(shape, dtype)
+    _fill_cache(k_cache, v_cache, bt, context_lens, block_size, children[2:], sigma, dtype)
+    T = int(query_lens.sum())
+    new_rng = np.random.Generator(np.random.PCG64(children[1]))
+    key_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, dtype).reshape(T, num_kv_heads, head_size)
+    value_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, dtype).reshape(T, num_kv_heads, head_size)
+    q = _draw(new_rng, T * num_heads * head_size, sigma, dtype).reshape(T, num_heads, head_size)
+    cu = np.zeros(S + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(query_lens)
+    slot = np.empty(T, dtype=np.int64)
+    for s in range(S):
+        pos = np.arange(context_lens[s], seq_lens[s])
+        slot[cu[s]:cu[s + 1]] = slots_of(bt[s], pos, block_size)
+    return Workload(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                    head_size=head_size, block_size=block_size, scale=1.0 / math.sqrt(head_size),
+                    causal=causal, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=bt,
+                    seq_lens=seq_lens, cu_seqlens_q=cu, key_new=key_new, value_new=value_new,
+                    slot_mapping=slot, partition_size=partition_size, sigma=sigma)
+
+
+# --------------------------------------------------------------------------
+# The five workloads.  `scale_down` shrinks batch and lengths for parity runs
+# while keeping head shapes, block size, dtype and length distribution shape.
+# --------------------------------------------------------------------------
+
+CONFIG_NAMES = {
+    1: "tiny_mha_decode_f32",
+    2: "llama7b_mha_decode_bf16",
+    3: "gqa_decode_bf16",
+    4: "long_context_splitkv_decode_bf16",
+    5: "mixed_chunked_prefill_decode_bf16",
+}
+
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4}
+
+
+def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
+    """Sequence lengths of a workload, drawn from the metadata stream."""
+    if cfg == 1:
+        n = num_seqs or 4
+        return rng.integers(1, min(256, max_len or 256), size=n, endpoint=True)
+    if cfg == 2:
+        n = num_seqs or 64
+        hi = min(4096, max_len or 4096)
+        return rng.integers(min(200, hi), hi, size=n, endpoint=True)
+    if cfg == 3:
+        n = num_seqs or 256
+        z = rng.standard_normal(n)
+        L = np.rint(np.exp(math.log(1024.0) + 0.8 * z))
+        return np.clip(L, 16, min(8192, max_len or 8192)).astype(np.int64)
+    if cfg == 4:
+        n = num_seqs or 8
+        hi = min(131072, max_len or 131072)
+        return rng.integers(min(32768, hi // 4), hi, size=n, endpoint=True)
+    raise ValueError(cfg)
+
+
+def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
+                max_len: Optional[int] = None, num_chunks: Optional[int] = None,
+                chunk_len: Optional[int] = None) -> Workload:
+    """Build workload `cfg` (1..5).  num_seqs / max_len / num_chunks /
+    chunk_len shrink it for quick parity runs; None keeps the full size."""
+    if seed is None:
+        seed = DEFAULT_SEEDS[cfg]
+    root = np.random.SeedSequence(seed)
+    meta = np.random.Generator(np.random.PCG64(root))
+    name = CONFIG_NAMES[cfg]
+    if cfg == 1:
+        L = config_lengths(1, meta, num_seqs, max_len)
+        return make_decode(name, L, 8, 8, 64, 16, "f32", seed, num_blocks=128,
+                           meta_rng=meta, root=root)
+    if cfg == 2:
+        L = config_lengths(2, meta, num_seqs, max_len)
+        return make_decode(name, L, 32, 32, 128, 16, "bf16", seed, meta_rng=meta, root=root)
+    if cfg == 3:
+        L = config_lengths(3, meta, num_seqs, max_len)
+        return make_decode(name, L, 32, 8, 128, 16, "bf16", seed, meta_rng=meta, root=root)
+    if cfg == 4:
+        L = config_lengths(4, meta, num_seqs, max_len)
+        return make_decode(name, L, 64, 8, 128, 16, "bf16", seed, sigma=0.5,
+                           partition_size=512, meta_rng=meta, root=root)
+    if cfg == 5:
+        nc = 4 if num_chunks is None else num_chunks
+        cl = 512 if chunk_len is None else chunk_len
+        nd = 128 if num_seqs is None else num_seqs
+        ctx_hi = 4096 if max_len is None else min(4096, max_len)
+        dec_hi = 4096 if max_len is None else min(4096, max_len)
+        ctx = meta.integers(0, ctx_hi, size=nc, endpoint=True)
+        dec_L = meta.integers(min(64, dec_hi), dec_hi, size=nd, endpoint=True)
+        context = np.concatenate([ctx, dec_L - 1]).astype(np.int64)
+        qlens = np.concatenate([np.full(nc, cl), np.ones(nd)]).astype(np.int64)
+        return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16", seed, causal=True,
+                           meta_rng=meta, root=root)
+    raise ValueError(cfg)
+
+
+# --------------------------------------------------------------------------
+# Algorithmic byte and flop counts (what the method must move / compute).
+# --------------------------------------------------------------------------
+
+def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
+    """KV bytes of every valid token read once, plus q, out, block-table
+    entries and seq_lens; for a mixed step also the new K/V read and written
+    and the slot_mapping read."""
+    e = w.elem_bytes
+    L = w.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * e
+    qo = 2 * w.num_q_rows * w.num_heads * w.head_size * e
+    meta = 4 * int(sum(blocks_needed(x, w.block_size) for x in L)) + 4 * w.num_seqs
+    if w.cu_seqlens_q is not None:
+        meta += 4 * (w.num_seqs + 1)
+    total = kv + qo + meta
+    if include_write and w.slot_mapping is not None:
+        T = int(w.slot_mapping.shape[0])
+        total += 2 * 2 * T * w.num_kv_heads * w.head_size * e + 8 * T
+    return total
+
+
+def attention_flops(w: Workload) -> int:
+    """2 flops per multiply-add over QK^T and PV for the scores each query
+    row actually uses (causal rows stop at their own position)."""
+    ql = w.query_lens.astype(np.int64)
+    L = w.seq_lens.astype(np.int64)
+    total = 0
+    for s in range(w.num_seqs):
+        if w.causal and w.cu_seqlens_q is not None:
+            ctx = L[s] - ql[s]
+            keys = int(ql[s] * ctx + ql[s] * (ql[s] + 1) // 2)
+        else:
+            keys = int(ql[s] * L[s])
+        total += 4 * w.num_heads * w.head_size * keys
+    return total

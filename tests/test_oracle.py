@@ -1,0 +1,452 @@
+"""Pins for the CPU oracle: each test checks the oracle against something
+other than itself (brute force, closed forms, invariants, a library routine,
+facts printed on the pages)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_50_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+# ---------------------------------------------------------------- helpers
+
+def brute_attention(Q, K, V, scale, causal):
+    """Pure-Python attention on contiguous K/V (no pool, no numpy math).
+    Q: list[q_len][D], K/V: list[L][D].  Row i sees keys j <= i + L - q_len
+    when causal."""
+    q_len, L = len(Q), len(K)
+    outs, lses = [], []
+    for i in range(q_len):
+        lim = i + L - q_len if causal else L - 1
+        keys = [j for j in range(L) if j <= lim]
+        if not keys:
+            outs.append([0.0] * len(V[0]) if V else [])
+            lses.append(-math.inf)
+            continue
+        s = [scale * sum(a * b for a, b in zip(Q[i], K[j])) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        tot = sum(e)
+        o = [sum(e[n] * V[keys[n]][d] for n in range(len(keys))) / tot for d in range(len(V[0]))]
+        outs.append(o)
+        lses.append(m + math.log(tot))
+    return outs, lses
+
+
+def tiny_pool(rng, seq_lens, Hkv, D, bs, dtype="f32", extra=3):
+    """Random contiguous per-sequence K/V plus the same data scattered into a
+    shuffled pool.  Returns (Kc, Vc, bt, Kseq, Vseq)."""
+    nb = [-(-L // bs) for L in seq_lens]
+    num_blocks = 1 + sum(nb) + extra
+    perm = rng.permutation(np.arange(1, num_blocks))
+    bt = np.zeros((len(seq_lens), max(max(nb), 1)), dtype=np.int32)
+    Kc = np.full((num_blocks, bs, Hkv, D), np.nan, dtype=np.float32)
+    Vc = np.full_like(Kc, np.nan)
+    Kseq, Vseq = [], []
+    p = 0
+    for s, L in enumerate(seq_lens):
+        bt[s, :nb[s]] = perm[p:p + nb[s]]
+        p += nb[s]
+        K = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+        V = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+        for j in range(L):
+            Kc[bt[s, j // bs], j % bs] = K[j]
+            Vc[bt[s, j // bs], j % bs] = V[j]
+        Kseq.append(K)
+        Vseq.append(V)
+    return Kc, Vc, bt, Kseq, Vseq
+
+
+def repack(Kc, bt, seq_lens, bs_old, bs_new, rng, Vc=None):
+    """Store the same logical tokens in a fresh shuffled pool with another
+    block size."""
+    Hkv, D = Kc.shape[2], Kc.shape[3]
+    nb = [-(-L // bs_new) for L in seq_lens]
+    num_blocks = 1 + sum(nb) + 2
+    perm = rng.permutation(np.arange(1, num_blocks))
+    bt2 = np.zeros((len(seq_lens), max(max(nb), 1)), dtype=np.int32)
+    out = []
+    for cache in (Kc, Vc):
+        c2 = np.full((num_blocks, bs_new, Hkv, D), np.nan, dtype=cache.dtype)
+        out.append(c2)
+    p = 0
+    for s, L in enumerate(seq_lens):
+        bt2[s, :nb[s]] = perm[p:p + nb[s]]
+        p += nb[s]
+        for j in range(L):
+            for c_old, c_new in zip((Kc, Vc), out):
+                c_new[bt2[s, j // bs_new], j % bs_new] = c_old[bt[s, j // bs_old], j % bs_old]
+    return out[0], out[1], bt2
+
+
+# ---------------------------------------------------------------- P-brute
+
+@pytest.mark.parametrize("bs", [4, 8, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_matches_bruteforce(bs, causal):
+    rng = np.random.default_rng(100 + bs + 7 * causal)
+    Hq, Hkv, D = 4, 2, 8
+    seq_lens = [1, 5, 17, 40]
+    qlens = [1, 3, 17, 6] if causal else [1, 1, 1, 1]
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, seq_lens, Hkv, D, bs)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), Hq, D)).astype(np.float32)
+    scale = 0.37
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), scale, bs, "f32",
+                                      cu_seqlens_q=cu, causal=causal)
+    g = Hq // Hkv
+    for s, L in enumerate(seq_lens):
+        for h in range(Hq):
+            kvh = h // g
+            Q = [list(map(float, q[r, h])) for r in range(cu[s], cu[s + 1])]
+            K = [list(map(float, Kseq[s][j, kvh])) for j in range(L)]
+            V = [list(map(float, Vseq[s][j, kvh])) for j in range(L)]
+            bo, bl = brute_attention(Q, K, V, scale, causal)
+            np.testing.assert_allclose(out[cu[s]:cu[s + 1], h], np.array(bo), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[cu[s]:cu[s + 1], h], np.array(bl), rtol=0, atol=1e-12)
+
+
+def test_bruteforce_hand_example():
+    """Closed form worked by hand: q=(1,0), keys e0,e1, values (1,2),(3,4),
+    scale 1: weights e/(e+1), 1/(e+1)."""
+    e = math.e
+    o, l = brute_attention([[1.0, 0.0]], [[1.0, 0.0], [0.0, 1.0]], [[1.0, 2.0], [3.0, 4.0]], 1.0, False)
+    w0, w1 = e / (e + 1), 1 / (e + 1)
+    assert abs(o[0][0] - (w0 * 1 + w1 * 3)) < 1e-15
+    assert abs(o[0][1] - (w0 * 2 + w1 * 4)) < 1e-15
+    assert abs(l[0] - math.log(e + 1)) < 1e-15
+    # same example through the paged oracle, block size 1, blocks reversed
+    Kc = np.zeros((3, 1, 1, 2), np.float32)
+    Vc = np.zeros((3, 1, 1, 2), np.float32)
+    Kc[2, 0, 0] = [1, 0]; Kc[1, 0, 0] = [0, 1]
+    Vc[2, 0, 0] = [1, 2]; Vc[1, 0, 0] = [3, 4]
+    out, lse = oracle.paged_attention(np.array([[[1, 0]]], np.float32), Kc, Vc,
+                                      np.array([[2, 1]], np.int32), np.array([2]), 1.0, 1, "f32")
+    np.testing.assert_allclose(out[0, 0], [w0 + 3 * w1, 2 * w0 + 4 * w1], atol=1e-15)
+    assert abs(lse[0, 0] - math.log(e + 1)) < 1e-15
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_oracle_block_permutation_invariant():
+    rng = np.random.default_rng(5)
+    seq_lens = [7, 33, 64, 1]
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 16, 8)
+    q = rng.standard_normal((4, 4, 16)).astype(np.float32)
+    o1, l1 = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.25, 8, "f32")
+    perm = rng.permutation(Kc.shape[0] - 1) + 1          # keep block 0 fixed
+    newid = np.zeros(Kc.shape[0], np.int64)
+    newid[1:] = perm
+    Kp = np.empty_like(Kc); Vp = np.empty_like(Vc)
+    Kp[newid] = Kc; Vp[newid] = Vc
+    bt2 = np.where(bt > 0, newid[bt], 0).astype(np.int32)
+    o2, l2 = oracle.paged_attention(q, Kp, Vp, bt2, np.array(seq_lens), 0.25, 8, "f32")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_oracle_block_size_equivalence():
+    """The same logical K/V stored with block size 8, 16 and 32 gives
+    bit-identical outputs."""
+    rng = np.random.default_rng(6)
+    seq_lens = [5, 31, 70, 96]
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 16, 8)
+    q = rng.standard_normal((4, 2, 16)).astype(np.float32)
+    ref = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.3, 8, "f32")
+    for bs in (16, 32):
+        K2, V2, bt2 = repack(Kc, bt, seq_lens, 8, bs, rng, Vc)
+        got = oracle.paged_attention(q, K2, V2, bt2, np.array(seq_lens), 0.3, bs, "f32")
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+def test_oracle_ignores_poison_in_unused_slots():
+    rng = np.random.default_rng(7)
+    seq_lens = [9, 16, 23]
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 1, 8, 8)     # unused slots already NaN
+    q = rng.standard_normal((3, 2, 8)).astype(np.float32)
+    o1, l1 = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.5, 8, "f32")
+    Kz = np.nan_to_num(Kc, nan=0.0); Vz = np.nan_to_num(Vc, nan=0.0)
+    o2, l2 = oracle.paged_attention(q, Kz, Vz, bt, np.array(seq_lens), 0.5, 8, "f32")
+    assert np.isfinite(o1).all()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_oracle_gqa_equals_expanded_mha():
+    """Query head h uses kv head h // g: expanding the caches g times along
+    the head axis and running MHA gives the same result."""
+    rng = np.random.default_rng(8)
+    seq_lens = [12, 40]
+    g = 4
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 8, 16)
+    q = rng.standard_normal((2, 2 * g, 8)).astype(np.float32)
+    o1, l1 = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.4, 16, "f32")
+    Ke = np.repeat(Kc, g, axis=2); Ve = np.repeat(Vc, g, axis=2)
+    o2, l2 = oracle.paged_attention(q, Ke, Ve, bt, np.array(seq_lens), 0.4, 16, "f32")
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+def test_oracle_linear_in_values():
+    rng = np.random.default_rng(9)
+    seq_lens = [20, 3]
+    Kc, V1, bt, _, _ = tiny_pool(rng, seq_lens, 2, 8, 8)
+    # values on a 2^-10 grid so that V1 + V2 is exact in float32
+    V1 = np.round(V1 * 1024) / 1024
+    V2 = np.where(np.isnan(V1), np.nan, np.round(rng.standard_normal(V1.shape) * 1024) / 1024).astype(np.float32)
+    q = rng.standard_normal((2, 2, 8)).astype(np.float32)
+    a = oracle.paged_attention(q, Kc, V1, bt, np.array(seq_lens), 0.5, 8, "f32")[0]
+    b = oracle.paged_attention(q, Kc, V2, bt, np.array(seq_lens), 0.5, 8, "f32")[0]
+    c = oracle.paged_attention(q, Kc, V1 + V2, bt,
+                               np.array(seq_lens), 0.5, 8, "f32")[0]
+    np.testing.assert_allclose(a + b, c, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_oracle_single_token_returns_value_exactly():
+    rng = np.random.default_rng(10)
+    Kc, Vc, bt, _, Vseq = tiny_pool(rng, [1, 1], 2, 8, 16)
+    q = rng.standard_normal((2, 4, 8)).astype(np.float32) * 10
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array([1, 1]), 0.7, 16, "f32")
+    for s in range(2):
+        for h in range(4):
+            assert np.array_equal(out[s, h], Vseq[s][0, h // 2].astype(np.float64))
+
+
+def test_oracle_uniform_logits_give_mean():
+    """scale 0 makes every weight equal: output = mean of V, lse = ln L."""
+    rng = np.random.default_rng(11)
+    seq_lens = [13, 50]
+    Kc, Vc, bt, _, Vseq = tiny_pool(rng, seq_lens, 1, 8, 8)
+    q = rng.standard_normal((2, 3, 8)).astype(np.float32)
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.0, 8, "f32")
+    for s, L in enumerate(seq_lens):
+        for h in range(3):
+            np.testing.assert_allclose(out[s, h], Vseq[s][:, 0].astype(np.float64).mean(0), atol=1e-12)
+            assert abs(lse[s, h] - math.log(L)) < 1e-12
+
+
+def test_oracle_equal_keys_lse_closed_form():
+    """All keys equal to k0: every logit is scale*q.k0, so lse = that + ln L."""
+    rng = np.random.default_rng(12)
+    L, D = 37, 8
+    k0 = rng.standard_normal(D).astype(np.float32)
+    Kc, Vc, bt, _, _ = tiny_pool(rng, [L], 1, D, 8)
+    valid = ~np.isnan(Kc[..., 0])
+    Kc[valid] = k0
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    _, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 0.3, 8, "f32")
+    expect = 0.3 * float(np.dot(q[0, 0].astype(np.float64), k0.astype(np.float64))) + math.log(L)
+    assert abs(lse[0, 0] - expect) < 1e-12
+
+
+def test_oracle_needle_selects_one_value():
+    """q = a*e0 and exactly one key with b*e0 (others orthogonal to e0): the
+    output is that key's value up to exp(-a*b*scale) ~ 1e-157."""
+    rng = np.random.default_rng(13)
+    L, D = 70, 16
+    Kc, Vc, bt, _, Vseq = tiny_pool(rng, [L], 1, D, 16)
+    valid = ~np.isnan(Kc[..., 0, 0])
+    Kc[valid, 0, 0] = 0.0
+    jstar = 47
+    Kc[bt[0, jstar // 16], jstar % 16, 0, 0] = 64.0
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, 0] = 64.0
+    out, _ = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 1 / math.sqrt(128), 16, "f32")
+    np.testing.assert_allclose(out[0, 0], Vseq[0][jstar, 0].astype(np.float64), atol=1e-12, rtol=0)
+
+
+def test_oracle_empty_sequence():
+    rng = np.random.default_rng(14)
+    Kc, Vc, bt, _, _ = tiny_pool(rng, [4, 1], 1, 8, 8)
+    q = rng.standard_normal((2, 1, 8)).astype(np.float32)
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array([0, 1]), 0.5, 8, "f32")
+    assert np.array_equal(out[0, 0], np.zeros(8)) and lse[0, 0] == -np.inf
+    assert np.isfinite(out[1]).all()
+
+
+# ---------------------------------------------------------------- causal
+
+def test_oracle_causal_single_query_equals_decode():
+    rng = np.random.default_rng(15)
+    seq_lens = [9, 40, 1]
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 8, 8)
+    q = rng.standard_normal((3, 4, 8)).astype(np.float32)
+    cu = np.arange(4, dtype=np.int32)
+    a = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.5, 8, "f32")
+    b = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.5, 8, "f32",
+                               cu_seqlens_q=cu, causal=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_oracle_causal_rows_are_prefix_decodes():
+    """Bottom-right alignment: row i of a chunk of q_len rows over a
+    sequence of L tokens equals non-causal attention over the first
+    L - q_len + i + 1 tokens."""
+    rng = np.random.default_rng(16)
+    L, ql = 45, 11
+    Kc, Vc, bt, _, _ = tiny_pool(rng, [L], 2, 8, 8)
+    q = rng.standard_normal((ql, 2, 8)).astype(np.float32)
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 0.5, 8, "f32",
+                                      cu_seqlens_q=np.array([0, ql], np.int32), causal=True)
+    for i in range(ql):
+        o, l = oracle.paged_attention(q[i:i + 1], Kc, Vc, bt, np.array([L - ql + i + 1]), 0.5, 8, "f32")
+        # equal up to BLAS summation order (different matrix shapes)
+        np.testing.assert_allclose(out[i], o[0], atol=1e-13, rtol=0)
+        np.testing.assert_allclose(lse[i], l[0], atol=1e-13, rtol=0)
+
+
+def test_oracle_causal_no_context_matches_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    L, H, D = 29, 3, 16
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, [L], H, D, 8)
+    q = rng.standard_normal((L, H, D)).astype(np.float32)
+    out, _ = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 0.25, 8, "f32",
+                                    cu_seqlens_q=np.array([0, L], np.int32), causal=True)
+    Q = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    K = torch.from_numpy(Kseq[0].astype(np.float64)).permute(1, 0, 2)
+    V = torch.from_numpy(Vseq[0].astype(np.float64)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=0.25)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+
+
+def test_oracle_noncausal_matches_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(18)
+    L, H, D = 50, 2, 8
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, [L], H, D, 16)
+    q = rng.standard_normal((1, H, D)).astype(np.float32)
+    out, _ = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 0.35, 16, "f32")
+    Q = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    K = torch.from_numpy(Kseq[0].astype(np.float64)).permute(1, 0, 2)
+    V = torch.from_numpy(Vseq[0].astype(np.float64)).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=0.35)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- split / merge
+
+@pytest.mark.parametrize("P", [8, 16, 64, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_split_merge_equals_unsplit(P, causal):
+    rng = np.random.default_rng(19 + P)
+    seq_lens = [1, 17, 64, 100]
+    qlens = [1, 5, 1, 9] if causal else [1, 1, 1, 1]
+    Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 8, 8)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), 4, 8)).astype(np.float32)
+    a = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.5, 8, "f32", cu_seqlens_q=cu,
+                               causal=causal)
+    b = oracle.split_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.5, 8, "f32", P, cu_seqlens_q=cu,
+                               causal=causal)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-12, rtol=0)
+
+
+def test_merge_single_partition_is_identity_and_handles_empty():
+    o = np.array([[1.0, 2.0]])
+    l = np.array([0.3])
+    mo, ml = oracle.merge_partials([o], [l])
+    assert np.array_equal(mo, o) and np.array_equal(ml, l)
+    mo, ml = oracle.merge_partials([o, np.zeros_like(o)], [l, np.array([-np.inf])])
+    assert np.allclose(mo, o) and np.allclose(ml, l)
+    mo, ml = oracle.merge_partials([o, o], [np.array([-np.inf]), np.array([-np.inf])])
+    assert np.array_equal(mo, np.zeros_like(o)) and ml[0] == -np.inf
+
+
+def test_merge_two_halves_closed_form():
+    """Two partitions with one key each: merged weights are softmax of the
+    two logits."""
+    s0, s1 = 0.7, -1.2
+    v0, v1 = np.array([[1.0, -1.0]]), np.array([[3.0, 5.0]])
+    mo, ml = oracle.merge_partials([v0, v1], [np.array([s0]), np.array([s1])])
+    w0 = math.exp(s0) / (math.exp(s0) + math.exp(s1))
+    np.testing.assert_allclose(mo, w0 * v0 + (1 - w0) * v1, atol=1e-15)
+    assert abs(ml[0] - math.log(math.exp(s0) + math.exp(s1))) < 1e-15
+
+
+# ---------------------------------------------------------------- kv write
+
+def test_oracle_kv_write_roundtrip_bit_exact():
+    rng = np.random.default_rng(20)
+    bs, Hkv, D = 8, 2, 8
+    nblk = 10
+    Kc = np.full((nblk, bs, Hkv, D), 0x7FC0, np.uint16)
+    Vc = Kc.copy()
+    T = 30
+    slots = rng.choice(np.arange(bs, nblk * bs), size=T, replace=False).astype(np.int64)
+    slots[[3, 11, 29]] = -1
+    key = rng.integers(0, 65535, size=(T + 4, Hkv, D)).astype(np.uint16)   # 4 padded rows
+    val = rng.integers(0, 65535, size=(T + 4, Hkv, D)).astype(np.uint16)
+    oracle.kv_cache_write(Kc, Vc, key, val, slots, bs)
+    written = np.zeros((nblk * bs), bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        assert np.array_equal(Kc.reshape(-1, Hkv, D)[s], key[t])
+        assert np.array_equal(Vc.reshape(-1, Hkv, D)[s], val[t])
+        written[s] = True
+    assert (Kc.reshape(-1, Hkv, D)[~written] == 0x7FC0).all()
+    assert (Vc.reshape(-1, Hkv, D)[~written] == 0x7FC0).all()
+
+
+def test_kv_write_then_attention_matches_contiguous():
+    """Writing a sequence's tokens through slot_mapping and then gathering
+    through its block table reproduces contiguous attention: the slot and
+    block-table conventions agree."""
+    rng = np.random.default_rng(21)
+    bs, Hkv, D, L = 8, 1, 8, 29
+    nblk = 8
+    bt = np.array([[5, 2, 7, 1]], np.int32)
+    K = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    V = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    slots = np.array([int(bt[0, j // bs]) * bs + j % bs for j in range(L)], np.int64)
+    Kc = np.full((nblk, bs, Hkv, D), np.nan, np.float32); Vc = Kc.copy()
+    oracle.kv_cache_write(Kc, Vc, K, V, slots, bs)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array([L]), 0.5, bs, "f32")
+    bo, bl = brute_attention([list(map(float, q[0, 0]))], [list(map(float, k[0])) for k in K],
+                             [list(map(float, v[0])) for v in V], 0.5, False)
+    np.testing.assert_allclose(out[0, 0], bo[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- widening & page facts
+
+def test_widen_bf16_matches_torch_for_all_patterns():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+
+
+def test_page_facts():
+    facts = json.load(open(GOLDEN))
+    ex = facts["allocate_slots_example"]
+    assert oracle.blocks_for_tokens(ex["new_tokens"], ex["block_size"]) == ex["blocks"]
+    f = facts["block_bytes_formula"]
+    # Llama-7B-shaped layer (32 kv heads x 128) at the default block size in bf16
+    assert oracle.block_bytes(f["default_block_size"], 32, 128, f["bf16_bytes"]) == \
+        f["kv_factor"] * 16 * 32 * 128 * 2 == 262144
+    # GQA shape (8 kv heads x 128)
+    assert oracle.block_bytes(16, 8, 128, 2) == 65536
+    assert facts["slot_padding"]["pad_slot"] == -1 and facts["slot_padding"]["null_block_id"] == 0
+
+
+def test_oracle_on_generated_tiny_config():
+    """Generated workload 1 runs through the oracle with finite outputs,
+    and its unused slots really are poisoned."""
+    w = W.make_config(1)
+    out, lse = oracle.paged_attention(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens,
+                                      w.scale, w.block_size, w.dtype)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    valid = w.valid_slot_mask()
+    assert np.isnan(w.k_cache[~valid]).all() and not np.isnan(w.k_cache[valid]).any()

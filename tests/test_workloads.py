@@ -1,0 +1,131 @@
+"""Input generator checks: rounding, determinism, shapes and metadata."""
+import math
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_50_amd import workloads as W
+
+
+def test_bf16_rne_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-38).astype(np.float32),          # subnormals
+        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38, np.inf, -np.inf], np.float32),
+    ])
+    # exact ties: low 16 bits = 0x8000, both parities of bit 16
+    ties = (rng.integers(0, 2**31, 2000).astype(np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32)])
+    x = x[np.isfinite(x) | np.isinf(x)]
+    mine = W.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ok = ~np.isnan(x)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def test_bf16_roundtrip_widen():
+    b = np.arange(0, 65536, 97, dtype=np.uint32).astype(np.uint16)
+    f = W.bf16_bits_to_f32(b)
+    ok = ~np.isnan(f)
+    assert np.array_equal(W.f32_to_bf16_bits(f[ok]), b[ok])
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_deterministic_per_seed(cfg):
+    kw = dict(num_seqs=3, max_len=300) if cfg != 5 else dict(num_seqs=3, max_len=200,
+                                                             num_chunks=2, chunk_len=40)
+    a = W.make_config(cfg, **kw)
+    b = W.make_config(cfg, **kw)
+    for f in ("q", "k_cache", "v_cache", "block_tables", "seq_lens"):
+        assert np.array_equal(getattr(a, f).view(np.uint8), getattr(b, f).view(np.uint8)), f
+    c = W.make_config(cfg, seed=W.DEFAULT_SEEDS[cfg] + 100, **kw)
+    assert not np.array_equal(a.q, c.q)
+
+
+def test_thread_count_does_not_change_values(monkeypatch):
+    a = W.make_config(3, num_seqs=6, max_len=500)
+    monkeypatch.setattr(W, "_GEN_THREADS", 1)
+    b = W.make_config(3, num_seqs=6, max_len=500)
+    assert np.array_equal(a.k_cache, b.k_cache) and np.array_equal(a.v_cache, b.v_cache)
+
+
+def _check_tables(w):
+    bs = w.block_size
+    seen = set()
+    for s in range(w.num_seqs):
+        nb = W.blocks_needed(w.seq_lens[s], bs)
+        row = w.block_tables[s]
+        assert (row[:nb] >= 1).all() and (row[:nb] < w.num_blocks).all()
+        assert (row[nb:] == 0).all()                      # null-block padding
+        for b in row[:nb]:
+            assert int(b) not in seen
+            seen.add(int(b))
+    valid = w.valid_slot_mask()
+    assert not valid[0].any()                             # block 0 never holds data
+    # every valid slot is finite, every other slot is NaN
+    if w.slot_mapping is None:
+        assert not np.isnan(W.bf16_bits_to_f32(w.k_cache[valid]) if w.dtype == "bf16"
+                            else w.k_cache[valid]).any()
+    inval = W.bf16_bits_to_f32(w.k_cache[~valid]) if w.dtype == "bf16" else w.k_cache[~valid]
+    assert np.isnan(inval).all()
+
+
+def test_config1_full():
+    w = W.make_config(1)
+    assert w.q.shape == (4, 8, 64) and w.k_cache.shape == (128, 16, 8, 64)
+    assert w.dtype == "f32" and w.num_blocks == 128
+    assert ((w.seq_lens >= 1) & (w.seq_lens <= 256)).all()
+    assert abs(w.scale - 1 / 8) < 1e-15
+    _check_tables(w)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_decode_configs_small(cfg):
+    w = W.make_config(cfg, num_seqs=5, max_len=1000)
+    Hq, Hkv = {2: (32, 32), 3: (32, 8), 4: (64, 8)}[cfg]
+    assert w.q.shape == (5, Hq, 128) and w.k_cache.shape[1:] == (16, Hkv, 128)
+    assert w.dtype == "bf16" and w.q.dtype == np.uint16
+    total = sum(W.blocks_needed(L, 16) for L in w.seq_lens)
+    assert w.num_blocks == 1 + math.ceil(1.1 * total)
+    _check_tables(w)
+    if cfg == 4:
+        assert w.partition_size == 512 and w.sigma == 0.5
+        x = W.bf16_bits_to_f32(w.q).astype(np.float64)
+        assert 0.4 < x.std() < 0.6
+
+
+def test_config3_length_distribution():
+    rng = np.random.Generator(np.random.PCG64(2))
+    L = W.config_lengths(3, rng)
+    assert L.shape == (256,) and L.min() >= 16 and L.max() <= 8192
+    assert 700 < np.median(L) < 1400
+
+
+def test_config5_small_structure():
+    w = W.make_config(5, num_seqs=6, max_len=300, num_chunks=2, chunk_len=48)
+    ql = w.query_lens
+    assert list(ql[:2]) == [48, 48] and (ql[2:] == 1).all()
+    assert w.causal and w.block_size == 32 and w.num_kv_heads == 8 and w.num_heads == 32
+    assert w.slot_mapping.shape == (int(ql.sum()),) and w.slot_mapping.dtype == np.int64
+    assert w.key_new.shape == (int(ql.sum()), 8, 128)
+    # new tokens' slots are exactly the last q_len positions of each sequence
+    for s in range(w.num_seqs):
+        L = int(w.seq_lens[s])
+        pos = np.arange(L - ql[s], L)
+        exp = W.slots_of(w.block_tables[s], pos, 32)
+        assert np.array_equal(w.slot_mapping[w.cu_seqlens_q[s]:w.cu_seqlens_q[s + 1]], exp)
+        # those slots are still poisoned before the write
+        flat = w.k_cache.reshape(-1, 8, 128)
+        assert (flat[exp] == W.BF16_QNAN).all()
+    _check_tables(w)
+
+
+def test_algorithmic_bytes_llama_shape():
+    w = W.make_config(2, num_seqs=2, max_len=300)
+    L = w.seq_lens.astype(int)
+    nb = sum(W.blocks_needed(x, 16) for x in L)
+    expect = L.sum() * 2 * 32 * 128 * 2 + 2 * 2 * 32 * 128 * 2 + 4 * nb + 4 * 2
+    assert W.algorithmic_bytes(w) == expect
+    assert w.kv_block_bytes() == 262144
