@@ -1,0 +1,252 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input: for a
+decode workload one paged_attention_decode call (partition kernel + split
+merge) for one attention layer; for the mixed workload the slot write plus
+one paged_attention_varlen call.  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line (rank 0).  `value` is achieved HBM GB/s of the whole step
+(algorithmic bytes / step time); `roofline` is the dominant kernel's achieved
+rate against the MI355X peak, from per-launch HIP events recorded by the
+library inside the timed region; `cpu_baseline` times the fp64 CPU oracle on
+the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2..5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + µs/step, 1 MI355X"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+WORKLOAD_DESC = {
+    1: "4 seqs, 8/8 heads, head 64, block 16, fp32, seq_lens U[1,256], seed 0",
+    2: "64 seqs, 32/32 heads, head 128, block 16, bf16, seq_lens U[200,4096], seed 1",
+    3: "256 seqs, 32/8 heads, head 128, block 16, bf16, seq_lens lognormal(median 1024, sigma 0.8) in [16,8192], seed 2",
+    4: "8 seqs, 64/8 heads, head 128, block 16, bf16, seq_lens U[32768,131072], 512-token partitions, N(0,0.5), seed 3",
+    5: "slot write + varlen: 4 causal chunks of 512 (context U[0,4096]) + 128 decode rows (U[64,4096]), 32/8 heads, head 128, block 32, bf16, seed 4",
+}
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "paged_kv_cache_50_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str, kernel: str):
+    """HBM traffic per launch measured by rocprofv3 counters for this exact
+    kernel source, or None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{workload_name}:{kernel}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """fp64 oracle over the workload's sequences, repeated until the time
+    budget is used (at least one pass over a bounded sample)."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_50_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    kc, vc = w.k_cache, w.v_cache
+    if w.slot_mapping is not None:
+        kc, vc = kc.copy(), vc.copy()
+        oracle.kv_cache_write(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size)
+    pairs = [(s, h) for s in range(w.num_seqs) for h in range(w.num_kv_heads)]
+    # bytes of one (seq, kv head) pair: its K/V tokens plus q/out rows
+    e = w.elem_bytes
+    g = w.num_heads // w.num_kv_heads
+    ql = w.query_lens
+    done_bytes = 0
+    done_pairs = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        s, h = pairs[i % len(pairs)]
+        oracle.paged_attention(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size,
+                               w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
+                               pairs=[(s, h)])
+        done_bytes += int(w.seq_lens[s]) * 2 * w.head_size * e + 2 * int(ql[s]) * g * w.head_size * e
+        done_pairs += 1
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (done_pairs >= len(pairs) and el >= budget_s / 4):
+            break
+    el = time.perf_counter() - t0
+    sample = (f"{done_pairs} (sequence, kv head) pairs of the same workload "
+              f"({done_pairs / len(pairs):.2f} passes), numpy fp64 oracle")
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; a multi-GPU figure is not "
+              "part of it (sharding is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from paged_kv_cache_50_amd import pagedkv, workloads as W
+    from tests import gpu_util as G
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        return 1
+    pagedkv.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.time()
+    w = W.make_config(args.workload)
+    print(f"[bench] generated {w.name} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    ps = w.partition_size if args.partition_size is None else args.partition_size
+    dw = G.DevWorkload(w, device=dev)
+    ws_bytes = pagedkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                       w.max_seq_len, ps)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    S, T = w.num_seqs, w.num_q_rows
+
+    def step():
+        if w.slot_mapping is not None:
+            pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new,
+                                   dw.slot_mapping)
+        if w.cu_seqlens_q is None:
+            pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
+                                           dw.seq_lens, w.scale, w.max_seq_len,
+                                           partition_size=ps, workspace=ws)
+        else:
+            pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
+                                           dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
+                                           w.max_seq_len, causal=w.causal, partition_size=ps,
+                                           workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pagedkv.timing_read()                 # drop anything recorded before
+    pagedkv.timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    kern_ms = pagedkv.timing_read()
+    pagedkv.timing_enable(False)
+    ms_per_step = ms_total / args.steps
+
+    B = W.algorithmic_bytes(w)
+    e = w.elem_bytes
+    out_bytes = T * w.num_heads * w.head_size * e
+    write_bytes = 0
+    if w.slot_mapping is not None:
+        write_bytes = 2 * 2 * len(w.slot_mapping) * w.num_kv_heads * w.head_size * e + 8 * len(w.slot_mapping)
+    gbs = B / (ms_per_step * 1e-3) / 1e9
+    kavg = float(np.mean(kern_ms)) if kern_ms else None
+    if w.cu_seqlens_q is None:
+        kernel = "attn_partition"
+        # the partition kernel reads every KV token, q and the metadata; the
+        # merge kernel writes out (charged to the merge, not here)
+        main_bytes = B - out_bytes
+        achieved = main_bytes / (kavg * 1e-3) / 1e9 if kavg else None
+        roof = {"bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                "traffic": load_traffic(w.name, kernel),
+                "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms)}
+    else:
+        kernel = "attn_prefill"
+        flops = W.attention_flops(w)
+        ql = w.query_lens
+        pre_flops = 0
+        for s in range(S):
+            if ql[s] > 1:
+                ctx = int(w.seq_lens[s]) - int(ql[s])
+                pre_flops += 4 * w.num_heads * w.head_size * (int(ql[s]) * ctx + int(ql[s]) * (int(ql[s]) + 1) // 2)
+        achieved = pre_flops / (kavg * 1e-3) / 1e12 if kavg else None
+        roof = {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+                "traffic": load_traffic(w.name, kernel),
+                "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms),
+                "total_flops": flops}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16"}[w.dtype],
+        "data": "synthetic (seeded; shapes and length distributions of the workload)",
+        "config": {"workload": w.name, "description": WORKLOAD_DESC[args.workload],
+                   "num_seqs": S, "query_rows": T, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "kv_tokens": int(w.seq_lens.sum()),
+                   "algorithmic_bytes": int(B), "partition_size": ps,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    del dw
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

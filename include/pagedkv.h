@@ -1,0 +1,232 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: paged KV-cache attention on AMD MI355X
+ * (gfx950).
+ *
+ * Operations (as described by the vLLM pages):
+ *   - the KV-cache slot write ("reshape_and_cache"): vLLM book
+ *     «Implémentation du cœur du moteur d'inférence haute performance vLLM»,
+ *     ch. 6 "Écriture du KV cache : do_kv_cache_update", and ch. 5.2
+ *     "slot_mapping et la block table";
+ *   - attention over a paged cache, decode and variable-length (chunked
+ *     prefill) batches, with an optional split of the key range whose partial
+ *     results are merged by log-sum-exp: ch. 6 "Structure des métadonnées",
+ *     "build() étape par étape" (split buffer), "Flux des paramètres du chemin
+ *     non-cascadé" and "forward()" (merge of partial attention states);
+ *   - block bytes = 2 * block_size * num_kv_heads * head_size * dtype_bytes:
+ *     «Khám phá vLLM: Giải phẫu hệ thống suy luận LLM thông lượng cao», §1 note.
+ *
+ * Conventions shared by every entry point
+ *   Cache layout: K and V are separate tensors, each
+ *     [num_blocks, block_size, num_kv_heads, head_size], row-major inside a
+ *     block (ch. 6 "Transformation de la disposition mémoire du KV cache").
+ *     Consecutive blocks are block_stride elements apart (0 = dense, i.e.
+ *     block_size * num_kv_heads * head_size), so a block-outermost buffer
+ *     shared by several layers can be passed as is.
+ *   Slots: slot = physical_block * block_size + offset_in_block.
+ *   Block tables: int32 [num_seqs, max_blocks_per_seq]; row s lists sequence
+ *     s's physical blocks in logical order; only the first
+ *     ceil(seq_len / block_size) entries are read.  Padding entries should be
+ *     the null block 0 (ch. 5.2); the kernels never read a padding entry.
+ *   seq_lens: int32 [num_seqs] = cached context + new query tokens (ch. 6
+ *     "Structure des métadonnées"); the new tokens' K/V must already be in the
+ *     cache when attention runs.  seq_len 0 is legal and yields zero output
+ *     and lse = -inf.
+ *   GQA: query head h reads kv head h / (num_heads / num_kv_heads).
+ *   Causal (varlen only): query row i of a sequence with q_len rows sits at
+ *     absolute position i + seq_len - q_len and sees keys j <= that position
+ *     (ch. 6 "Branche de masque").
+ *   Output: written in place, same dtype and layout as q; float32 results are
+ *     rounded to bfloat16 by round-to-nearest-even.
+ *   lse_out (optional, may be NULL): float32 [rows, num_heads], natural-log
+ *     log-sum-exp of the scaled logits each row saw; -inf for an empty row.
+ *
+ * Memory and execution
+ *   Every pointer argument of type void* / int32_t* / int64_t* / float* that
+ *   names a tensor is a DEVICE pointer, except in pkv_validate_metadata, which
+ *   takes host pointers.  The caller allocates and owns every buffer,
+ *   including the split workspace; the library never allocates, frees, copies
+ *   to the host or synchronizes.  Calls are asynchronous on `stream` (a
+ *   hipStream_t; NULL = the null stream), so they can be captured in a HIP
+ *   graph.  `out` must not alias q, the caches or the workspace.
+ *   Device tensors must be 16-byte aligned and dense in the last dimension;
+ *   q/out/key/value are dense [rows, heads, head_size].
+ *
+ * Errors
+ *   Host-side checks return a status and never abort: NULL pointers, bad sizes,
+ *   unsupported dtype/head_size/block_size combinations (a reason string is
+ *   available from pkv_unsupported_reason), misalignment, a too small
+ *   workspace.  A failed kernel launch returns PKV_ERR_HIP.
+ *   Device-resident metadata (block ids, slots, seq_lens, cu_seqlens_q) is not
+ *   validated on the fast path.  Out-of-range values give unspecified results
+ *   but never an out-of-bounds access: block ids are clamped into the pool,
+ *   slots outside the pool are skipped, seq_lens are clamped to
+ *   [0, min(max_seq_len, max_blocks_per_seq * block_size)] and query ranges
+ *   to [0, num_tokens] and at most max_query_len rows.  pkv_validate_metadata
+ *   checks all of this on host copies for tests and debugging.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  PKV_ERR_SHAPE = 2,       /* a size is negative / zero where it must be positive */
+  PKV_ERR_UNSUPPORTED = 3, /* dtype/head_size/block_size/head ratio not supported */
+  PKV_ERR_ALIGN = 4,       /* a pointer or stride is not 16-byte aligned          */
+  PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
+  PKV_ERR_METADATA = 6,    /* pkv_validate_metadata found invalid metadata        */
+  PKV_ERR_HIP = 7          /* a HIP launch failed                                 */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1
+} pkv_dtype;
+
+/* Descriptor of one layer's paged KV cache (no ownership is transferred). */
+typedef struct pkv_kv_cache {
+  void*   k_cache;       /* device [num_blocks, block_size, num_kv_heads, head_size] */
+  void*   v_cache;       /* device, same shape, dtype and block_stride as k_cache    */
+  int64_t num_blocks;    /* pool size, > 0                                          */
+  int32_t block_size;    /* tokens per block: 8, 16 or 32                           */
+  int32_t num_kv_heads;  /* > 0                                                     */
+  int32_t head_size;     /* 64 or 128                                               */
+  int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value)       */
+  int64_t block_stride;  /* elements between consecutive blocks; 0 = dense         */
+} pkv_kv_cache;
+
+/*
+ * Scatter new K/V rows into the cache ("reshape_and_cache", ch. 6 "Écriture du
+ * KV cache"): for t in [0, num_tokens) with slot = slot_mapping[t] >= 0,
+ *   k_cache[slot / block_size, slot % block_size, :, :] = key[t, :, :]
+ * and the same for value.  slot -1 (padding, ch. 5.2) writes nothing.  The
+ * token count is num_tokens (the length of slot_mapping); key/value may hold
+ * more, padded rows, which are never read.  Elements are copied bit for bit.
+ *   key, value   device [>= num_tokens, num_kv_heads, head_size], cache dtype
+ *   slot_mapping device int64 [num_tokens]
+ * Duplicate non-negative slots are undefined (one of the rows wins).
+ * num_tokens == 0 is a no-op returning PKV_OK.
+ */
+pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
+                              const int64_t* slot_mapping, int64_t num_tokens, void* stream);
+
+/*
+ * Partition size (tokens per key-range split) the attention calls use for
+ * these arguments: partition_size > 0 is used as given (a multiple of 32);
+ * -1 means never split; 0 selects the library default.  Returns 0 when the
+ * key range is not split, or a negative value if partition_size is invalid.
+ */
+int32_t pkv_choose_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * Workspace bytes an attention call needs (0 when it does not split): one
+ * float32 partial output [num_splits, num_heads, num_seqs, head_size] and one
+ * float32 log-sum-exp [num_splits, num_heads, num_seqs], the split buffer
+ * shape of ch. 6 "build() étape par étape", with
+ * num_splits = ceil(max_seq_len / partition) and rows indexed by sequence.
+ * Returns (size_t)-1 for invalid arguments.
+ */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t max_seq_len,
+                                     int32_t partition_size);
+
+/*
+ * Decode attention: one query row per sequence.
+ *   out, q        device [num_seqs, num_heads, head_size], cache dtype
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]
+ *   max_seq_len   host upper bound of seq_lens (sizes the launch and the split)
+ *   scale         logit scale (usually 1/sqrt(head_size))
+ *   partition_size see pkv_choose_partition_size
+ *   lse_out       optional device float32 [num_seqs, num_heads]
+ *   workspace     device, >= pkv_attention_workspace_bytes(...) bytes, 16-byte
+ *                 aligned; may be NULL when that size is 0
+ * num_seqs == 0 is a no-op.
+ */
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cache* cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                      int32_t max_seq_len, float scale, int32_t partition_size,
+                                      float* lse_out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * Variable-length attention over a flattened batch (ch. 6 "Structure des
+ * métadonnées": query_start_loc / seq_lens; «Khám phá vLLM» "Chạy forward
+ * pass": all sequences flattened into one super-sequence).  Sequence s owns
+ * query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q/out and attends to
+ * its seq_lens[s] cached tokens, causally if `causal` is non-zero.  Rows of
+ * sequences with one query row are computed by the decode kernels (split by
+ * partition_size, using the workspace); longer query ranges by the
+ * matrix-core prefill kernel.
+ *   out, q        device [num_tokens, num_heads, head_size]
+ *   cu_seqlens_q  device int32 [num_seqs + 1], non-decreasing, from 0
+ *   seq_lens      device int32 [num_seqs]
+ *   max_query_len host upper bound of the query lengths
+ *   lse_out       optional device float32 [num_tokens, num_heads]
+ */
+pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cache* cache,
+                                      const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t max_query_len, int32_t max_seq_len, float scale,
+                                      int32_t causal, int32_t partition_size, float* lse_out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Capability check in the spirit of supports_combination (ch. 6 "Matrice de
+ * capacités"): NULL when the combination is supported, else a static string
+ * saying why not.
+ */
+const char* pkv_unsupported_reason(int32_t dtype, int32_t head_size, int32_t block_size,
+                                   int32_t num_heads, int32_t num_kv_heads);
+
+/* Static, human-readable name of a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * Debug check of HOST copies of the metadata (synchronous, no GPU use):
+ * block ids of used entries in [1, num_blocks) (block 0 is the reserved null
+ * block), no block shared between used entries, seq_lens in
+ * [0, min(max_seq_len, max_blocks_per_seq * block_size)], cu_seqlens_q (may
+ * be NULL for decode) starting at 0, non-decreasing, ending at num_tokens,
+ * query lengths <= min(seq_len, max_query_len), and slot_mapping (may be NULL)
+ * entries either -1 or inside the pool, with no slot repeated.
+ * Returns PKV_OK or PKV_ERR_METADATA; when `msg` is not NULL a description of
+ * the first problem (or "") is written there, truncated to msg_len bytes.
+ */
+pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t num_seqs,
+                                 const int32_t* cu_seqlens_q, int32_t num_tokens,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 const int64_t* slot_mapping, int64_t num_slots,
+                                 int64_t num_blocks, int32_t block_size,
+                                 char* msg, size_t msg_len);
+
+/*
+ * Per-launch timing of the main attention kernel, for benchmarks.  When
+ * enabled, each attention call records a pair of HIP events on its stream
+ * around its main kernel (the decode partition kernel, or the prefill kernel
+ * of a varlen call).  pkv_timing_read waits for the recorded events, writes
+ * up to `cap` durations in milliseconds (oldest first) and returns how many
+ * were written; it then clears the record.  Up to 4096 launches are kept.
+ * Not for use under graph capture.  Returns PKV_OK or PKV_ERR_HIP.
+ */
+pkv_status pkv_timing_enable(int32_t enable);
+int32_t pkv_timing_read(float* ms, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -76,12 +76,12 @@ def gather_kv(cache: np.ndarray, block_table_row: np.ndarray, seq_len: int,
     entries are used.
     """
     nb = -(-seq_len // block_size)
-    blocks = [cache[int(block_table_row[i])] for i in range(nb)]
-    if not blocks:
-        shape = cache.shape[2:] if kv_head is None else cache.shape[3:]
-        return np.zeros((0,) + tuple(shape), dtype=cache.dtype)
-    tokens = np.concatenate(blocks, axis=0)[:seq_len]     # [L, Hkv, D]
-    return tokens if kv_head is None else tokens[:, kv_head]
+    ids = np.asarray(block_table_row[:nb], dtype=np.int64)
+    if kv_head is None:
+        blocks = cache[ids]                                # [nb, bs, Hkv, D]
+    else:
+        blocks = cache[ids, :, kv_head, :]                 # [nb, bs, D]
+    return blocks.reshape((nb * block_size,) + blocks.shape[2:])[:seq_len]
 
 
 def _softmax_rows(S: np.ndarray, V: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

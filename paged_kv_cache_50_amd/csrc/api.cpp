@@ -1,0 +1,431 @@
+// Host side of libpagedkv.so: argument validation, kernel selection, launch
+// geometry, split workspace layout, per-launch timing and the host metadata
+// checker.  The C ABI is declared in include/pagedkv.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+
+#include "../../include/pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv::AttnArgs;
+
+constexpr int32_t kDefaultPartition = 512;
+constexpr int32_t kPartitionQuantum = 32;
+constexpr int64_t kMaxGridZ = 65535;
+constexpr int64_t kMaxGridY = 65535;
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t num_heads,
+                   int32_t num_kv_heads) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return "dtype must be PKV_F32 or PKV_BF16";
+  if (head_size != 64 && head_size != 128) return "head_size must be 64 or 128";
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return "block_size must be 8, 16 or 32";
+  if (num_kv_heads <= 0) return "num_kv_heads must be positive";
+  if (num_heads <= 0) return "num_heads must be positive";
+  if (num_heads % num_kv_heads != 0) return "num_heads must be a multiple of num_kv_heads";
+  return nullptr;
+}
+
+pkv_status check_cache(const pkv_kv_cache* c, int32_t num_heads) {
+  if (!c || !c->k_cache || !c->v_cache) return PKV_ERR_NULL;
+  if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_size <= 0)
+    return PKV_ERR_SHAPE;
+  if (reason(c->dtype, c->head_size, c->block_size, num_heads > 0 ? num_heads : c->num_kv_heads,
+             c->num_kv_heads))
+    return PKV_ERR_UNSUPPORTED;
+  const int64_t dense = (int64_t)c->block_size * c->num_kv_heads * c->head_size;
+  if (c->block_stride != 0 && c->block_stride < dense) return PKV_ERR_SHAPE;
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_ALIGN;
+  const int64_t stride = c->block_stride ? c->block_stride : dense;
+  if ((stride * elem_bytes(c->dtype)) % 16 != 0) return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
+int64_t block_stride_elems(const pkv_kv_cache* c) {
+  return c->block_stride ? c->block_stride
+                         : (int64_t)c->block_size * c->num_kv_heads * c->head_size;
+}
+
+// Query heads handled together by one workgroup of the VALU kernel.
+int heads_per_chunk(int group) {
+  for (int gt : {8, 4, 2, 1})
+    if (group % gt == 0) return gt;
+  return 1;
+}
+
+// ----------------------------------------------------------------- timing
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  static constexpr int kCap = 4096;
+  hipEvent_t start[kCap] = {};
+  hipEvent_t stop[kCap] = {};
+  int64_t head = 0;  // oldest unread record
+  int64_t tail = 0;  // next record
+};
+Timing g_timing;
+
+bool timing_begin(hipStream_t st, int* slot) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.enabled) return false;
+  const int i = (int)(g_timing.tail % Timing::kCap);
+  if (!g_timing.start[i]) {
+    if (hipEventCreate(&g_timing.start[i]) != hipSuccess) return false;
+    if (hipEventCreate(&g_timing.stop[i]) != hipSuccess) return false;
+  }
+  if (g_timing.tail - g_timing.head >= Timing::kCap) g_timing.head++;  // overwrite oldest
+  if (hipEventRecord(g_timing.start[i], st) != hipSuccess) return false;
+  *slot = i;
+  return true;
+}
+
+void timing_end(hipStream_t st, int slot) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (hipEventRecord(g_timing.stop[slot], st) == hipSuccess) g_timing.tail++;
+}
+
+// ----------------------------------------------------------------- launch helpers
+pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_size, int gt,
+                                unsigned gx, unsigned gy, int64_t z_total, hipStream_t st) {
+  for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
+    a.z_base = (int32_t)z0;
+    const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
+    if (pkv::launch_attn_valu(a, dtype, head_size, block_size, gt, dim3(gx, gy, gz), st) !=
+        hipSuccess)
+      return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
+  if (pkv::launch_splitkv_reduce(a, dtype, head_size, st) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+int32_t num_splits_for(int32_t max_seq_len, int32_t P) {
+  if (P <= 0) return 1;
+  return std::max<int32_t>(1, (int32_t)(((int64_t)max_seq_len + P - 1) / P));
+}
+
+AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
+                   const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                   int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t max_seq_len,
+                   int32_t max_query_len, float scale, int32_t P, int32_t nsplits, float* lse_out,
+                   void* workspace) {
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = nullptr;
+  a.lse_out = lse_out;
+  a.ws_o = nullptr;
+  a.ws_lse = nullptr;
+  if (nsplits > 1) {
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + (int64_t)nsplits * num_heads * num_seqs * cache->head_size;
+  }
+  a.block_stride = block_stride_elems(cache);
+  a.num_blocks = cache->num_blocks;
+  a.max_blocks_per_seq = max_blocks;
+  a.block_size = cache->block_size;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.max_seq_len = max_seq_len;
+  a.max_query_len = max_query_len;
+  a.partition_size = nsplits > 1 ? P : 0;
+  a.num_splits = nsplits;
+  a.head_chunks = 1;
+  a.z_base = 0;
+  a.mode = pkv::kModeDecode;
+  a.causal = 0;
+  a.skip_multi_row = 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_unsupported_reason(int32_t dtype, int32_t head_size, int32_t block_size,
+                                   int32_t num_heads, int32_t num_kv_heads) {
+  return reason(dtype, head_size, block_size, num_heads, num_kv_heads);
+}
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid size or shape argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported dtype/head_size/block_size/head combination";
+    case PKV_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_METADATA: return "invalid metadata";
+    case PKV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t pkv_choose_partition_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t partition_size) {
+  (void)num_seqs;
+  (void)num_heads;
+  (void)num_kv_heads;
+  if (max_seq_len < 0) return -1;
+  if (partition_size == -1) return 0;
+  if (partition_size < -1) return -1;
+  if (partition_size > 0) {
+    if (partition_size % kPartitionQuantum != 0) return -1;
+    return partition_size;
+  }
+  return max_seq_len > kDefaultPartition ? kDefaultPartition : 0;
+}
+
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t max_seq_len,
+                                     int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seq_len < 0)
+    return (size_t)-1;
+  const int32_t P =
+      pkv_choose_partition_size(num_seqs, num_heads, num_kv_heads, max_seq_len, partition_size);
+  if (P < 0) return (size_t)-1;
+  const int32_t ns = num_splits_for(max_seq_len, P);
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)ns * num_heads * num_seqs;
+  return rows * head_size * sizeof(float) + rows * sizeof(float);
+}
+
+pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
+                              const int64_t* slot_mapping, int64_t num_tokens, void* stream) {
+  pkv_status st = check_cache(cache, cache ? cache->num_kv_heads : 0);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value)) return PKV_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0) return PKV_ERR_ALIGN;
+  pkv::KvWriteArgs a{};
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.key = key;
+  a.value = value;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_slots = cache->num_blocks * cache->block_size;
+  a.block_stride_bytes = block_stride_elems(cache) * elem_bytes(cache->dtype);
+  a.block_size = cache->block_size;
+  a.row_bytes = cache->num_kv_heads * cache->head_size * elem_bytes(cache->dtype);
+  if (num_tokens > (int64_t)INT32_MAX * 4) return PKV_ERR_SHAPE;
+  return pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                 : PKV_ERR_HIP;
+}
+
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cache* cache,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                                      int32_t max_seq_len, float scale, int32_t partition_size,
+                                      float* lse_out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  pkv_status st = check_cache(cache, num_heads);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
+    return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !block_tables || !seq_lens) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
+  const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads,
+                                              max_seq_len, partition_size);
+  if (P < 0) return PKV_ERR_SHAPE;
+  const int32_t ns = num_splits_for(max_seq_len, P);
+  if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
+  if (ns > 1) {
+    const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
+                                                      cache->head_size, max_seq_len, P);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                         num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
+  a.mode = pkv::kModeDecode;
+  const int group = num_heads / cache->num_kv_heads;
+  const int gt = heads_per_chunk(group);
+  a.head_chunks = group / gt;
+  int tslot = 0;
+  const bool timed = timing_begin(s, &tslot);
+  st = launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt,
+                            (unsigned)(cache->num_kv_heads * a.head_chunks), (unsigned)ns, num_seqs,
+                            s);
+  if (timed) timing_end(s, tslot);
+  if (st != PKV_OK) return st;
+  if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
+  return st;
+}
+
+pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cache* cache,
+                                      const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                      int32_t max_query_len, int32_t max_seq_len, float scale,
+                                      int32_t causal, int32_t partition_size, float* lse_out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_cache(cache, num_heads);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
+      max_query_len < 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
+    return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
+  const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads,
+                                              max_seq_len, partition_size);
+  if (P < 0) return PKV_ERR_SHAPE;
+  const int32_t ns = num_splits_for(max_seq_len, P);
+  if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
+  if (ns > 1) {
+    const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
+                                                      cache->head_size, max_seq_len, P);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                         num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, P,
+                         ns, lse_out, workspace);
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.causal = causal ? 1 : 0;
+  const int group = num_heads / cache->num_kv_heads;
+  const int gt = heads_per_chunk(group);
+  a.head_chunks = group / gt;
+  const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
+
+  // Rows of sequences with several query rows (chunked prefill).
+  if (max_query_len > 1) {
+    AttnArgs r = a;
+    r.mode = pkv::kModeVarlenRows;
+    r.partition_size = 0;
+    r.ws_o = nullptr;
+    r.ws_lse = nullptr;
+    int tslot = 0;
+    const bool timed = timing_begin(s, &tslot);
+    st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
+                              num_tokens, s);
+    if (timed) timing_end(s, tslot);
+    if (st != PKV_OK) return st;
+  }
+  // Sequences with one query row (decode rows), split over the key range.
+  a.mode = pkv::kModeVarlenOne;
+  st = launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt, gx,
+                            (unsigned)ns, num_seqs, s);
+  if (st != PKV_OK) return st;
+  if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
+  return st;
+}
+
+pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t num_seqs,
+                                 const int32_t* cu_seqlens_q, int32_t num_tokens,
+                                 int32_t max_query_len, int32_t max_seq_len,
+                                 const int64_t* slot_mapping, int64_t num_slots,
+                                 int64_t num_blocks, int32_t block_size, char* msg,
+                                 size_t msg_len) {
+  auto fail = [&](const char* fmt, ...) {
+    if (msg && msg_len) {
+      va_list ap;
+      va_start(ap, fmt);
+      vsnprintf(msg, msg_len, fmt, ap);
+      va_end(ap);
+    }
+    return PKV_ERR_METADATA;
+  };
+  if (msg && msg_len) msg[0] = '\0';
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail("bad sizes");
+  if (num_seqs > 0 && (!block_tables || !seq_lens)) return fail("NULL block_tables or seq_lens");
+  std::unordered_set<int32_t> used;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = seq_lens[s];
+    if (L < 0) return fail("seq_lens[%d] = %d is negative", s, L);
+    if (L > max_seq_len) return fail("seq_lens[%d] = %d exceeds max_seq_len %d", s, L, max_seq_len);
+    if ((int64_t)L > (int64_t)max_blocks_per_seq * block_size)
+      return fail("seq_lens[%d] = %d needs more than %d blocks", s, L, max_blocks_per_seq);
+    const int32_t nb = (L + block_size - 1) / block_size;
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t b = block_tables[(int64_t)s * max_blocks_per_seq + i];
+      if (b <= 0 || b >= num_blocks)
+        return fail("block_tables[%d][%d] = %d outside [1, %lld)", s, i, b, (long long)num_blocks);
+      if (!used.insert(b).second) return fail("block %d used twice (seq %d)", b, s);
+    }
+  }
+  if (cu_seqlens_q) {
+    if (cu_seqlens_q[0] != 0) return fail("cu_seqlens_q[0] = %d, expected 0", cu_seqlens_q[0]);
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t ql = cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+      if (ql < 0) return fail("cu_seqlens_q decreases at %d", s);
+      if (ql > max_query_len) return fail("query length %d of seq %d > max_query_len", ql, s);
+      if (ql > seq_lens[s]) return fail("query length %d of seq %d > seq_len %d", ql, s, seq_lens[s]);
+    }
+    if (cu_seqlens_q[num_seqs] != num_tokens)
+      return fail("cu_seqlens_q[-1] = %d, expected num_tokens %d", cu_seqlens_q[num_seqs],
+                  num_tokens);
+  }
+  if (slot_mapping) {
+    std::unordered_set<int64_t> slots;
+    const int64_t cap = num_blocks * block_size;
+    for (int64_t t = 0; t < num_slots; ++t) {
+      const int64_t sl = slot_mapping[t];
+      if (sl == -1) continue;
+      if (sl < 0 || sl >= cap) return fail("slot_mapping[%lld] = %lld outside the pool", (long long)t, (long long)sl);
+      if (!slots.insert(sl).second) return fail("slot %lld written twice", (long long)sl);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.enabled = enable != 0;
+  g_timing.head = g_timing.tail = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_timing_read(float* ms, int32_t cap) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  int32_t n = 0;
+  for (int64_t k = g_timing.head; k < g_timing.tail && n < cap; ++k) {
+    const int i = (int)(k % Timing::kCap);
+    if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess) return -1;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_timing.start[i], g_timing.stop[i]) != hipSuccess) return -1;
+    if (ms) ms[n] = t;
+    ++n;
+  }
+  g_timing.head = g_timing.tail;
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Work-item resolution shared by the attention and reduce kernels: maps a
+// workgroup's grid.z index to (sequence, query row, visible key range,
+// partitioning).  Both kernels must agree exactly, so it lives in one place.
+#pragma once
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+// Resolved work item of one workgroup.
+struct Item {
+  int seq;
+  int row;       // query row in q / out
+  int L_end;     // keys 0 .. L_end-1 are visible to this row
+  int nparts;    // partitions the row's key range is split into
+  int P;         // partition size in tokens
+};
+
+// Maps the workgroup to (sequence, row, key range).  Returns false when the
+// workgroup has nothing to do.  Identical logic runs in the reduce kernel.
+__device__ __forceinline__ bool resolve_item(const AttnArgs& a, int z, Item& it) {
+  int seq, row, qlen = 1, qidx = 0;
+  if (a.mode == kModeDecode) {
+    seq = z;
+    row = z;
+  } else if (a.mode == kModeVarlenOne) {
+    seq = z;
+    int qs = clamp_i(a.cu_seqlens_q[seq], 0, a.num_tokens);
+    int qe = clamp_i(a.cu_seqlens_q[seq + 1], 0, a.num_tokens);
+    if (qe - qs != 1) return false;
+    row = qs;
+  } else {
+    row = z;
+    // last sequence whose query range starts at or before this row
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (clamp_i(a.cu_seqlens_q[mid], 0, a.num_tokens) <= row) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    int qs = clamp_i(a.cu_seqlens_q[seq], 0, a.num_tokens);
+    int qe = clamp_i(a.cu_seqlens_q[seq + 1], 0, a.num_tokens);
+    qlen = qe - qs;
+    qidx = row - qs;
+    if (qidx < 0 || qidx >= qlen) return false;       // row outside every range
+    if (qlen == 1) return false;                       // owned by the one-row launch
+    if (a.skip_multi_row) return false;
+    if (qidx >= a.max_query_len) return false;         // beyond the host bound: not computed
+  }
+  int L = clamp_seq_len(a.seq_lens[seq], a.max_seq_len, a.max_blocks_per_seq, a.block_size);
+  int L_end = L;
+  if (a.causal && a.mode == kModeVarlenRows) L_end = min(L, max(0, qidx + L - qlen + 1));
+  it.seq = seq;
+  it.row = row;
+  it.L_end = L_end;
+  if (a.partition_size > 0 && a.mode != kModeVarlenRows) {
+    it.P = a.partition_size;
+    it.nparts = max(1, (L_end + it.P - 1) / it.P);
+  } else {
+    it.P = max(L_end, 1);
+    it.nparts = 1;
+  }
+  return true;
+}
+
+}  // namespace pkv

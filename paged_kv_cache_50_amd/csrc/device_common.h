@@ -1,0 +1,71 @@
+// Device helpers shared by the gfx950 kernels: bfloat16 conversions, DPP
+// lane reductions, 16-byte vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bfloat16 -> float32 is exact: the 16 stored bits are the high half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// One DPP move of a float within a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// DPP controls (GCN/CDNA encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // row_mirror: lane i <-> 15-i within 16
+
+// Sum over aligned groups of N lanes (N = 4, 8, 16, 32); every lane of the
+// group receives the total.  Within a row of 16 the butterfly is done with DPP.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float acc_log2(float x) { return log2f(x); }
+
+// Sequence length actually used: clamped into what the block table row and
+// the launch (max_seq_len) can address, so bad metadata never leads to an
+// out-of-bounds access.
+__device__ __forceinline__ int clamp_seq_len(int L, int max_seq_len, int max_blocks, int bs) {
+  int cap = min(max_seq_len, max_blocks * bs);
+  return min(max(L, 0), cap);
+}
+
+__device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+}  // namespace pkv

@@ -1,0 +1,74 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libpagedkv.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// How the attention kernels map grid.z to work.
+enum AttnMode : int32_t {
+  kModeDecode = 0,     // z = sequence; one query row per sequence (row = sequence)
+  kModeVarlenOne = 1,  // z = sequence; only sequences with exactly one query row
+  kModeVarlenRows = 2  // z = query row; only rows of sequences with > 1 query rows, no split
+};
+
+// Arguments of the attention kernels (passed by value).
+struct AttnArgs {
+  void* out;                       // [rows, num_heads, D], cache dtype
+  const void* q;                   // [rows, num_heads, D]
+  const void* k_cache;             // [num_blocks, BS, Hkv, D]
+  const void* v_cache;
+  const int32_t* block_tables;     // [num_seqs, max_blocks_per_seq]
+  const int32_t* seq_lens;         // [num_seqs]
+  const int32_t* cu_seqlens_q;     // [num_seqs + 1] or nullptr (decode)
+  float* lse_out;                  // [rows, num_heads] or nullptr
+  float* ws_o;                     // [num_splits, num_heads, num_seqs, D]
+  float* ws_lse;                   // [num_splits, num_heads, num_seqs]
+  int64_t block_stride;            // elements between blocks
+  int64_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t block_size;
+  int32_t num_seqs;
+  int32_t num_tokens;              // rows of q/out
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t max_seq_len;
+  int32_t max_query_len;
+  int32_t partition_size;          // tokens per split; 0 = one partition
+  int32_t num_splits;              // splits the workspace holds
+  int32_t head_chunks;             // query-head chunks per kv head
+  int32_t z_base;                  // offset added to blockIdx.z
+  int32_t mode;                    // AttnMode
+  int32_t causal;
+  int32_t skip_multi_row;          // kModeVarlenRows: 1 if another kernel owns multi-row seqs
+  float scale_log2;                // scale * log2(e)
+};
+
+struct KvWriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int64_t num_slots;               // num_blocks * block_size
+  int64_t block_stride_bytes;
+  int32_t block_size;
+  int32_t row_bytes;               // num_kv_heads * head_size * elem_bytes
+};
+
+// Launchers (return the launch error, hipSuccess on success).
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+// General VALU attention kernel: float32 or bfloat16 caches, head size 64/128,
+// block size 8/16/32, any GQA ratio.
+hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
+                            int heads_per_chunk, dim3 grid, hipStream_t stream);
+
+// Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
+hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,
+                                 hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,285 @@
+"""Thin ctypes binding of libpagedkv.so (declared in include/pagedkv.h).
+
+Only argument marshalling happens here: torch tensors supply device pointers,
+shapes and the current HIP stream; every step of the computation runs in the
+library's kernels.  There is no fallback: if the library is missing, or a
+tensor is not on the GPU, a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_OK = 0
+PKV_F32 = 0
+PKV_BF16 = 1
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
+                4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_METADATA", 7: "PKV_ERR_HIP"}
+
+
+class PkvKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("block_stride", ctypes.c_int64),
+    ]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+_vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_size_t)
+_SIGS = {
+    "pkv_kv_cache_write": (_i32, [ctypes.POINTER(PkvKvCache), _vp, _vp, _vp, _i64, _vp]),
+    "pkv_choose_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _i32, _vp,
+                                          _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_paged_attention_varlen": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                          _vp, _vp, _sz, _vp]),
+    "pkv_unsupported_reason": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_validate_metadata": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _i64, _i64,
+                                     _i32, ctypes.c_char_p, _sz]),
+    "pkv_timing_enable": (_i32, [_i32]),
+    "pkv_timing_read": (_i32, [ctypes.POINTER(ctypes.c_float), _i32]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpagedkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m paged_kv_cache_50_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pkv_status_string(status).decode()
+
+
+def unsupported_reason(dtype: int, head_size: int, block_size: int, num_heads: int,
+                       num_kv_heads: int) -> Optional[str]:
+    r = lib().pkv_unsupported_reason(dtype, head_size, block_size, num_heads, num_kv_heads)
+    return None if r is None else r.decode()
+
+
+def choose_partition_size(num_seqs, num_heads, num_kv_heads, max_seq_len, partition_size=0) -> int:
+    return int(lib().pkv_choose_partition_size(num_seqs, num_heads, num_kv_heads, max_seq_len,
+                                               partition_size))
+
+
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, max_seq_len,
+                    partition_size=0) -> int:
+    n = lib().pkv_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size,
+                                            max_seq_len, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(2, "workspace_bytes")
+    return int(n)
+
+
+# --------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU fallback)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def cache_descriptor(k_cache, v_cache) -> PkvKvCache:
+    """Describe [num_blocks, block_size, num_kv_heads, head_size] caches whose
+    blocks may be strided (dense inside a block)."""
+    _require_gpu(k_cache, v_cache)
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same 4-D shape and dtype")
+    nb, bs, hkv, d = k_cache.shape
+    for t in (k_cache, v_cache):
+        if t.stride(3) != 1 or t.stride(2) != d or t.stride(1) != hkv * d:
+            raise ValueError("cache blocks must be dense [block_size, num_kv_heads, head_size]")
+    if k_cache.stride(0) != v_cache.stride(0):
+        raise ValueError("k_cache and v_cache must share the block stride")
+    return PkvKvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
+                      _dtype_code(k_cache), k_cache.stride(0) if nb > 1 else 0)
+
+
+def _check(status: int, what: str):
+    if status != PKV_OK:
+        raise PagedKVError(status, what)
+
+
+def kv_cache_write(k_cache, v_cache, key, value, slot_mapping) -> None:
+    """Scatter key/value rows [>= T, Hkv, D] into the caches at slot_mapping
+    (int64 [T], -1 = skip).  In place, asynchronous on the current stream."""
+    torch = _torch()
+    _require_gpu(key, value, slot_mapping)
+    desc = cache_descriptor(k_cache, v_cache)
+    if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous int64 tensor")
+    for t in (key, value):
+        if not t.is_contiguous() or t.dtype != k_cache.dtype or tuple(t.shape[1:]) != tuple(k_cache.shape[2:]):
+            raise ValueError("key/value must be contiguous [T, num_kv_heads, head_size] in the cache dtype")
+    T = slot_mapping.shape[0]
+    if key.shape[0] < T or value.shape[0] < T:
+        raise ValueError("key/value hold fewer rows than slot_mapping")
+    _check(lib().pkv_kv_cache_write(ctypes.byref(desc), key.data_ptr(), value.data_ptr(),
+                                    slot_mapping.data_ptr(), T, _stream(key)), "kv_cache_write")
+
+
+def _workspace(ws, need: int, device):
+    torch = _torch()
+    if need == 0:
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _meta(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                           max_seq_len: int, partition_size: int = 0, workspace=None,
+                           lse_out=None):
+    """Decode attention, one query row per sequence.  out/q: [S, Hq, D].
+    max_seq_len is a host-side upper bound of seq_lens (no device sync)."""
+    _require_gpu(out, q, block_tables, seq_lens, workspace, lse_out)
+    desc = cache_descriptor(k_cache, v_cache)
+    _meta(block_tables, "block_tables")
+    _meta(seq_lens, "seq_lens")
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache dtype")
+    S, Hq, D = q.shape
+    if out.shape != q.shape or D != k_cache.shape[3] or block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("shape mismatch")
+    if lse_out is not None and (tuple(lse_out.shape) != (S, Hq) or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must be a contiguous float32 [num_seqs, num_heads]")
+    need = workspace_bytes(S, Hq, desc.num_kv_heads, D, max_seq_len, partition_size)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    _check(lib().pkv_paged_attention_decode(
+        out.data_ptr(), q.data_ptr(), ctypes.byref(desc), block_tables.data_ptr(),
+        block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
+        int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
+        "paged_attention_decode")
+    return out
+
+
+def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
+                           scale: float, max_query_len: int, max_seq_len: int, causal: bool = True,
+                           partition_size: int = 0, workspace=None, lse_out=None):
+    """Variable-length attention over a flattened batch (q/out [T, Hq, D])."""
+    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out)
+    desc = cache_descriptor(k_cache, v_cache)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        _meta(t, n)
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache dtype")
+    T, Hq, D = q.shape
+    S = seq_lens.shape[0]
+    if out.shape != q.shape or cu_seqlens_q.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch")
+    if lse_out is not None and (tuple(lse_out.shape) != (T, Hq) or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must be a contiguous float32 [num_tokens, num_heads]")
+    need = workspace_bytes(S, Hq, desc.num_kv_heads, D, max_seq_len, partition_size)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    _check(lib().pkv_paged_attention_varlen(
+        out.data_ptr(), q.data_ptr(), ctypes.byref(desc), cu_seqlens_q.data_ptr(),
+        seq_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], S, T, Hq,
+        int(max_query_len), int(max_seq_len), float(scale), 1 if causal else 0,
+        int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
+        "paged_attention_varlen")
+    return out
+
+
+def validate_metadata(block_tables, seq_lens, max_seq_len, num_blocks, block_size,
+                      cu_seqlens_q=None, num_tokens=0, max_query_len=0, slot_mapping=None):
+    """Check host copies of the metadata (numpy arrays or CPU tensors).
+    Returns "" when valid, else the first problem found."""
+    import numpy as np
+
+    def arr(x, dt):
+        if x is None:
+            return None
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(x, dtype=dt)
+
+    bt = arr(block_tables, np.int32)
+    sl = arr(seq_lens, np.int32)
+    cu = arr(cu_seqlens_q, np.int32)
+    sm = arr(slot_mapping, np.int64)
+    msg = ctypes.create_string_buffer(256)
+    st = lib().pkv_validate_metadata(
+        bt.ctypes.data, bt.shape[1], sl.ctypes.data, sl.shape[0],
+        None if cu is None else cu.ctypes.data, int(num_tokens), int(max_query_len),
+        int(max_seq_len), None if sm is None else sm.ctypes.data,
+        0 if sm is None else sm.shape[0], int(num_blocks), int(block_size), msg, 256)
+    return "" if st == PKV_OK else (msg.value.decode() or "invalid metadata")
+
+
+def timing_enable(enable: bool = True) -> None:
+    _check(lib().pkv_timing_enable(1 if enable else 0), "timing_enable")
+
+
+def timing_read(cap: int = 4096):
+    """Durations (ms) of the main attention kernel of each call since the
+    last read; waits for them to finish."""
+    buf = (ctypes.c_float * cap)()
+    n = lib().pkv_timing_read(buf, cap)
+    if n < 0:
+        raise PagedKVError(7, "timing_read")
+    return [buf[i] for i in range(n)]
+
+
+def default_scale(head_size: int) -> float:
+    return 1.0 / math.sqrt(head_size)
