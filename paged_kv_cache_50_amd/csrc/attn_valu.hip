@@ -65,8 +65,7 @@ __device__ __forceinline__ float frag_dot<uint16_t>(const u32x4& k, const u32x4&
   float s = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k[w]),
-                                        __builtin_bit_cast(bf16x2_t, q[w]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k[w]), as_bf16x2(q[w]), s, false);
   return s;
 }
 

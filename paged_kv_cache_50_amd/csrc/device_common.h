@@ -15,6 +15,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Reinterpret a 32-bit word as two bfloat16 lanes.  Takes the word by value:
+// applying __builtin_bit_cast directly to a vector-element subscript (v[i])
+// reads element 0 with this compiler, so callers must go through here.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2_t, x); }
+
 // bfloat16 -> float32 is exact: the 16 stored bits are the high half.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
