@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <unordered_set>
@@ -59,6 +60,21 @@ int64_t block_stride_elems(const pkv_kv_cache* c) {
                          : (int64_t)c->block_size * c->num_kv_heads * c->head_size;
 }
 
+// Decode kernel choice.  The matrix-core kernel pays off once a kv head
+// serves several query heads (a dense g x tokens contraction); with one query
+// head per kv head the work is a matrix-vector product and stays on the VALU.
+// PKV_DECODE_KERNEL=valu|mfma forces one variant (for A/B measurements).
+constexpr int kMfmaMinGroup = 4;
+constexpr int kMfmaTokensPerWg = 2048;
+
+bool use_mfma_decode(const pkv_kv_cache* c, int group) {
+  if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
+  static const char* force = std::getenv("PKV_DECODE_KERNEL");
+  if (force && std::strcmp(force, "valu") == 0) return false;
+  if (force && std::strcmp(force, "mfma") == 0) return true;
+  return group >= kMfmaMinGroup;
+}
+
 // Query heads handled together by one workgroup of the VALU kernel.
 int heads_per_chunk(int group) {
   for (int gt : {8, 4, 2, 1})
@@ -103,11 +119,46 @@ pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_
   for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
     a.z_base = (int32_t)z0;
     const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
-    if (pkv::launch_attn_valu(a, dtype, head_size, block_size, gt, dim3(gx, gy, gz), st) !=
+    if (pkv::launch_attn_valu(a, dtype, head_size, block_size, gt, dim3(gx, gz, gy), st) !=
         hipSuccess)
       return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+// One-row attention (decode, or the one-row sequences of a varlen batch):
+// picks the kernel, the head chunking and the partitions per workgroup (left
+// in `a` for the split merge that follows), launches over all z.
+pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, int64_t z_total,
+                          hipStream_t st) {
+  const int group = a.num_heads / cache->num_kv_heads;
+  if (use_mfma_decode(cache, group)) {
+    a.head_chunks = (group + 15) / 16;
+    // a workgroup streams about kMfmaTokensPerWg tokens: consecutive
+    // partitions share its queries and block-table row, and its fixed cost
+    // (queries, first loads, merge) is paid once per stream
+    // Small partitions: a workgroup covers 4 of them, one per wave (merged in
+    // LDS, then across workgroups by the split merge); larger ones: the waves
+    // share the workgroup's partitions tile by tile.
+    a.wave_per_part = (a.partition_size > 0 && a.partition_size <= kMfmaTokensPerWg / 4) ? 1 : 0;
+    a.parts_per_wg = a.partition_size <= 0 ? 1
+                     : a.wave_per_part ? 4
+                     : std::max(1, kMfmaTokensPerWg / a.partition_size);
+    const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
+    const unsigned gparts = (gy + a.parts_per_wg - 1) / a.parts_per_wg;
+    for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
+      a.z_base = (int32_t)z0;
+      const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
+      if (pkv::launch_attn_mfma_decode(a, cache->block_size, dim3(gx, gz, gparts), st) != hipSuccess)
+        return PKV_ERR_HIP;
+    }
+    a.z_base = 0;
+    return PKV_OK;
+  }
+  const int gt = heads_per_chunk(group);
+  a.head_chunks = group / gt;
+  return launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt,
+                              (unsigned)(cache->num_kv_heads * a.head_chunks), gy, z_total, st);
 }
 
 pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
@@ -153,6 +204,8 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.partition_size = nsplits > 1 ? P : 0;
   a.num_splits = nsplits;
   a.head_chunks = 1;
+  a.parts_per_wg = 1;
+  a.wave_per_part = 0;
   a.z_base = 0;
   a.mode = pkv::kModeDecode;
   a.causal = 0;
@@ -269,14 +322,9 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                          num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
   a.mode = pkv::kModeDecode;
-  const int group = num_heads / cache->num_kv_heads;
-  const int gt = heads_per_chunk(group);
-  a.head_chunks = group / gt;
   int tslot = 0;
   const bool timed = timing_begin(s, &tslot);
-  st = launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt,
-                            (unsigned)(cache->num_kv_heads * a.head_chunks), (unsigned)ns, num_seqs,
-                            s);
+  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
   if (timed) timing_end(s, tslot);
   if (st != PKV_OK) return st;
   if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
@@ -339,8 +387,7 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
   }
   // Sequences with one query row (decode rows), split over the key range.
   a.mode = pkv::kModeVarlenOne;
-  st = launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt, gx,
-                            (unsigned)ns, num_seqs, s);
+  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
   if (st != PKV_OK) return st;
   if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
   return st;

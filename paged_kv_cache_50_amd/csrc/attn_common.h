@@ -14,6 +14,7 @@ struct Item {
   int row;       // query row in q / out
   int L_end;     // keys 0 .. L_end-1 are visible to this row
   int nparts;    // partitions the row's key range is split into
+  int nranges;   // workgroup ranges of parts_per_wg partitions (one partial each)
   int P;         // partition size in tokens
 };
 
@@ -57,9 +58,12 @@ __device__ __forceinline__ bool resolve_item(const AttnArgs& a, int z, Item& it)
   if (a.partition_size > 0 && a.mode != kModeVarlenRows) {
     it.P = a.partition_size;
     it.nparts = max(1, (L_end + it.P - 1) / it.P);
+    // partials are kept per workgroup range of parts_per_wg partitions
+    it.nranges = (it.nparts + a.parts_per_wg - 1) / a.parts_per_wg;
   } else {
     it.P = max(L_end, 1);
     it.nparts = 1;
+    it.nranges = 1;
   }
   return true;
 }

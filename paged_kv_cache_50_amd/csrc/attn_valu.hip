@@ -19,8 +19,8 @@
 //   running sum l, fp32 accumulator) over the tokens it sees, so the hot loop
 //   needs only the in-row dot-product reduction (DPP); the 4*RPW states are
 //   merged once at the end (shuffles inside a wave, LDS across waves).
-//   Block ids are read with wave-uniform (scalar) loads; the next step's
-//   K/V loads are issued before the current step is computed.
+//   Block ids are read with wave-uniform (scalar) loads one step ahead; the
+//   next step's K/V loads are issued before the current step is computed.
 //   Tokens past the partition end are loaded from a clamped, in-bounds slot
 //   and removed by select (never by multiply), so stale NaNs in unused slots
 //   cannot leak into the result.
@@ -114,12 +114,12 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   __shared__ float s_l[kWaves][GT];
 
   Item it;
-  if (!resolve_item(a, blockIdx.z + a.z_base, it)) return;
-  const int part = blockIdx.y;
+  if (!resolve_item(a, blockIdx.y + a.z_base, it)) return;
+  const int part = blockIdx.z;  // partitions on the slowest axis: empty ones dispatch last
   if (part >= it.nparts) return;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int group = a.num_heads / a.num_kv_heads;
@@ -152,30 +152,33 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   const int64_t max_blk = a.num_blocks - 1;
   const int nsteps = (pend > pstart) ? (pend - pstart + TPS - 1) / TPS : 0;
 
-  u32x4 kcur[kNls], vcur[kNls], knxt[kNls], vnxt[kNls];
+  u32x4 kA[kNls], vA[kNls], kB[kNls], vB[kNls];   // ping-pong step buffers
 
-  // Issue the loads of one wave step.  The block of each load is wave
-  // uniform (a load covers RPW consecutive tokens inside one block); a load
-  // wholly past the partition end reads the last valid block instead.
-  auto issue = [&](int step, u32x4* kr, u32x4* vr) {
+  // Block ids of one wave step (wave uniform, scalar loads), fetched one
+  // step early so that issuing a step's loads never waits on them.  A step
+  // spans NBS blocks; a load covers RPW consecutive tokens inside one block.
+  constexpr int NBS = TPS > BS ? TPS / BS : 1;
+  const int last_bi = (pend - 1) / BS;
+  auto fetch_ids = [&](int step, int64_t* ids) {
+    const int t0 = pstart + step * TPS;
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+      const int bi = __builtin_amdgcn_readfirstlane(min(t0 / BS + b, last_bi));
+      ids[b] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+    }
+  };
+  // Tokens past the partition end read a slot of a valid block (in bounds).
+  auto issue = [&](int step, const int64_t* ids, u32x4* kr, u32x4* vr) {
 #pragma unroll
     for (int i = 0; i < kNls; ++i) {
-      int t0 = pstart + step * TPS + i * RPW;                        // wave uniform
-      int tb = __builtin_amdgcn_readfirstlane(min(t0, pend - 1));
-      int blk = bt[tb / BS];
-      int64_t phys = min((int64_t)max(blk, 0), max_blk);
-      int64_t off = phys * a.block_stride + (int64_t)(t0 % BS) * tok_stride + lane_off;
+      const int t0 = pstart + step * TPS + i * RPW;                  // wave uniform
+      const int64_t off = ids[(i * RPW) / BS] + (int64_t)(t0 % BS) * tok_stride + lane_off;
       kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + off));
       vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + off));
     }
   };
 
-  int step = wave;
-  if (step < nsteps) issue(step, kcur, vcur);
-  for (; step < nsteps; step += kWaves) {
-    const bool more = step + kWaves < nsteps;
-    if (more) issue(step + kWaves, knxt, vnxt);
-
+  auto compute = [&](int step, const u32x4* K, const u32x4* V) {
     const int tbase = pstart + step * TPS + r;
     float s[kNls][GT];
 #pragma unroll
@@ -183,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
       const bool valid = tbase + i * RPW < pend;
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float d = group_sum<LPR>(frag_dot<T>(kcur[i], qf[h]));
+        float d = group_sum<LPR>(frag_dot<T>(K[i], qf[h]));
         s[i][h] = valid ? d * a.scale_log2 : -INFINITY;
       }
     }
@@ -191,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kNls; ++i) {
       const bool valid = tbase + i * RPW < pend;
-      frag_widen<T>(vcur[i], vf[i]);
+      frag_widen<T>(V[i], vf[i]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) vf[i][e] = valid ? vf[i][e] : 0.f;
     }
@@ -220,13 +223,30 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
         acc[h][e] = o;
       }
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < kNls; ++i) {
-        kcur[i] = knxt[i];
-        vcur[i] = vnxt[i];
-      }
+  };
+
+  // Two steps in flight per wave; buffers alternate instead of being copied.
+  int64_t ids[NBS];
+  int step = wave;
+  if (step < nsteps) {
+    fetch_ids(step, ids);
+    issue(step, ids, kA, vA);
+    if (step + kWaves < nsteps) fetch_ids(step + kWaves, ids);
+  }
+  while (step < nsteps) {
+    if (step + kWaves < nsteps) {
+      issue(step + kWaves, ids, kB, vB);
+      if (step + 2 * kWaves < nsteps) fetch_ids(step + 2 * kWaves, ids);
     }
+    compute(step, kA, vA);
+    step += kWaves;
+    if (step >= nsteps) break;
+    if (step + kWaves < nsteps) {
+      issue(step + kWaves, ids, kA, vA);
+      if (step + 2 * kWaves < nsteps) fetch_ids(step + 2 * kWaves, ids);
+    }
+    compute(step, kB, vB);
+    step += kWaves;
   }
 
   // Merge the RPW row states of this wave (rows are LPR lanes apart).
@@ -279,7 +299,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
       Ls = fmaf(s_l[w][h], f, Ls);
     }
     const int head = h0 + h;
-    if (it.nparts == 1) {
+    if (it.nranges == 1) {
       const float v = Ls > 0.f ? O / Ls : 0.f;
       store_out<T>(a.out, ((int64_t)it.row * a.num_heads + head) * D + d, v);
       if (d == 0 && a.lse_out)

@@ -71,6 +71,15 @@ __device__ __forceinline__ int clamp_seq_len(int L, int max_seq_len, int max_blo
   return min(max(L, 0), cap);
 }
 
+// Wave-uniform read of read-only metadata through the scalar cache.  Going
+// through the constant address space makes the compiler emit s_load (waited
+// on with lgkmcnt) instead of a vector load; a vector load here would make
+// the next wait for it also drain every K/V load still in flight.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t* p, int64_t i) {
+  return ((const_i32*)(p))[i];
+}
+
 __device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
 }  // namespace pkv

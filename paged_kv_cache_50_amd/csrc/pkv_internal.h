@@ -39,6 +39,9 @@ struct AttnArgs {
   int32_t partition_size;          // tokens per split; 0 = one partition
   int32_t num_splits;              // splits the workspace holds
   int32_t head_chunks;             // query-head chunks per kv head
+  int32_t parts_per_wg;            // consecutive partitions one workgroup covers (>= 1);
+                                   // the workspace holds one partial per workgroup range
+  int32_t wave_per_part;           // 1: wave w of a workgroup owns partition w of its range
   int32_t z_base;                  // offset added to blockIdx.z
   int32_t mode;                    // AttnMode
   int32_t causal;
@@ -66,6 +69,12 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 // block size 8/16/32, any GQA ratio.
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream);
+
+// Grouped-query decode on the matrix cores: bfloat16, head size 128, up to 16
+// query heads per kv-head chunk (head_chunks = ceil(group / 16)).
+// grid = (num_kv_heads * head_chunks, sequences, ceil(partitions / parts_per_wg)).
+hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, dim3 grid,
+                                   hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,
