@@ -75,6 +75,14 @@ bool use_mfma_decode(const pkv_kv_cache* c, int group) {
   return group >= kMfmaMinGroup;
 }
 
+// Prefill kernel choice: the matrix-core kernel for bfloat16 / head 128;
+// PKV_PREFILL_KERNEL=valu forces the generic row kernel (A/B measurements).
+bool use_mfma_prefill(const pkv_kv_cache* c) {
+  if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
+  static const char* force = std::getenv("PKV_PREFILL_KERNEL");
+  return !(force && std::strcmp(force, "valu") == 0);
+}
+
 // Query heads handled together by one workgroup of the VALU kernel.
 int heads_per_chunk(int group) {
   for (int gt : {8, 4, 2, 1})
@@ -206,6 +214,7 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.head_chunks = 1;
   a.parts_per_wg = 1;
   a.wave_per_part = 0;
+  a.head_chunks_gc = 1;
   a.z_base = 0;
   a.mode = pkv::kModeDecode;
   a.causal = 0;
@@ -380,8 +389,23 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
     r.ws_lse = nullptr;
     int tslot = 0;
     const bool timed = timing_begin(s, &tslot);
-    st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
-                              num_tokens, s);
+    if (use_mfma_prefill(cache)) {
+      int gc = 16;
+      while (group % gc) gc >>= 1;
+      r.head_chunks_gc = gc;
+      const int rows_per_wg = 16 * (16 / gc);
+      const unsigned qtiles = (unsigned)((max_query_len + rows_per_wg - 1) / rows_per_wg);
+      const unsigned gy = (unsigned)(cache->num_kv_heads * (group / gc));
+      for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
+        r.z_base = (int32_t)z0;
+        const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, num_seqs - z0);
+        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, dim3(qtiles, gy, gz), s) != hipSuccess)
+          st = PKV_ERR_HIP;
+      }
+    } else {
+      st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
+                                num_tokens, s);
+    }
     if (timed) timing_end(s, tslot);
     if (st != PKV_OK) return st;
   }

@@ -1,0 +1,275 @@
+// Chunked-prefill paged attention on the matrix cores (gfx950 MFMA).
+//
+// Rows of sequences with several query rows: a prefill chunk of q_len new
+// tokens attends to the sequence's seq_len cached tokens (its own new tokens
+// already written by the slot write), query row i sitting at absolute
+// position i + seq_len - q_len and, when causal, seeing keys j <= that
+// position (vLLM book, ch. 6 "Branche de masque" for the bottom-right
+// alignment; "Structure des métadonnées" for query_start_loc / seq_lens;
+// «Khám phá vLLM», "Chạy forward pass", for the flattened batch).
+//
+// Work decomposition: a workgroup of 8 waves owns 16 column tiles of one kv
+// head's query-head group, a column tile being 16 consecutive query rows of
+// one query head; wave w owns column tiles 2w and 2w+1.  With g query heads
+// per kv head (chunks of GC <= 16 heads), the workgroup covers 16 / GC row
+// blocks of 16 rows.  The key range [0, kv_end) is walked in 32-token tiles
+// that all 512 threads load cooperatively (one 16-byte chunk of K and one of
+// V per thread: whole 256-byte token rows) into a double-buffered LDS ring,
+// one barrier per tile; the next tile's loads are in flight while the
+// current one is computed.  Per wave and tile:
+//   S^T[32 tok x 16 rows] = K . Q^T        (8 A reads from LDS, 8 MFMAs per column tile)
+//   online softmax per column (= query row), causal mask by select
+//   O^T[128 x 16] += V^T . P^T             (V^T via ds_read_b64_tr_b16, shared by both tiles)
+// Tiles lying wholly above a wave's rows on the causal diagonal are skipped.
+#include "attn_common.h"
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = 128;
+constexpr int kTile = 32;
+constexpr int kKBytes = kTile * kD * 2;          // 8 KiB
+constexpr int kVPitch = kD * 2 + 16;
+constexpr int kVBytes = kTile * kVPitch;
+constexpr int kStageBytes = kKBytes + kVBytes;
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + ((c ^ (t & 15)) << 4); }
+
+__device__ __forceinline__ float xmax16_32(float x) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
+}
+__device__ __forceinline__ float xsum16_32(float x) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(p16[0]) + __int_as_float(p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p32[0]) + __int_as_float(p32[1]);
+}
+
+template <int BS>
+__global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_lds[2 * kStageBytes];
+
+  const int seq = blockIdx.z + a.z_base;
+  const int qs = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq), 0, a.num_tokens);
+  const int qe = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq + 1), 0, a.num_tokens);
+  const int q_len = min(qe - qs, a.max_query_len);
+  if (qe - qs <= 1) return;                          // one-row sequences: decode kernels
+  const int GC = a.head_chunks_gc;                   // query heads per column group
+  const int R = 16 / GC;                             // row blocks per workgroup
+  const int q0 = blockIdx.x * 16 * R;
+  if (q0 >= q_len) return;
+  const int group = a.num_heads / a.num_kv_heads;
+  const int chunks = group / GC;
+  const int kvh = blockIdx.y / chunks;
+  const int hbase = kvh * group + (blockIdx.y % chunks) * GC;
+  const int L = clamp_seq_len(load_uniform_i32(a.seq_lens, seq), a.max_seq_len,
+                              a.max_blocks_per_seq, BS);
+  const int off = L - (qe - qs);                     // absolute position of row i = i + off
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+
+  // key range of the workgroup
+  const int q_last = min(q0 + 16 * R, q_len) - 1;
+  const int kv_end = a.causal ? max(0, min(L, q_last + off + 1)) : L;
+  const int ntiles = (kv_end + kTile - 1) / kTile;
+
+  // this wave's two column tiles: (row block, head)
+  int rowb[2], head[2];
+  bool live[2];
+  int wave_last_pos = -1;                            // largest key position this wave may see
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ct = 2 * wave + c;
+    rowb[c] = q0 + (ct / GC) * 16;
+    head[c] = hbase + ct % GC;
+    live[c] = rowb[c] < q_len;
+    if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
+  }
+  if (!a.causal) wave_last_pos = L - 1;
+
+  // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
+  bf16x8_t qb[2][4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = rowb[c] + n;
+    const bool ok = live[c] && row < q_len;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(qp + (4 * j + kg) * 8);
+      qb[c][j] = as_bf16x8(v);
+    }
+  }
+
+  f32x4 o[2][8];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) o[c][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = -INFINITY;
+    lsum[c] = 0.f;
+  }
+
+  // cooperative tile loads: thread -> (token tid/16, chunk tid%16); each wave
+  // covers 4 consecutive tokens, which share a block (block ids wave uniform)
+  const int ltok = tid >> 4;
+  const int lchunk = tid & 15;
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
+  const uint32_t head_off = (uint32_t)kvh * kD;
+  const int64_t max_blk = a.num_blocks - 1;
+  const int last_bi = max(0, kv_end - 1) / BS;
+
+  auto fetch_id = [&](int t) -> int64_t {
+    const int bi = __builtin_amdgcn_readfirstlane(min((t * kTile + 4 * wave) / BS, last_bi));
+    return min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+  };
+  u32x4 kreg, vreg;
+  auto issue = [&](int t, int64_t boff) {
+    const uint32_t lo = (uint32_t)((t * kTile + ltok) % BS) * tok_stride + head_off + lchunk * 8;
+    kreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + boff + lo));
+    vreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + boff + lo));
+  };
+  auto stage = [&](int t, char* buf) {
+    u32x4 v = vreg;
+    if (t * kTile + ltok >= kv_end) v = u32x4{0u, 0u, 0u, 0u};   // never multiply stale data
+    *reinterpret_cast<u32x4*>(buf + ktile_off(ltok, lchunk)) = kreg;
+    *reinterpret_cast<u32x4*>(buf + kKBytes + ltok * kVPitch + lchunk * 16) = v;
+  };
+
+  auto compute = [&](int t, const char* buf) {
+    const int j0 = t * kTile;
+    if (j0 > wave_last_pos) return;                  // wholly above this wave's diagonal
+    const char* kl = buf;
+    const char* vl = buf + kKBytes;
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sacc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + ktile_off(tt * 16 + n, 4 * j + kg)));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][j], sacc[c][tt], 0, 0, 0);
+      }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int qpos = rowb[c] + n + off;            // this lane's column = query row
+      const int lim = a.causal ? min(qpos, kv_end - 1) : kv_end - 1;
+      float s[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + tt * 16 + 4 * kg + i;
+          s[tt * 4 + i] = (j <= lim) ? sacc[c][tt][i] * a.scale_log2 : -INFINITY;
+        }
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+      mx = xmax16_32(mx);
+      const float mn = fmaxf(m[c], mx);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m[c] - mref);
+      m[c] = mn;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(s[e] - mref);
+        psum += p;
+        pb[c][e] = (__bf16)p;
+      }
+      lsum[c] = lsum[c] * alpha + psum;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
+    }
+    const int jj = n >> 2, q4 = n & 3;
+    const char* r0 = vl + (4 * kg + jj) * kVPitch + q4 * 8;
+    const char* r1 = r0 + 16 * kVPitch;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r0 + jd * 32));
+      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r1 + jd * 32));
+      bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        o[c][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[c], o[c][jd], 0, 0, 0);
+    }
+  };
+
+  // double-buffered key/value tiles, one barrier per tile
+  int64_t boff = 0;
+  if (ntiles > 0) {
+    boff = fetch_id(0);
+    issue(0, boff);
+    if (ntiles > 1) boff = fetch_id(1);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    char* buf = s_lds + (t & 1) * kStageBytes;
+    stage(t, buf);
+    if (t + 1 < ntiles) {
+      issue(t + 1, boff);
+      if (t + 2 < ntiles) boff = fetch_id(t + 2);
+    }
+    __syncthreads();
+    compute(t, buf);
+  }
+
+  // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float ls = xsum16_32(lsum[c]);
+    const int row = rowb[c] + n;
+    if (!live[c] || row >= q_len) continue;
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const uint32_t w0 = pack_bf16x2(o[c][jd][0] * inv, o[c][jd][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[c][jd][2] * inv, o[c][jd][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * jd + 4 * kg) = make_uint2(w0, w1);
+    }
+    if (kg == 0 && a.lse_out)
+      a.lse_out[(int64_t)(qs + row) * a.num_heads + head[c]] =
+          ls > 0.f ? (m[c] + acc_log2(ls)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, dim3 grid,
+                                    hipStream_t stream) {
+  switch (block_size) {
+    case 8: hipLaunchKernelGGL((attn_mfma_prefill_kernel<8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((attn_mfma_prefill_kernel<16>), grid, dim3(kThreads), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((attn_mfma_prefill_kernel<32>), grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

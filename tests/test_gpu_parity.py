@@ -303,3 +303,58 @@ def test_gqa_equals_expanded_mha_gpu():
     dw2 = G.DevWorkload(w2)
     G.run(dw2)
     G.assert_close(G.dev_to_f64(dw2.out), gqa, "bf16", "gqa vs expanded mha")
+
+
+# ------------------------------------------------------------------ chunked prefill shapes
+
+@pytest.mark.parametrize("hq,hkv,bs,causal", [(32, 8, 32, True), (8, 8, 16, True), (16, 8, 8, True),
+                                              (64, 8, 16, False), (16, 1, 32, True), (24, 4, 16, True)])
+def test_parity_prefill_shapes(hq, hkv, bs, causal):
+    """Prefill chunks of several lengths (one tile, several tiles, ragged
+    tails), with and without prior context, mixed with decode rows."""
+    ctx = [0, 37, 300, 5, 0, 129]
+    ql = [70, 1, 33, 200, 1, 17]
+    w = W.make_varlen("prefill", ctx, ql, hq, hkv, 128, bs, "bf16", seed=hq + bs + causal,
+                      causal=causal)
+    _announce(f"prefill hq={hq} hkv={hkv} bs={bs} causal={causal}")
+    dw = G.DevWorkload(w)
+    G.run(dw)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"prefill {hq}/{hkv} bs={bs} causal={causal}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "prefill")
+
+
+def test_prefill_needle_bit_exact():
+    """Causal chunk whose rows each see a needle key placed at a row-dependent
+    position at or before the row's own position: exact block indexing and
+    bottom-right alignment in the prefill path."""
+    ctx, qlen = 90, 40
+    w = W.make_varlen("pneedle", [ctx], [qlen], 8, 2, 128, 16, "bf16", seed=3, causal=True)
+    kc, vc = G.oracle_inputs(w)          # caches after the slot write
+    valid = w.valid_slot_mask()
+    kc[valid, :, 0] = 0
+    b64 = np.uint16(0x4280)
+    L = ctx + qlen
+    # row i (absolute position ctx + i) gets needle at key position i * 3 (<= ctx + i)
+    w.q[:] = 0
+    for i in range(qlen):
+        j = 3 * i
+        kc[w.block_tables[0, j // 16], j % 16, :, 0] = b64
+    # a key at position p is seen by row i iff p <= ctx + i; give each row a
+    # distinct needle direction so rows do not see each other's needles
+    kc[valid, :, :] = kc[valid, :, :]
+    for i in range(qlen):
+        j = 3 * i
+        kc[w.block_tables[0, j // 16], j % 16, :, :] = 0
+        kc[w.block_tables[0, j // 16], j % 16, :, 1 + i] = b64
+        w.q[i, :, 1 + i] = b64
+    # write the modified cache directly and skip the slot write
+    w.k_cache, w.v_cache = kc, vc
+    w.slot_mapping = None
+    dw = G.DevWorkload(w)
+    G.run(dw, write=False)
+    got = G.dev_to_bits(dw.out)
+    for i in range(qlen):
+        j = 3 * i
+        for h in range(8):
+            assert np.array_equal(got[i, h], vc[w.block_tables[0, j // 16], j % 16, h // 4]), (i, h)
