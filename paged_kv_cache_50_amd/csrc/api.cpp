@@ -390,10 +390,10 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
     int tslot = 0;
     const bool timed = timing_begin(s, &tslot);
     if (use_mfma_prefill(cache)) {
-      int gc = 16;
+      int gc = 8;
       while (group % gc) gc >>= 1;
       r.head_chunks_gc = gc;
-      const int rows_per_wg = 16 * (16 / gc);
+      const int rows_per_wg = 16 * (8 / gc);
       const unsigned qtiles = (unsigned)((max_query_len + rows_per_wg - 1) / rows_per_wg);
       const unsigned gy = (unsigned)(cache->num_kv_heads * (group / gc));
       for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {

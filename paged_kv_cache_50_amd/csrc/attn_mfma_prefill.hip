@@ -8,19 +8,30 @@
 // alignment; "Structure des métadonnées" for query_start_loc / seq_lens;
 // «Khám phá vLLM», "Chạy forward pass", for the flattened batch).
 //
-// Work decomposition: a workgroup of 8 waves owns 16 column tiles of one kv
+// Work decomposition: a workgroup of 4 waves owns 8 column tiles of one kv
 // head's query-head group, a column tile being 16 consecutive query rows of
 // one query head; wave w owns column tiles 2w and 2w+1.  With g query heads
-// per kv head (chunks of GC <= 16 heads), the workgroup covers 16 / GC row
-// blocks of 16 rows.  The key range [0, kv_end) is walked in 32-token tiles
-// that all 512 threads load cooperatively (one 16-byte chunk of K and one of
-// V per thread: whole 256-byte token rows) into a double-buffered LDS ring,
-// one barrier per tile; the next tile's loads are in flight while the
-// current one is computed.  Per wave and tile:
+// per kv head (chunks of GC <= 8 heads), the workgroup covers 8 / GC row
+// blocks of 16 rows.  Several workgroups share a CU, so their MFMA and
+// softmax phases interleave.  The key range [0, kv_end) is walked in 32-token
+// tiles that the 256 threads load cooperatively (two 16-byte chunks of K and
+// two of V per thread: whole 256-byte token rows) straight into a 4-stage LDS
+// ring with global_load_lds (no registers held), one barrier per tile, three
+// tiles in flight ahead of the one being computed.  The direct loads write
+// lane l's 16 bytes at offset 16*l, so the swizzled LDS layouts (16-byte slot
+// c ^ f(row)) are produced by choosing which chunk each lane fetches.  Tokens
+// past the key range load the last valid token (finite data; their
+// probabilities are exactly 0).  Per wave and tile:
 //   S^T[32 tok x 16 rows] = K . Q^T        (8 A reads from LDS, 8 MFMAs per column tile)
 //   online softmax per column (= query row), causal mask by select
 //   O^T[128 x 16] += V^T . P^T             (V^T via ds_read_b64_tr_b16, shared by both tiles)
-// Tiles lying wholly above a wave's rows on the causal diagonal are skipped.
+// Tiles lying wholly above a wave's rows on the causal diagonal are skipped,
+// and masks are applied only to tiles that cross a diagonal or the range end.
+// The running max used as the exponent reference is raised only when a
+// column's max grows by more than 2^8 (then the accumulators are rescaled);
+// otherwise probabilities up to 2^8 are accumulated against the old
+// reference.  The result is unchanged: output and log-sum-exp are formed
+// from the same reference.
 #include "attn_common.h"
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -28,20 +39,28 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
+constexpr int kColTiles = 2 * kWaves;          // column tiles per workgroup
+constexpr float kRescaleSlack = 8.f;            // log2 of the largest unscaled probability
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr int kTile = 32;
 constexpr int kKBytes = kTile * kD * 2;          // 8 KiB
-constexpr int kVPitch = kD * 2 + 16;
-constexpr int kVBytes = kTile * kVPitch;
-constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kVBytes = kTile * kD * 2;
+constexpr int kStageBytes = kKBytes + kVBytes;   // 16 KiB
+constexpr int kStages = 4;                       // LDS ring depth
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + ((c ^ (t & 15)) << 4); }
+// 16-byte slot of chunk c of token row t: K rows are swizzled so 16 lanes
+// reading one chunk of 16 rows (MFMA A operand) hit distinct bank groups; V
+// rows so the transposed reads (16 rows x 32 bytes) spread over all banks.
+__device__ __forceinline__ int kslot(int t, int c) { return c ^ (t & 15); }
+__device__ __forceinline__ int vslot(int t, int c) { return c ^ ((t & 7) << 1); }
+__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (kslot(t, c) << 4); }
 
 __device__ __forceinline__ float xmax16_32(float x) {
   auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -57,16 +76,16 @@ __device__ __forceinline__ float xsum16_32(float x) {
 }
 
 template <int BS>
-__global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char s_lds[2 * kStageBytes];
+__global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_lds[kStages * kStageBytes];
 
   const int seq = blockIdx.z + a.z_base;
   const int qs = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq), 0, a.num_tokens);
   const int qe = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq + 1), 0, a.num_tokens);
   const int q_len = min(qe - qs, a.max_query_len);
   if (qe - qs <= 1) return;                          // one-row sequences: decode kernels
-  const int GC = a.head_chunks_gc;                   // query heads per column group
-  const int R = 16 / GC;                             // row blocks per workgroup
+  const int GC = a.head_chunks_gc;                   // query heads per column group (<= 8)
+  const int R = kColTiles / GC;                      // row blocks per workgroup
   const int q0 = blockIdx.x * 16 * R;
   if (q0 >= q_len) return;
   const int group = a.num_heads / a.num_kv_heads;
@@ -101,6 +120,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
     if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
   }
   if (!a.causal) wave_last_pos = L - 1;
+  // smallest position among the wave's rows: tiles ending at or before it
+  // need no causal mask
+  const int wave_first_pos = a.causal ? min(rowb[0], rowb[1]) + off : (1 << 30);
 
   // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
   bf16x8_t qb[2][4];
@@ -116,6 +138,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
       qb[c][j] = as_bf16x8(v);
     }
   }
+  // the queries must be resident before any tile load is issued: otherwise
+  // the first use of them inside the tile loop would wait for every load in
+  // flight on each iteration
+  __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
 
   f32x4 o[2][8];
   float m[2], lsum[2];
@@ -127,33 +153,46 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
     lsum[c] = 0.f;
   }
 
-  // cooperative tile loads: thread -> (token tid/16, chunk tid%16); each wave
-  // covers 4 consecutive tokens, which share a block (block ids wave uniform)
-  const int ltok = tid >> 4;
-  const int lchunk = tid & 15;
+  // cooperative tile loads: load u (0, 1) of thread tid fills LDS row
+  // r = 16u + tid/16, slot tid%16, with the chunk of token r that belongs
+  // there; each wave covers 4 consecutive tokens per load, inside one block
+  // (block ids wave uniform).
+  const int lrow = tid >> 4;
+  const int lslot = tid & 15;
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
   const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
   const uint32_t head_off = (uint32_t)kvh * kD;
   const int64_t max_blk = a.num_blocks - 1;
-  const int last_bi = max(0, kv_end - 1) / BS;
+  const int last_tok = max(0, kv_end - 1);
 
-  auto fetch_id = [&](int t) -> int64_t {
-    const int bi = __builtin_amdgcn_readfirstlane(min((t * kTile + 4 * wave) / BS, last_bi));
-    return min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+  // block offsets of tile t's two 16-token halves for this wave (scalar
+  // loads, fetched one iteration before they are used)
+  auto fetch_ids = [&](int t, int64_t* ids) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tw = min(t * kTile + 16 * u + 4 * wave, last_tok);       // wave's first token
+      const int bi = __builtin_amdgcn_readfirstlane(tw / BS);
+      ids[u] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+    }
   };
-  u32x4 kreg, vreg;
-  auto issue = [&](int t, int64_t boff) {
-    const uint32_t lo = (uint32_t)((t * kTile + ltok) % BS) * tok_stride + head_off + lchunk * 8;
-    kreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + boff + lo));
-    vreg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + boff + lo));
-  };
-  auto stage = [&](int t, char* buf) {
-    u32x4 v = vreg;
-    if (t * kTile + ltok >= kv_end) v = u32x4{0u, 0u, 0u, 0u};   // never multiply stale data
-    *reinterpret_cast<u32x4*>(buf + ktile_off(ltok, lchunk)) = kreg;
-    *reinterpret_cast<u32x4*>(buf + kKBytes + ltok * kVPitch + lchunk * 16) = v;
+  // issue the direct-to-LDS loads of tile t into stage buf (4 per thread);
+  // tokens clamped to the last valid one stay in the block of the wave's
+  // first token
+  auto issue = [&](int t, const int64_t* ids, char* buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 16 * u + lrow;
+      const int tok = min(t * kTile + r, last_tok);
+      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off;
+      const int kch = kslot(r, lslot);   // slot s holds chunk s ^ f(r): involution
+      const int vch = vslot(r, lslot);
+      char* kdst = buf + u * 4096 + wave * 1024;
+      char* vdst = buf + kKBytes + u * 4096 + wave * 1024;
+      __builtin_amdgcn_global_load_lds(kc + ids[u] + lo + kch * 8, (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vc + ids[u] + lo + vch * 8, (lds_void*)vdst, 16, 0, 0);
+    }
   };
 
   auto compute = [&](int t, const char* buf) {
@@ -175,6 +214,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
         for (int c = 0; c < 2; ++c)
           sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][j], sacc[c][tt], 0, 0, 0);
       }
+    const bool masked = (j0 + kTile > kv_end) || (j0 + kTile - 1 > wave_first_pos);
     bf16x8_t pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -186,16 +226,24 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + tt * 16 + 4 * kg + i;
-          s[tt * 4 + i] = (j <= lim) ? sacc[c][tt][i] * a.scale_log2 : -INFINITY;
+          const float v = sacc[c][tt][i] * a.scale_log2;
+          s[tt * 4 + i] = (!masked || j <= lim) ? v : -INFINITY;
         }
       float mx = s[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
       mx = xmax16_32(mx);
-      const float mn = fmaxf(m[c], mx);
-      const float mref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m[c] - mref);
-      m[c] = mn;
+      // raise the reference only when the max outgrows it by the slack
+      const bool raise = mx > m[c] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mn = raise ? mx : m[c];
+        const float alpha = (m[c] == -INFINITY) ? 0.f : fast_exp2(m[c] - mn);
+        m[c] = mn;
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
+      }
+      const float mref = (m[c] == -INFINITY) ? 0.f : m[c];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -203,17 +251,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
         psum += p;
         pb[c][e] = (__bf16)p;
       }
-      lsum[c] = lsum[c] * alpha + psum;
-#pragma unroll
-      for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
+      lsum[c] += psum;
     }
+    // lane (kg, n) reads 8 bytes of row 4kg + n/4 (and row + 16): dims
+    // 16jd + 4(n%4) .. +3, i.e. half (n%4)&1 of chunk 2jd + (n%4)/2
     const int jj = n >> 2, q4 = n & 3;
-    const char* r0 = vl + (4 * kg + jj) * kVPitch + q4 * 8;
-    const char* r1 = r0 + 16 * kVPitch;
+    const int t0 = 4 * kg + jj, t1 = t0 + 16;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
-      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r0 + jd * 32));
-      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r1 + jd * 32));
+      const int ch = 2 * jd + (q4 >> 1);
+      const char* p0 = vl + t0 * (kD * 2) + (vslot(t0, ch) << 4) + (q4 & 1) * 8;
+      const char* p1 = vl + t1 * (kD * 2) + (vslot(t1, ch) << 4) + (q4 & 1) * 8;
+      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
       bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -221,22 +271,36 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_prefill_kernel(const At
     }
   };
 
-  // double-buffered key/value tiles, one barrier per tile
-  int64_t boff = 0;
-  if (ntiles > 0) {
-    boff = fetch_id(0);
-    issue(0, boff);
-    if (ntiles > 1) boff = fetch_id(1);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    char* buf = s_lds + (t & 1) * kStageBytes;
-    stage(t, buf);
-    if (t + 1 < ntiles) {
-      issue(t + 1, boff);
-      if (t + 2 < ntiles) boff = fetch_id(t + 2);
+  // LDS ring: tile t lives in stage t % kStages.  Before computing tile t a
+  // thread waits for its own loads of t (the loads of up to kStages - 2 later
+  // tiles may stay in flight), then the barrier makes t visible to all and
+  // guarantees every wave has finished tile t - 1, whose stage is refilled.
+  constexpr int kLoadsPerTile = 4;
+  int64_t ids[2];
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) {
+      fetch_ids(t, ids);
+      issue(t, ids, s_lds + t * kStageBytes);
     }
-    __syncthreads();
-    compute(t, buf);
+  if (kStages - 1 < ntiles) fetch_ids(kStages - 1, ids);
+  for (int t = 0; t < ntiles; ++t) {
+    const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    // a bare barrier: __syncthreads() would add a fence that drains the
+    // loads of the tiles still in flight.  Each thread has waited for its own
+    // loads of tile t above; LDS reads of tile t - 1 were consumed before.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int tn = t + kStages - 1;
+    if (tn < ntiles) {
+      issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
+      if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
+    }
+    compute(t, s_lds + (t % kStages) * kStageBytes);
   }
 
   // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]

@@ -80,6 +80,10 @@ __device__ __forceinline__ int32_t load_uniform_i32(const int32_t* p, int64_t i)
   return ((const_i32*)(p))[i];
 }
 
+// s_waitcnt immediate (gfx9 encoding) waiting until at most n vector memory
+// operations of this wave are outstanding; lgkm and exp counts are ignored.
+constexpr int vmcnt_enc(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 __device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
 }  // namespace pkv

@@ -42,7 +42,7 @@ struct AttnArgs {
   int32_t parts_per_wg;            // consecutive partitions one workgroup covers (>= 1);
                                    // the workspace holds one partial per workgroup range
   int32_t wave_per_part;           // 1: wave w of a workgroup owns partition w of its range
-  int32_t head_chunks_gc;          // prefill: query heads per column group (power of 2, <= 16)
+  int32_t head_chunks_gc;          // prefill: query heads per column group (power of 2, <= 8)
   int32_t z_base;                  // offset added to blockIdx.z
   int32_t mode;                    // AttnMode
   int32_t causal;
@@ -78,7 +78,7 @@ hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, dim3 grid,
                                    hipStream_t stream);
 
 // Chunked prefill on the matrix cores (rows of sequences with > 1 query
-// rows): bfloat16, head size 128.  grid = (query tiles of 256 / head_chunks_gc
+// rows): bfloat16, head size 128.  grid = (query tiles of 128 / head_chunks_gc
 // rows, num_kv_heads * group / head_chunks_gc, sequences).
 hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, dim3 grid,
                                     hipStream_t stream);
