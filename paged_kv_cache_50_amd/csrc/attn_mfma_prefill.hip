@@ -32,6 +32,8 @@
 // otherwise probabilities up to 2^8 are accumulated against the old
 // reference.  The result is unchanged: output and log-sum-exp are formed
 // from the same reference.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -62,11 +64,15 @@ __device__ __forceinline__ int kslot(int t, int c) { return c ^ (t & 15); }
 __device__ __forceinline__ int vslot(int t, int c) { return c ^ ((t & 7) << 1); }
 __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (kslot(t, c) << 4); }
 
+// NaN-propagating max (v_maximum3_f32): unlike fmaxf it needs no
+// canonicalisation of its operands.
+__device__ __forceinline__ float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
 __device__ __forceinline__ float xmax16_32(float x) {
   auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
+  x = vmax(__int_as_float(p16[0]), __int_as_float(p16[1]));
   auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
+  return vmax(__int_as_float(p32[0]), __int_as_float(p32[1]));
 }
 __device__ __forceinline__ float xsum16_32(float x) {
   auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -120,9 +126,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
     if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
   }
   if (!a.causal) wave_last_pos = L - 1;
-  // smallest position among the wave's rows: tiles ending at or before it
-  // need no causal mask
-  const int wave_first_pos = a.causal ? min(rowb[0], rowb[1]) + off : (1 << 30);
 
   // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
   bf16x8_t qb[2][4];
@@ -195,9 +198,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
     }
   };
 
-  auto compute = [&](int t, const char* buf) {
+  // MASKED: the tile may hold keys past a row's causal limit or the range
+  // end, or lie wholly above this wave's rows (skipped).
+  auto compute = [&](int t, const char* buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = t * kTile;
-    if (j0 > wave_last_pos) return;                  // wholly above this wave's diagonal
+    if (MASKED && j0 > wave_last_pos) return;        // wholly above this wave's diagonal
     const char* kl = buf;
     const char* vl = buf + kKBytes;
     f32x4 sacc[2][2];
@@ -214,31 +220,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
         for (int c = 0; c < 2; ++c)
           sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][j], sacc[c][tt], 0, 0, 0);
       }
-    const bool masked = (j0 + kTile > kv_end) || (j0 + kTile - 1 > wave_first_pos);
     bf16x8_t pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qpos = rowb[c] + n + off;            // this lane's column = query row
       const int lim = a.causal ? min(qpos, kv_end - 1) : kv_end - 1;
+      // raw logits; the scale is applied inside the exponent (one FMA)
       float s[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + tt * 16 + 4 * kg + i;
-          const float v = sacc[c][tt][i] * a.scale_log2;
-          s[tt * 4 + i] = (!masked || j <= lim) ? v : -INFINITY;
+          s[tt * 4 + i] = (!MASKED || j <= lim) ? sacc[c][tt][i] : -INFINITY;
         }
-      float mx = s[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-      mx = xmax16_32(mx);
-      // raise the reference only when the max outgrows it by the slack
+      float mx = vmax(vmax(vmax(s[0], s[1]), vmax(s[2], s[3])), vmax(vmax(s[4], s[5]), vmax(s[6], s[7])));
+      mx = xmax16_32(mx) * a.scale_log2;             // scale > 0 preserves the max
+      // raise the reference only when the max outgrows it by the slack; the
+      // accumulators are then rescaled (alpha = 1 for columns that keep it)
       const bool raise = mx > m[c] + kRescaleSlack;
+      const float mn = raise ? mx : m[c];
+      const float alpha = (m[c] == -INFINITY) ? 0.f : fast_exp2(m[c] - mn);
+      m[c] = mn;
       if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float mn = raise ? mx : m[c];
-        const float alpha = (m[c] == -INFINITY) ? 0.f : fast_exp2(m[c] - mn);
-        m[c] = mn;
         lsum[c] *= alpha;
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
@@ -247,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(s[e] - mref);
+        const float p = fast_exp2(fmaf(s[e], a.scale_log2, -mref));
         psum += p;
         pb[c][e] = (__bf16)p;
       }
@@ -284,7 +288,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
       issue(t, ids, s_lds + t * kStageBytes);
     }
   if (kStages - 1 < ntiles) fetch_ids(kStages - 1, ids);
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, auto masked_tag) {
     const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
     if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
     else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
@@ -300,8 +304,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_prefill_kernel(const At
       issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
       if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
     }
-    compute(t, s_lds + (t % kStages) * kStageBytes);
-  }
+    compute(t, s_lds + (t % kStages) * kStageBytes, masked_tag);
+  };
+  // Tiles wholly at or below the workgroup's first row position and inside
+  // the key range need no mask for any wave; the rest (the diagonal band and
+  // the range end) take the masked path.  Every wave runs both loops over
+  // the same tiles, so the barriers stay matched.
+  const int unmasked_end = a.causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
+  const int tm = min(ntiles, max(0, (unmasked_end + 1) / kTile));
+  for (int t = 0; t < tm; ++t) step(t, std::false_type{});
+  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{});
 
   // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]
 #pragma unroll
