@@ -107,8 +107,13 @@ bool timing_begin(hipStream_t st, int* slot) {
   if (!g_timing.enabled) return false;
   const int i = (int)(g_timing.tail % Timing::kCap);
   if (!g_timing.start[i]) {
-    if (hipEventCreate(&g_timing.start[i]) != hipSuccess) return false;
-    if (hipEventCreate(&g_timing.stop[i]) != hipSuccess) return false;
+    // timing-only events: without the system-scope fence a record costs no
+    // L2 writeback/invalidate (which would otherwise add a few microseconds
+    // around every timed launch and cool the caches of the next kernel)
+    if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess)
+      return false;
+    if (hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess)
+      return false;
   }
   if (g_timing.tail - g_timing.head >= Timing::kCap) g_timing.head++;  // overwrite oldest
   if (hipEventRecord(g_timing.start[i], st) != hipSuccess) return false;
