@@ -39,27 +39,38 @@ WORKLOAD_DESC = {
 }
 
 
-def kernel_source_hash() -> str:
+# Sources that determine each attention kernel's memory traffic: its own
+# translation unit, the shared device headers and the host launch logic.
+KERNEL_SOURCES = {
+    "attn_valu_kernel": ["attn_valu.hip"],
+    "attn_mfma_decode_kernel": ["attn_mfma_decode.hip"],
+    "attn_mfma_prefill_kernel": ["attn_mfma_prefill.hip"],
+}
+COMMON_SOURCES = ["device_common.h", "attn_common.h", "pkv_internal.h", "api.cpp"]
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel's counters depend on."""
     d = os.path.join(ROOT, "paged_kv_cache_50_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in COMMON_SOURCES + KERNEL_SOURCES[kernel]:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name: str, kernel: str):
-    """HBM traffic per launch measured by rocprofv3 counters for this exact
-    kernel source, or None."""
+def load_traffic(workload_name: str):
+    """HBM bytes per launch of the workload's dominant kernel, measured by
+    rocprofv3 FETCH_SIZE / WRITE_SIZE on the current source of that kernel,
+    or None when no such measurement exists."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(f"{workload_name}:{kernel}")
+        rec = json.load(open(p)).get(workload_name)
+        if not rec or rec.get("source_hash") != kernel_source_hash(rec["kernel"]):
+            return None
     except Exception:
-        return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -121,8 +132,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; a multi-GPU figure is not "
-              "part of it (sharding is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py: runs on exactly one GPU; --gpus N > 1 is not supported (the "
+              "kernels work on one GPU's share of the batch)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -199,7 +210,6 @@ def main() -> int:
     gbs = B / (ms_per_step * 1e-3) / 1e9
     kavg = float(np.mean(kern_ms)) if kern_ms else None
     if w.cu_seqlens_q is None:
-        kernel = "attn_partition"
         # the partition kernel reads every KV token, q and the metadata; the
         # merge kernel writes out (charged to the merge, not here)
         main_bytes = B - out_bytes
@@ -207,10 +217,10 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
-                "traffic": load_traffic(w.name, kernel),
-                "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms)}
+                "traffic": load_traffic(w.name),
+                "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms),
+                "kernel_bytes": int(main_bytes)}
     else:
-        kernel = "attn_prefill"
         flops = W.attention_flops(w)
         ql = w.query_lens
         pre_flops = 0
@@ -219,11 +229,18 @@ def main() -> int:
                 ctx = int(w.seq_lens[s]) - int(ql[s])
                 pre_flops += 4 * w.num_heads * w.head_size * (int(ql[s]) * ctx + int(ql[s]) * (int(ql[s]) + 1) // 2)
         achieved = pre_flops / (kavg * 1e-3) / 1e12 if kavg else None
+        # bytes the prefill kernel must move: its sequences' keys and values
+        # once, their query rows in and out
+        pre_kv = sum(int(w.seq_lens[s]) for s in range(S) if ql[s] > 1)
+        pre_rows = int(sum(int(x) for x in ql if x > 1))
+        pre_bytes = (pre_kv * 2 * w.num_kv_heads * w.head_size * e
+                     + 2 * pre_rows * w.num_heads * w.head_size * e)
         roof = {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-                "traffic": load_traffic(w.name, kernel),
+                "traffic": load_traffic(w.name),
                 "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms),
+                "kernel_flops": int(pre_flops), "kernel_bytes": int(pre_bytes),
                 "total_flops": flops}
 
     rec = {
