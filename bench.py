@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -49,13 +50,21 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ["device_common.h", "attn_common.h", "pkv_internal.h", "api.cpp"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that
+    edits of comments alone keep a kernel's stored measurements valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the sources a kernel's counters depend on."""
+    """Hash of the code a kernel's counters depend on."""
     d = os.path.join(ROOT, "paged_kv_cache_50_amd", "csrc")
     h = hashlib.sha256()
     for f in COMMON_SOURCES + KERNEL_SOURCES[kernel]:
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(_code_only(open(os.path.join(d, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,12 +22,15 @@
 //   ds_read_b64_tr_b16, two reads per 16-dim tile.
 //   O^T's accumulator column is again the lane's head, so the rescale by
 //   exp(m_old - m_new) is a plain per-lane multiply.
-// A workgroup (4 waves) owns one (sequence, kv-head chunk, key partition);
-// the grid puts partitions on its slowest axis so that the workgroups of
-// partitions a short sequence does not have are dispatched last.  Waves take
-// 32-token tiles round-robin, keep two tiles in flight (the next tile's loads,
-// and the block ids of the one after, are issued before the current tile is
-// computed) and merge their softmax states through LDS at the end.
+// A workgroup (4 waves) owns one (sequence, kv-head chunk, range of
+// consecutive key partitions); the grid puts ranges on its slowest axis so
+// that the workgroups of ranges a short sequence does not have are dispatched
+// last.  Either wave w owns partition w of a full 4-partition range, or the
+// waves take the range's 32-token tiles round-robin.  A wave copies its tile
+// from registers into its LDS area, issues the next tile's loads into the
+// same registers (block ids run one tile further ahead) and computes from LDS
+// while they are in flight; the 4 waves merge their softmax states through
+// LDS at the end and write the row, or the range's partial result.
 // Tokens past the partition end are loaded from an in-bounds slot of the last
 // valid block; their logits are replaced by -inf and their V rows by zeros
 // (select, never multiply), so stale NaNs in unused cache slots cannot reach
