@@ -80,21 +80,82 @@ __global__ void __launch_bounds__(256) splitkv_reduce_kernel(const AttnArgs a) {
   }
 }
 
+// Few ranges per row (at most kMaxFewRanges): grid = (rows, head groups).
+// A group of D/4 lanes owns one query head and issues every load of it at
+// once (all ranges' lse and partial rows, indices clamped in bounds, unused
+// ranges weighted 0), so a row costs one memory round trip, and rows that
+// were not split cost one early-exiting workgroup per head group.
+constexpr int kMaxFewRanges = 8;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) splitkv_reduce_few_kernel(const AttnArgs a) {
+  constexpr int LR = D / 4;
+  constexpr int NG = 256 / LR;
+  Item it;
+  if (!resolve_item(a, blockIdx.x, it)) return;
+  if (it.nranges <= 1) return;
+  const int nr = min(it.nranges, kMaxFewRanges);
+  const int g = threadIdx.x / LR, c = threadIdx.x % LR;
+  const int head = blockIdx.y * NG + g;
+  if (head >= a.num_heads) return;
+  const int64_t stride = (int64_t)a.num_heads * a.num_seqs;   // between partitions
+  const int64_t base = (int64_t)head * a.num_seqs + it.seq;
+  float l[kMaxFewRanges];
+  f32x4 v[kMaxFewRanges];
+#pragma unroll
+  for (int p = 0; p < kMaxFewRanges; ++p) {
+    const int64_t e = base + (int64_t)min(p, nr - 1) * stride;
+    l[p] = a.ws_lse[e];
+    v[p] = *reinterpret_cast<const f32x4*>(a.ws_o + e * D + 4 * c);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kMaxFewRanges; ++p) M = fmaxf(M, p < nr ? l[p] : -INFINITY);
+  const float Mref = (M == -INFINITY) ? 0.f : M;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+#pragma unroll
+  for (int p = 0; p < kMaxFewRanges; ++p) {
+    const float w = p < nr ? fast_exp2(l[p] - Mref) : 0.f;
+    acc += w * v[p];
+    wsum += w;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t oidx = ((int64_t)it.row * a.num_heads + head) * D + 4 * c;
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oidx) = acc * inv;
+  } else {
+    const uint32_t w0 = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    const uint32_t w1 = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oidx) = make_uint2(w0, w1);
+  }
+  if (c == 0 && a.lse_out)
+    a.lse_out[(int64_t)it.row * a.num_heads + head] =
+        wsum > 0.f ? (M + acc_log2(wsum)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
+  const int max_ranges = a.partition_size > 0
+      ? (a.num_splits + a.parts_per_wg - 1) / a.parts_per_wg : 1;
+  constexpr int NG = 256 / (D / 4);
+  if (max_ranges <= kMaxFewRanges)
+    hipLaunchKernelGGL((splitkv_reduce_few_kernel<T, D>),
+                       dim3(a.num_seqs, (a.num_heads + NG - 1) / NG), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((splitkv_reduce_kernel<T, D>), dim3(a.num_seqs, a.num_heads), dim3(256), 0,
+                       st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
-  dim3 grid(a.num_seqs, a.num_heads);
-  if (dtype == 0 && head_size == 64)
-    hipLaunchKernelGGL((splitkv_reduce_kernel<float, 64>), grid, dim3(256), 0, st, a);
-  else if (dtype == 0 && head_size == 128)
-    hipLaunchKernelGGL((splitkv_reduce_kernel<float, 128>), grid, dim3(256), 0, st, a);
-  else if (dtype == 1 && head_size == 64)
-    hipLaunchKernelGGL((splitkv_reduce_kernel<uint16_t, 64>), grid, dim3(256), 0, st, a);
-  else if (dtype == 1 && head_size == 128)
-    hipLaunchKernelGGL((splitkv_reduce_kernel<uint16_t, 128>), grid, dim3(256), 0, st, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (dtype == 0 && head_size == 64) return launch_typed<float, 64>(a, st);
+  if (dtype == 0 && head_size == 128) return launch_typed<float, 128>(a, st);
+  if (dtype == 1 && head_size == 64) return launch_typed<uint16_t, 64>(a, st);
+  if (dtype == 1 && head_size == 128) return launch_typed<uint16_t, 128>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv
