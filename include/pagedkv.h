@@ -133,7 +133,10 @@ int32_t pkv_choose_partition_size(int32_t num_seqs, int32_t num_heads, int32_t n
  * float32 partial output [num_splits, num_heads, num_seqs, head_size] and one
  * float32 log-sum-exp [num_splits, num_heads, num_seqs], the split buffer
  * shape of ch. 6 "build() étape par étape", with
- * num_splits = ceil(max_seq_len / partition) and rows indexed by sequence.
+ * num_splits = ceil(max_seq_len / partition) and rows indexed by sequence,
+ * followed by an int32 [num_seqs] dispatch order of the sequences (each part
+ * 16-byte aligned).  The contents are scratch of one call: nothing needs to
+ * be initialised, and calls sharing a workspace must be ordered on a stream.
  * Returns (size_t)-1 for invalid arguments.
  */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

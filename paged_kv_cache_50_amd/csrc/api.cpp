@@ -157,6 +157,10 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
     a.parts_per_wg = a.partition_size <= 0 ? 1
                      : a.wave_per_part ? 4
                      : std::max(1, kMfmaTokensPerWg / a.partition_size);
+    // With the sequences ordered longest first, the last key ranges (which
+    // only long sequences have) are dispatched first and the first ranges of
+    // the shortest sequences last: close to longest-processing-time first.
+    a.range_desc = a.seq_order ? 1 : 0;
     const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
     const unsigned gparts = (gy + a.parts_per_wg - 1) / a.parts_per_wg;
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
@@ -176,6 +180,29 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
 
 pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
   if (pkv::launch_splitkv_reduce(a, dtype, head_size, st) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// Split workspace: partial outputs [rows, head_size] fp32, their lse [rows]
+// fp32, then the sequence dispatch order int32 [num_seqs] (16-byte aligned).
+size_t order_offset(size_t rows, int32_t head_size) {
+  return align16(rows * head_size * sizeof(float) + rows * sizeof(float));
+}
+
+// One-row decode launches with a split workspace order their sequences
+// longest first (the planner writes the order into the workspace).
+pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspace,
+                          hipStream_t st) {
+  if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads))
+    return PKV_OK;
+  const size_t rows = (size_t)a.num_splits * a.num_heads * a.num_seqs;
+  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                              order_offset(rows, cache->head_size));
+  if (pkv::launch_seq_order(a.seq_lens, a.num_seqs, a.max_seq_len, order, st) != hipSuccess)
+    return PKV_ERR_HIP;
+  a.seq_order = order;
   return PKV_OK;
 }
 
@@ -200,6 +227,7 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.lse_out = lse_out;
   a.ws_o = nullptr;
   a.ws_lse = nullptr;
+  a.seq_order = nullptr;
   if (nsplits > 1) {
     a.ws_o = static_cast<float*>(workspace);
     a.ws_lse = a.ws_o + (int64_t)nsplits * num_heads * num_seqs * cache->head_size;
@@ -277,7 +305,7 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
   const int32_t ns = num_splits_for(max_seq_len, P);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)ns * num_heads * num_seqs;
-  return rows * head_size * sizeof(float) + rows * sizeof(float);
+  return order_offset(rows, head_size) + align16((size_t)num_seqs * sizeof(int32_t));
 }
 
 pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
@@ -336,6 +364,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                          num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
   a.mode = pkv::kModeDecode;
+  st = plan_seq_order(a, cache, workspace, s);
+  if (st != PKV_OK) return st;
   int tslot = 0;
   const bool timed = timing_begin(s, &tslot);
   st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
@@ -416,6 +446,8 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
   }
   // Sequences with one query row (decode rows), split over the key range.
   a.mode = pkv::kModeVarlenOne;
+  st = plan_seq_order(a, cache, workspace, s);
+  if (st != PKV_OK) return st;
   st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
   if (st != PKV_OK) return st;
   if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);

@@ -86,12 +86,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
   __shared__ float s_l[kWaves][16];
 
   Item it;
-  if (!resolve_item(a, blockIdx.y + a.z_base, it)) return;
+  const int zi = blockIdx.y + a.z_base;
+  if (!resolve_item(a, a.seq_order ? load_uniform_i32(a.seq_order, zi) : zi, it)) return;
   // This workgroup covers partitions [part_first, part_end) of the row (one
   // "range"); ranges sit on the slowest grid axis so that the workgroups of
   // ranges a short sequence does not have dispatch last.
-  const int part_first = blockIdx.z * a.parts_per_wg;
-  if (blockIdx.z >= it.nranges) return;
+  const int rz = a.range_desc ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
+  const int part_first = rz * a.parts_per_wg;
+  if (rz >= it.nranges) return;
   const int part_end = min(part_first + a.parts_per_wg, it.nparts);
 
   const int lane = threadIdx.x & 63;
@@ -285,7 +287,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
     s_l[wave][n] = lsum;
   }
   __syncthreads();
-  const int range = blockIdx.z;
+  const int range = rz;
   for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
     const int h = idx / kD;
     const int d = idx % kD;

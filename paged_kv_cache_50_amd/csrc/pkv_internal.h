@@ -26,6 +26,7 @@ struct AttnArgs {
   float* lse_out;                  // [rows, num_heads] or nullptr
   float* ws_o;                     // [num_splits, num_heads, num_seqs, D]
   float* ws_lse;                   // [num_splits, num_heads, num_seqs]
+  const int32_t* seq_order;        // [num_seqs] dispatch order of sequences, or nullptr
   int64_t block_stride;            // elements between blocks
   int64_t num_blocks;
   int32_t max_blocks_per_seq;
@@ -44,6 +45,7 @@ struct AttnArgs {
   int32_t wave_per_part;           // 1: wave w of a workgroup owns partition w of its range
   int32_t head_chunks_gc;          // prefill: query heads per column group (power of 2, <= 8)
   int32_t z_base;                  // offset added to blockIdx.z
+  int32_t range_desc;              // 1: grid.z runs over key ranges from the last one down
   int32_t mode;                    // AttnMode
   int32_t causal;
   int32_t skip_multi_row;          // kModeVarlenRows: 1 if another kernel owns multi-row seqs
@@ -82,6 +84,11 @@ hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, dim3 grid,
 // rows, num_kv_heads * group / head_chunks_gc, sequences).
 hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, dim3 grid,
                                     hipStream_t stream);
+
+// Permutation of 0..num_seqs-1 ordering sequences longest first (one
+// workgroup; seq_lens clamped to max_len).
+hipError_t launch_seq_order(const int32_t* seq_lens, int32_t num_seqs, int32_t max_len,
+                            int32_t* order, hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,
