@@ -261,6 +261,23 @@ def test_empty_and_single_token_sequences(dtype):
     G.assert_close(G.dev_to_f64(dw.out), ref, dtype, "edge")
 
 
+def test_many_sequences_longest_first_order():
+    """More sequences than the order planner has threads, lengths spanning
+    several buckets, ties and empty sequences: every row must still be
+    computed exactly once (split grouped decode, the planner's path)."""
+    rng = np.random.default_rng(11)
+    L = rng.integers(0, 400, size=3000)
+    L[::7] = 333                                   # many equal lengths
+    L[5] = 0
+    w = W.make_decode("many", L, 8, 2, 128, 16, "bf16", seed=11)
+    _announce(f"many sequences: {len(L)} seqs, max {L.max()}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=128)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", "many sequences")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "many sequences")
+
+
 def test_zero_sequences_is_noop():
     torch = G.torch()
     from paged_kv_cache_50_amd import pagedkv
