@@ -210,6 +210,43 @@ def main() -> int:
     pagedkv.timing_enable(False)
     ms_per_step = ms_total / args.steps
 
+    # Outside the timed region: the per-step distribution (each step between
+    # its own events) and the step replayed as a HIP graph (no host launch
+    # overhead).  Same workload, same buffers.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    per_step_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+    graph_us = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()                                  # warm the side stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / args.steps
+        del g
+    except Exception as exc:                        # reported, never fatal
+        print(f"[bench] graph replay unavailable: {exc}", file=sys.stderr, flush=True)
+
     B = W.algorithmic_bytes(w)
     e = w.elem_bytes
     out_bytes = T * w.num_heads * w.head_size * e
@@ -263,6 +300,8 @@ def main() -> int:
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "step_us_p10_p50_p90": [round(float(np.percentile(per_step_us, q)), 2) for q in (10, 50, 90)],
+        "graph_replay_us_per_step": round(graph_us, 2) if graph_us else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

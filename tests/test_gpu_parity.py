@@ -242,6 +242,41 @@ def test_run_to_run_deterministic():
     assert np.array_equal(G.dev_to_bits(dw.out), a)
 
 
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_graph_replay_matches_eager(cfg):
+    """The calls enqueue plain kernels only (no memset, no host sync), so a
+    captured step replays to the eager result, bit for bit, with eager work
+    between the replays."""
+    torch = G.torch()
+    if cfg == 3:
+        w = W.make_config(3, num_seqs=12, max_len=2000)
+    else:
+        w = W.make_config(5, num_seqs=10, max_len=900, num_chunks=3, chunk_len=77)
+    _announce(f"graph replay config{cfg}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=128)
+    torch.cuda.synchronize()
+    want = G.dev_to_bits(dw.out).copy()
+    want_lse = dw.lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        G.run(dw, partition_size=128)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        G.run(dw, partition_size=128)
+    for i in range(3):
+        dw.out.zero_()
+        dw.lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(G.dev_to_bits(dw.out), want), f"replay {i}"
+        assert torch.equal(dw.lse, want_lse), f"replay {i} lse"
+
+
 # ------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
