@@ -38,15 +38,20 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
+from .fp8 import e4m3_decode
+
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 value of stored elements: float32 arrays, or bfloat16
-    bit patterns (uint16) whose value is the float32 with those high bits."""
+    """Exact float64 value of stored elements: float32 arrays, bfloat16 bit
+    patterns (uint16) whose value is the float32 with those high bits, or
+    e4m3 codes (uint8; the value before the per-head scale)."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_decode(x)
     raise ValueError(dtype)
 
 
@@ -114,11 +119,14 @@ def attention_seq_kvhead(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray
                          block_table_row: np.ndarray, seq_len: int, row0: int, row1: int,
                          kv_head: int, num_heads: int, scale: float, block_size: int,
                          dtype: str, causal: bool,
-                         key_range: Optional[Tuple[int, int]] = None):
+                         key_range: Optional[Tuple[int, int]] = None,
+                         k_scale=None, v_scale=None):
     """Attention of query rows row0..row1-1 of one sequence for the query
     heads of one kv head.  key_range=(a, b) restricts the keys to logical
-    positions a..b-1 (used to express a split).  Returns out [q_len, g, D]
-    and lse [q_len, g] in float64."""
+    positions a..b-1 (used to express a split).  dtype is the cache's; with
+    an fp8 cache the queries are bfloat16 and cached values are
+    decode(code) * k_scale[kv_head] (v_scale for V).  Returns out
+    [q_len, g, D] and lse [q_len, g] in float64."""
     Hkv = k_cache.shape[2]
     g = num_heads // Hkv
     q_len = row1 - row0
@@ -126,7 +134,11 @@ def attention_seq_kvhead(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray
     L = int(seq_len)
     K = widen(gather_kv(k_cache, block_table_row, L, block_size, kv_head), dtype)  # [L, D]
     V = widen(gather_kv(v_cache, block_table_row, L, block_size, kv_head), dtype)
-    Q = widen(q[row0:row1, kv_head * g:(kv_head + 1) * g], dtype)                 # [q_len, g, D]
+    if dtype == "fp8":
+        K = K * float(np.float32(k_scale[kv_head]))
+        V = V * float(np.float32(v_scale[kv_head]))
+    qdtype = "bf16" if dtype == "fp8" else dtype
+    Q = widen(q[row0:row1, kv_head * g:(kv_head + 1) * g], qdtype)                # [q_len, g, D]
     S = scale * (Q.reshape(q_len * g, D) @ K.T)                                   # [q_len*g, L]
     S = S.reshape(q_len, g, L)
     j = np.arange(L)
@@ -145,12 +157,14 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                     block_tables: np.ndarray, seq_lens: np.ndarray, scale: float,
                     block_size: int, dtype: str, cu_seqlens_q: Optional[np.ndarray] = None,
                     causal: bool = False,
-                    pairs: Optional[Sequence[Tuple[int, int]]] = None):
+                    pairs: Optional[Sequence[Tuple[int, int]]] = None,
+                    k_scale=None, v_scale=None):
     """Attention over a paged KV cache, as defined above.
 
     q: [num_rows, num_heads, D]; decode when cu_seqlens_q is None (row s is
     sequence s), else sequence s owns rows cu_seqlens_q[s]..cu_seqlens_q[s+1]-1.
     pairs: optional list of (seq, kv_head) to evaluate; other rows stay NaN.
+    dtype "fp8": e4m3 caches with per-kv-head scales k_scale / v_scale.
     Returns out [num_rows, num_heads, D] and lse [num_rows, num_heads], float64
     (lse in natural log).
     """
@@ -168,7 +182,8 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         if r1 <= r0:
             continue
         o, l = attention_seq_kvhead(q, k_cache, v_cache, block_tables[s], int(seq_lens[s]),
-                                    r0, r1, kvh, num_heads, scale, block_size, dtype, causal)
+                                    r0, r1, kvh, num_heads, scale, block_size, dtype, causal,
+                                    k_scale=k_scale, v_scale=v_scale)
         out[r0:r1, kvh * g:(kvh + 1) * g] = o
         lse[r0:r1, kvh * g:(kvh + 1) * g] = l
     return out, lse
