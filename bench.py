@@ -37,6 +37,8 @@ WORKLOAD_DESC = {
     3: "256 seqs, 32/8 heads, head 128, block 16, bf16, seq_lens lognormal(median 1024, sigma 0.8) in [16,8192], seed 2",
     4: "8 seqs, 64/8 heads, head 128, block 16, bf16, seq_lens U[32768,131072], 512-token partitions, N(0,0.5), seed 3",
     5: "slot write + varlen: 4 causal chunks of 512 (context U[0,4096]) + 128 decode rows (U[64,4096]), 32/8 heads, head 128, block 32, bf16, seed 4",
+    6: "workload 2 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
+    7: "workload 3 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
 }
 
 
@@ -98,7 +100,11 @@ def cpu_baseline(w, budget_s: float = 12.0):
     kc, vc = w.k_cache, w.v_cache
     if w.slot_mapping is not None:
         kc, vc = kc.copy(), vc.copy()
-        oracle.kv_cache_write(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size)
+        if w.dtype == "fp8":
+            oracle.kv_cache_write_fp8(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size,
+                                      w.k_scale, w.v_scale)
+        else:
+            oracle.kv_cache_write(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size)
     pairs = [(s, h) for s in range(w.num_seqs) for h in range(w.num_kv_heads)]
     # bytes of one (seq, kv head) pair: its K/V tokens plus q/out rows
     e = w.elem_bytes
@@ -112,8 +118,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
         s, h = pairs[i % len(pairs)]
         oracle.paged_attention(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size,
                                w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
-                               pairs=[(s, h)])
-        done_bytes += int(w.seq_lens[s]) * 2 * w.head_size * e + 2 * int(ql[s]) * g * w.head_size * e
+                               pairs=[(s, h)], k_scale=w.k_scale, v_scale=w.v_scale)
+        done_bytes += (int(w.seq_lens[s]) * 2 * w.head_size * e
+                       + 2 * int(ql[s]) * g * w.head_size * w.io_bytes)
         done_pairs += 1
         i += 1
         el = time.perf_counter() - t0
@@ -131,7 +138,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -181,16 +188,17 @@ def main() -> int:
     def step():
         if w.slot_mapping is not None:
             pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new,
-                                   dw.slot_mapping)
+                                   dw.slot_mapping, k_scale=dw.k_scale, v_scale=dw.v_scale)
         if w.cu_seqlens_q is None:
             pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                            dw.seq_lens, w.scale, w.max_seq_len,
-                                           partition_size=ps, workspace=ws)
+                                           partition_size=ps, workspace=ws, k_scale=dw.k_scale,
+                                           v_scale=dw.v_scale)
         else:
             pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
                                            dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
                                            w.max_seq_len, causal=w.causal, partition_size=ps,
-                                           workspace=ws)
+                                           workspace=ws, k_scale=dw.k_scale, v_scale=dw.v_scale)
 
     for _ in range(args.warmup):
         step()
@@ -249,10 +257,7 @@ def main() -> int:
 
     B = W.algorithmic_bytes(w)
     e = w.elem_bytes
-    out_bytes = T * w.num_heads * w.head_size * e
-    write_bytes = 0
-    if w.slot_mapping is not None:
-        write_bytes = 2 * 2 * len(w.slot_mapping) * w.num_kv_heads * w.head_size * e + 8 * len(w.slot_mapping)
+    out_bytes = T * w.num_heads * w.head_size * w.io_bytes
     gbs = B / (ms_per_step * 1e-3) / 1e9
     kavg = float(np.mean(kern_ms)) if kern_ms else None
     if w.cu_seqlens_q is None:
@@ -280,7 +285,7 @@ def main() -> int:
         pre_kv = sum(int(w.seq_lens[s]) for s in range(S) if ql[s] > 1)
         pre_rows = int(sum(int(x) for x in ql if x > 1))
         pre_bytes = (pre_kv * 2 * w.num_kv_heads * w.head_size * e
-                     + 2 * pre_rows * w.num_heads * w.head_size * e)
+                     + 2 * pre_rows * w.num_heads * w.head_size * w.io_bytes)
         roof = {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
@@ -305,7 +310,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16"}[w.dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8 e4m3 cache, bf16 q/out"}[w.dtype],
         "data": "synthetic (seeded; shapes and length distributions of the workload)",
         "config": {"workload": w.name, "description": WORKLOAD_DESC[args.workload],
                    "num_seqs": S, "query_rows": T, "num_heads": w.num_heads,

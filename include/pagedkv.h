@@ -89,7 +89,10 @@ typedef enum {
 
 typedef enum {
   PKV_F32 = 0,
-  PKV_BF16 = 1
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2   /* cache only: e4m3 codes (OCP "fn" variant: bias 7, max 448,
+                        no infinities, 0x7F/0xFF NaN) with per-kv-head float32
+                        scales; q, out, key and value are then bfloat16 */
 } pkv_dtype;
 
 /* Descriptor of one layer's paged KV cache (no ownership is transferred). */
@@ -100,8 +103,15 @@ typedef struct pkv_kv_cache {
   int32_t block_size;    /* tokens per block: 8, 16 or 32                           */
   int32_t num_kv_heads;  /* > 0                                                     */
   int32_t head_size;     /* 64 or 128                                               */
-  int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value)       */
+  int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value, which
+                            are bfloat16 for PKV_FP8_E4M3)                          */
   int64_t block_stride;  /* elements between consecutive blocks; 0 = dense         */
+  const float* k_scale;  /* PKV_FP8_E4M3: device float32 [num_kv_heads]; cached code
+                            c of kv head h stands for e4m3(c) * k_scale[h].  The
+                            pages' (num_sequences, num_kv_heads) descale (vLLM book,
+                            ch. 6 "Flux des paramètres du chemin non-cascadé") is a
+                            broadcast of these per-layer scales.  NULL otherwise.  */
+  const float* v_scale;  /* the same for V                                          */
 } pkv_kv_cache;
 
 /*
@@ -110,8 +120,12 @@ typedef struct pkv_kv_cache {
  *   k_cache[slot / block_size, slot % block_size, :, :] = key[t, :, :]
  * and the same for value.  slot -1 (padding, ch. 5.2) writes nothing.  The
  * token count is num_tokens (the length of slot_mapping); key/value may hold
- * more, padded rows, which are never read.  Elements are copied bit for bit.
+ * more, padded rows, which are never read.  Elements are copied bit for bit,
+ * except into an fp8 cache: element x (bfloat16) of kv head h is stored as the
+ * e4m3 code nearest to x / k_scale[h] (v_scale for V), the quotient taken in
+ * float32 and saturated to +-448, ties to even, NaN as 0x7F.
  *   key, value   device [>= num_tokens, num_kv_heads, head_size], cache dtype
+ *                (bfloat16 for an fp8 cache)
  *   slot_mapping device int64 [num_tokens]
  * Duplicate non-negative slots are undefined (one of the rows wins).
  * num_tokens == 0 is a no-op returning PKV_OK.

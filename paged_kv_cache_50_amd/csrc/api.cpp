@@ -24,13 +24,18 @@ constexpr int32_t kPartitionQuantum = 32;
 constexpr int64_t kMaxGridZ = 65535;
 constexpr int64_t kMaxGridY = 65535;
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_FP8_E4M3 ? 1 : 2; }
+bool is_fp8(const pkv_kv_cache* c) { return c->dtype == PKV_FP8_E4M3; }
+// dtype of q / out (and of the split merge's output)
+int32_t io_dtype(int32_t dtype) { return dtype == PKV_FP8_E4M3 ? PKV_BF16 : dtype; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t num_heads,
                    int32_t num_kv_heads) {
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return "dtype must be PKV_F32 or PKV_BF16";
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3)
+    return "dtype must be PKV_F32, PKV_BF16 or PKV_FP8_E4M3";
+  if (dtype == PKV_FP8_E4M3 && head_size != 128) return "fp8 caches need head_size 128";
   if (head_size != 64 && head_size != 128) return "head_size must be 64 or 128";
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return "block_size must be 8, 16 or 32";
@@ -50,6 +55,7 @@ pkv_status check_cache(const pkv_kv_cache* c, int32_t num_heads) {
   const int64_t dense = (int64_t)c->block_size * c->num_kv_heads * c->head_size;
   if (c->block_stride != 0 && c->block_stride < dense) return PKV_ERR_SHAPE;
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_ALIGN;
+  if (c->dtype == PKV_FP8_E4M3 && (!c->k_scale || !c->v_scale)) return PKV_ERR_NULL;
   const int64_t stride = c->block_stride ? c->block_stride : dense;
   if ((stride * elem_bytes(c->dtype)) % 16 != 0) return PKV_ERR_ALIGN;
   return PKV_OK;
@@ -68,6 +74,7 @@ constexpr int kMfmaMinGroup = 4;
 constexpr int kMfmaTokensPerWg = 2048;
 
 bool use_mfma_decode(const pkv_kv_cache* c, int group) {
+  if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
   if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
   static const char* force = std::getenv("PKV_DECODE_KERNEL");
   if (force && std::strcmp(force, "valu") == 0) return false;
@@ -166,7 +173,8 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
-      if (pkv::launch_attn_mfma_decode(a, cache->block_size, dim3(gx, gz, gparts), st) != hipSuccess)
+      if (pkv::launch_attn_mfma_decode(a, cache->block_size, is_fp8(cache), dim3(gx, gz, gparts),
+                                       st) != hipSuccess)
         return PKV_ERR_HIP;
     }
     a.z_base = 0;
@@ -253,6 +261,8 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.causal = 0;
   a.skip_multi_row = 0;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
   return a;
 }
 
@@ -326,10 +336,14 @@ pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const 
   a.num_tokens = num_tokens;
   a.num_slots = cache->num_blocks * cache->block_size;
   a.block_stride_bytes = block_stride_elems(cache) * elem_bytes(cache->dtype);
+  a.head_size = cache->head_size;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
   a.block_size = cache->block_size;
   a.row_bytes = cache->num_kv_heads * cache->head_size * elem_bytes(cache->dtype);
   if (num_tokens > (int64_t)INT32_MAX * 4) return PKV_ERR_SHAPE;
-  return pkv::launch_kv_write(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+  return pkv::launch_kv_write(a, is_fp8(cache), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
                                                                                  : PKV_ERR_HIP;
 }
 
@@ -371,7 +385,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
   if (timed) timing_end(s, tslot);
   if (st != PKV_OK) return st;
-  if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
+  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
   return st;
 }
 
@@ -390,6 +404,8 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  // fp8 caches have the one-row (decode) kernel only
+  if (is_fp8(cache) && max_query_len > 1) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
@@ -450,7 +466,7 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
   if (st != PKV_OK) return st;
   st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
   if (st != PKV_OK) return st;
-  if (ns > 1) st = launch_reduce(a, cache->dtype, cache->head_size, s);
+  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
   return st;
 }
 

@@ -76,10 +76,17 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // of 16 different rows hit 16 different bank groups.
 __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + ((c ^ (t & 15)) << 4); }
 
-template <int BS>
+// FP8: the caches hold e4m3 codes with per-kv-head scales; a token row is
+// then 128 bytes, read by 8 lanes, and converted (exactly) to bfloat16 while
+// it is staged in LDS, so the matrix-core part is the same.  The K scale is
+// folded into the logit scale and the V scale into the output.
+template <int BS, bool FP8>
 __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const AttnArgs a) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   constexpr int kBlkPerTile = kTile / BS;
+  constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
+  constexpr int kRowsPerLoad = FP8 ? 8 : 4;          // token rows per wave load
+  constexpr int kLoads = kTile / kRowsPerLoad;       // loads per tile (K and V each)
 
   __shared__ __attribute__((aligned(16))) char s_lds[kWaves * kWaveLds];
   __shared__ float s_m[kWaves][16];
@@ -128,10 +135,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
   float m = -INFINITY, lsum = 0.f;
 
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
-  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
-  const uint32_t head_off = (uint32_t)kvh * kD;
+  const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
+  const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
+  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD * kEB;   // bytes
+  const uint32_t head_off = (uint32_t)kvh * kD * kEB;
+  const int64_t blk_stride = a.block_stride * kEB;
+  float logit_scale = a.scale_log2, out_scale = 1.f;
+  if constexpr (FP8) {
+    logit_scale *= a.k_scale[kvh];
+    out_scale = a.v_scale[kvh];
+  }
+  // lane's place in a natural load: token row within the load, byte offset
+  const int lrow = FP8 ? (lane >> 3) : kg;
+  const int lbyte = FP8 ? (lane & 7) * 16 : n * 16;
   const int64_t max_blk = a.num_blocks - 1;
   const int ntiles = (pend > pstart) ? (pend - pstart + kTile - 1) / kTile : 0;
   const int last_bi = (pend - 1) / BS;
@@ -145,18 +161,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
 #pragma unroll
     for (int b = 0; b < kBlkPerTile; ++b) {
       const int bi = __builtin_amdgcn_readfirstlane(min(tbase / BS + b, last_bi));
-      ids[b] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+      ids[b] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * blk_stride;
     }
   };
 
-  // K and V loads of one tile: 8 + 8 natural loads, each 4 whole token rows
-  // (row = 4i + kg, 16-byte chunk n).  Each 4-row group lies in one block.
+  // K and V loads of one tile: kLoads + kLoads natural loads, each
+  // kRowsPerLoad whole token rows (row kRowsPerLoad * i + lrow, 16 bytes at
+  // lbyte).  Each such group of rows lies in one block.
   auto issue = [&](const int64_t* ids, u32x4* K, u32x4* V) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = 4 * i + kg;
-      const int64_t boff = ids[(4 * i) / BS];
-      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off + n * 8;
+    for (int i = 0; i < kLoads; ++i) {
+      const int tok = kRowsPerLoad * i + lrow;
+      const int64_t boff = ids[(kRowsPerLoad * i) / BS];
+      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off + lbyte;
       K[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + boff + lo));
       V[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + boff + lo));
     }
@@ -168,12 +185,26 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
     const bool full = tbase + kTile <= pend;
     __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = 4 * i + kg;
-      *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
-      u32x4 v = V[i];
-      if (!full && tbase + tok >= pend) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + n * 16) = v;
+    for (int i = 0; i < kLoads; ++i) {
+      const int tok = kRowsPerLoad * i + lrow;
+      const bool dead = !full && tbase + tok >= pend;
+      if constexpr (FP8) {
+        // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
+        const int c = lane & 7;
+        u32x4 k0, k1, v0, v1;
+        e4m3x16_to_bf16x16(K[i], k0, k1);
+        e4m3x16_to_bf16x16(V[i], v0, v1);
+        if (dead) v0 = v1 = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
+        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32) = v0;
+        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32 + 16) = v1;
+      } else {
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
+        u32x4 v = V[i];
+        if (dead) v = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + n * 16) = v;
+      }
     }
     __asm__ volatile("" ::: "memory");
   };
@@ -201,7 +232,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tbase + tt * 16 + 4 * kg + i;
-        s[tt * 4 + i] = (full || tok < pend) ? sacc[tt][i] * a.scale_log2 : -INFINITY;
+        s[tt * 4 + i] = (full || tok < pend) ? sacc[tt][i] * logit_scale : -INFINITY;
       }
     float mx = s[0];
 #pragma unroll
@@ -257,7 +288,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
     tend = ntiles;
     tstep = kWaves;
   }
-  u32x4 kr[8], vr[8];
+  u32x4 kr[kLoads], vr[kLoads];
   int64_t ids[kBlkPerTile];
   if (tile < tend) {
     fetch_ids(tile, ids);
@@ -304,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
     }
     const int head = h0 + h;
     if (it.nranges == 1) {
-      const float v = Ls > 0.f ? O / Ls : 0.f;
+      const float v = Ls > 0.f ? O / Ls * out_scale : 0.f;
       static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * kD + d] =
           static_cast<uint16_t>(f32_to_bf16_rne(v));
       if (d == 0 && a.lse_out)
@@ -312,23 +343,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const Att
             Ls > 0.f ? (M + acc_log2(Ls)) * kLn2 : -INFINITY;
     } else {
       const int64_t widx = ((int64_t)range * a.num_heads + head) * a.num_seqs + it.seq;
-      a.ws_o[widx * kD + d] = Ls > 0.f ? O / Ls : 0.f;
+      a.ws_o[widx * kD + d] = Ls > 0.f ? O / Ls * out_scale : 0.f;
       if (d == 0) a.ws_lse[widx] = Ls > 0.f ? M + acc_log2(Ls) : -INFINITY;
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, dim3 grid,
-                                   hipStream_t stream) {
+template <bool FP8>
+hipError_t launch_typed(const AttnArgs& a, int block_size, dim3 grid, hipStream_t stream) {
   switch (block_size) {
-    case 8: hipLaunchKernelGGL((attn_mfma_decode_kernel<8>), grid, dim3(kThreads), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((attn_mfma_decode_kernel<16>), grid, dim3(kThreads), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((attn_mfma_decode_kernel<32>), grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_mfma_decode_kernel<8, FP8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((attn_mfma_decode_kernel<16, FP8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((attn_mfma_decode_kernel<32, FP8>), grid, dim3(kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
+                                   hipStream_t stream) {
+  return fp8 ? launch_typed<true>(a, block_size, grid, stream)
+             : launch_typed<false>(a, block_size, grid, stream);
 }
 
 }  // namespace pkv

@@ -35,6 +35,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// ---- e4m3 (OCP "fn" variant) <-> float32, with the gfx950 converters, which
+// round to nearest even and handle subnormals (out-of-range inputs must be
+// clamped first: they would become NaN).
+
+// Four e4m3 codes (bytes of w, low first) -> four bfloat16 (exact: every
+// e4m3 value is a bfloat16), as two words of two.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);    // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);     // bytes 2, 3
+  // the float32 results have zero low halves: keep the high 16 bits of each
+  uint2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  return r;
+}
+
+// Sixteen e4m3 codes -> two 16-byte chunks of eight bfloat16.
+__device__ __forceinline__ void e4m3x16_to_bf16x16(const u32x4 w, u32x4& c0, u32x4& c1) {
+  const uint2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+  const uint2 c = e4m3x4_to_bf16x4(w[2]), d = e4m3x4_to_bf16x4(w[3]);
+  c0 = u32x4{a.x, a.y, b.x, b.y};
+  c1 = u32x4{c.x, c.y, d.x, d.y};
+}
+
+// Saturate to the finite e4m3 range; NaN passes through.
+__device__ __forceinline__ float e4m3_sat(float t) {
+  return t > 448.f ? 448.f : (t < -448.f ? -448.f : t);
+}
+
+// Four floats (already saturated) -> four e4m3 codes, nearest even; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float t0, float t1, float t2, float t3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, w, true);
+  uint32_t u = (uint32_t)w;
+  if (t0 != t0) u = (u & 0xFFFFFF00u) | 0x7Fu;
+  if (t1 != t1) u = (u & 0xFFFF00FFu) | 0x7F00u;
+  if (t2 != t2) u = (u & 0xFF00FFFFu) | 0x7F0000u;
+  if (t3 != t3) u = (u & 0x00FFFFFFu) | 0x7F000000u;
+  return u;
+}
+
 // One DPP move of a float within a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

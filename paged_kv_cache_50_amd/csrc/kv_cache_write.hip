@@ -38,11 +38,52 @@ __global__ void __launch_bounds__(64 * kTokensPerWg) kv_write_kernel(const KvWri
   }
 }
 
+// e4m3 caches: key/value rows are bfloat16; element x of kv head h is stored
+// as the e4m3 code nearest to x / scale[h] (float32 division, saturated to
+// +-448, ties to even; NaN -> 0x7F).  A lane quantises 8 elements (16 bytes
+// in, 8 out), all of one head since head_size is a multiple of 8.
+__global__ void __launch_bounds__(64 * kTokensPerWg) kv_write_fp8_kernel(const KvWriteArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * kTokensPerWg + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= a.num_tokens) return;
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot / a.block_size;
+  const int64_t off = slot % a.block_size;
+  const int elems = a.row_bytes;                     // one byte per cached element
+  const int64_t dst = blk * a.block_stride_bytes + off * elems;
+  const int64_t src = t * (int64_t)elems * 2;
+  const char* __restrict__ ks = static_cast<const char*>(a.key) + src;
+  const char* __restrict__ vs = static_cast<const char*>(a.value) + src;
+  char* __restrict__ kd = static_cast<char*>(a.k_cache) + dst;
+  char* __restrict__ vd = static_cast<char*>(a.v_cache) + dst;
+  auto quant8 = [](const u32x4 x, float s) {
+    uint2 r;
+    r.x = f32x4_to_e4m3x4(e4m3_sat(bf16_lo(x[0]) / s), e4m3_sat(bf16_hi(x[0]) / s),
+                          e4m3_sat(bf16_lo(x[1]) / s), e4m3_sat(bf16_hi(x[1]) / s));
+    r.y = f32x4_to_e4m3x4(e4m3_sat(bf16_lo(x[2]) / s), e4m3_sat(bf16_hi(x[2]) / s),
+                          e4m3_sat(bf16_lo(x[3]) / s), e4m3_sat(bf16_hi(x[3]) / s));
+    return r;
+  };
+  for (int e = lane * 8; e < elems; e += 64 * 8) {
+    const int h = e / a.head_size;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(ks + 2 * e);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(vs + 2 * e);
+    *reinterpret_cast<uint2*>(kd + e) = quant8(kv, a.k_scale[h]);
+    *reinterpret_cast<uint2*>(vd + e) = quant8(vv, a.v_scale[h]);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
+hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8, hipStream_t stream) {
   const int64_t wgs = (a.num_tokens + kTokensPerWg - 1) / kTokensPerWg;
-  hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)wgs), dim3(64 * kTokensPerWg), 0, stream, a);
+  if (fp8)
+    hipLaunchKernelGGL(kv_write_fp8_kernel, dim3((unsigned)wgs), dim3(64 * kTokensPerWg), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)wgs), dim3(64 * kTokensPerWg), 0, stream,
+                       a);
   return hipGetLastError();
 }
 

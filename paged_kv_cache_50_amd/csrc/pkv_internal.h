@@ -50,6 +50,8 @@ struct AttnArgs {
   int32_t causal;
   int32_t skip_multi_row;          // kModeVarlenRows: 1 if another kernel owns multi-row seqs
   float scale_log2;                // scale * log2(e)
+  const float* k_scale;            // fp8 caches: per-kv-head scales (value = code * scale)
+  const float* v_scale;
 };
 
 struct KvWriteArgs {
@@ -62,21 +64,26 @@ struct KvWriteArgs {
   int64_t num_slots;               // num_blocks * block_size
   int64_t block_stride_bytes;
   int32_t block_size;
-  int32_t row_bytes;               // num_kv_heads * head_size * elem_bytes
+  int32_t row_bytes;               // num_kv_heads * head_size * elem_bytes (of the cache)
+  int32_t head_size;
+  const float* k_scale;            // fp8 caches: per-kv-head scales, else nullptr
+  const float* v_scale;
 };
 
 // Launchers (return the launch error, hipSuccess on success).
-hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+// fp8 = true: bfloat16 key/value quantised into e4m3 caches.
+hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8, hipStream_t stream);
 
 // General VALU attention kernel: float32 or bfloat16 caches, head size 64/128,
 // block size 8/16/32, any GQA ratio.
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream);
 
-// Grouped-query decode on the matrix cores: bfloat16, head size 128, up to 16
-// query heads per kv-head chunk (head_chunks = ceil(group / 16)).
+// Grouped-query decode on the matrix cores: bfloat16 (or e4m3 with fp8 =
+// true) caches, head size 128, up to 16 query heads per kv-head chunk
+// (head_chunks = ceil(group / 16)).
 // grid = (num_kv_heads * head_chunks, sequences, ceil(partitions / parts_per_wg)).
-hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, dim3 grid,
+hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
                                    hipStream_t stream);
 
 // Chunked prefill on the matrix cores (rows of sequences with > 1 query

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 PKV_OK = 0
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
                 4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_METADATA", 7: "PKV_ERR_HIP"}
 
@@ -32,6 +33,8 @@ class PkvKvCache(ctypes.Structure):
         ("head_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("block_stride", ctypes.c_int64),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -116,7 +119,15 @@ def _dtype_code(t) -> int:
         return PKV_F32
     if t.dtype == torch.bfloat16:
         return PKV_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return PKV_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _io_dtype(k_cache):
+    """dtype of q/out/key/value for a cache: bfloat16 for fp8 caches."""
+    torch = _torch()
+    return torch.bfloat16 if k_cache.dtype == torch.float8_e4m3fn else k_cache.dtype
 
 
 def _require_gpu(*ts):
@@ -134,10 +145,12 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def cache_descriptor(k_cache, v_cache) -> PkvKvCache:
+def cache_descriptor(k_cache, v_cache, k_scale=None, v_scale=None) -> PkvKvCache:
     """Describe [num_blocks, block_size, num_kv_heads, head_size] caches whose
-    blocks may be strided (dense inside a block)."""
-    _require_gpu(k_cache, v_cache)
+    blocks may be strided (dense inside a block).  fp8 (float8_e4m3fn) caches
+    need float32 [num_kv_heads] scales k_scale / v_scale."""
+    torch = _torch()
+    _require_gpu(k_cache, v_cache, k_scale, v_scale)
     if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must have the same 4-D shape and dtype")
     nb, bs, hkv, d = k_cache.shape
@@ -146,8 +159,15 @@ def cache_descriptor(k_cache, v_cache) -> PkvKvCache:
             raise ValueError("cache blocks must be dense [block_size, num_kv_heads, head_size]")
     if k_cache.stride(0) != v_cache.stride(0):
         raise ValueError("k_cache and v_cache must share the block stride")
-    return PkvKvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d,
-                      _dtype_code(k_cache), k_cache.stride(0) if nb > 1 else 0)
+    code = _dtype_code(k_cache)
+    if code == PKV_FP8_E4M3:
+        for t in (k_scale, v_scale):
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != (hkv,) or not t.is_contiguous():
+                raise ValueError("fp8 caches need contiguous float32 k_scale/v_scale [num_kv_heads]")
+    return PkvKvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, bs, hkv, d, code,
+                      k_cache.stride(0) if nb > 1 else 0,
+                      _ptr(k_scale) if code == PKV_FP8_E4M3 else None,
+                      _ptr(v_scale) if code == PKV_FP8_E4M3 else None)
 
 
 def _check(status: int, what: str):
@@ -155,17 +175,19 @@ def _check(status: int, what: str):
         raise PagedKVError(status, what)
 
 
-def kv_cache_write(k_cache, v_cache, key, value, slot_mapping) -> None:
+def kv_cache_write(k_cache, v_cache, key, value, slot_mapping, k_scale=None, v_scale=None) -> None:
     """Scatter key/value rows [>= T, Hkv, D] into the caches at slot_mapping
-    (int64 [T], -1 = skip).  In place, asynchronous on the current stream."""
+    (int64 [T], -1 = skip).  In place, asynchronous on the current stream.
+    fp8 caches take bfloat16 rows and quantise them with k_scale / v_scale."""
     torch = _torch()
     _require_gpu(key, value, slot_mapping)
-    desc = cache_descriptor(k_cache, v_cache)
+    desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise TypeError("slot_mapping must be a contiguous int64 tensor")
     for t in (key, value):
-        if not t.is_contiguous() or t.dtype != k_cache.dtype or tuple(t.shape[1:]) != tuple(k_cache.shape[2:]):
-            raise ValueError("key/value must be contiguous [T, num_kv_heads, head_size] in the cache dtype")
+        if not t.is_contiguous() or t.dtype != _io_dtype(k_cache) or tuple(t.shape[1:]) != tuple(k_cache.shape[2:]):
+            raise ValueError("key/value must be contiguous [T, num_kv_heads, head_size] in the cache's "
+                             "input dtype")
     T = slot_mapping.shape[0]
     if key.shape[0] < T or value.shape[0] < T:
         raise ValueError("key/value hold fewer rows than slot_mapping")
@@ -190,15 +212,15 @@ def _meta(t, name):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                            max_seq_len: int, partition_size: int = 0, workspace=None,
-                           lse_out=None):
+                           lse_out=None, k_scale=None, v_scale=None):
     """Decode attention, one query row per sequence.  out/q: [S, Hq, D].
     max_seq_len is a host-side upper bound of seq_lens (no device sync)."""
     _require_gpu(out, q, block_tables, seq_lens, workspace, lse_out)
-    desc = cache_descriptor(k_cache, v_cache)
+    desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     _meta(block_tables, "block_tables")
     _meta(seq_lens, "seq_lens")
-    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
-        raise ValueError("q/out must be contiguous and in the cache dtype")
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache's input dtype")
     S, Hq, D = q.shape
     if out.shape != q.shape or D != k_cache.shape[3] or block_tables.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("shape mismatch")
@@ -216,14 +238,15 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
 
 def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
                            scale: float, max_query_len: int, max_seq_len: int, causal: bool = True,
-                           partition_size: int = 0, workspace=None, lse_out=None):
+                           partition_size: int = 0, workspace=None, lse_out=None,
+                           k_scale=None, v_scale=None):
     """Variable-length attention over a flattened batch (q/out [T, Hq, D])."""
     _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out)
-    desc = cache_descriptor(k_cache, v_cache)
+    desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
         _meta(t, n)
-    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
-        raise ValueError("q/out must be contiguous and in the cache dtype")
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache's input dtype")
     T, Hq, D = q.shape
     S = seq_lens.shape[0]
     if out.shape != q.shape or cu_seqlens_q.shape[0] != S + 1 or block_tables.shape[0] != S:

@@ -37,6 +37,7 @@ from typing import Optional
 import numpy as np
 
 BF16_QNAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
 F32_QNAN_BITS = np.uint32(0x7FC00000)
 
 # Threads used to draw the per-sequence K/V streams.  The result does not
@@ -69,10 +70,12 @@ class Workload:
     """One attention-layer step: cache contents, metadata and queries.
 
     Floating-point arrays are float32 for dtype 'f32' and raw bfloat16 bits
-    (uint16) for dtype 'bf16'.
+    (uint16) for dtype 'bf16'.  dtype 'fp8': the caches hold e4m3 codes
+    (uint8) with per-kv-head float32 scales k_scale / v_scale; q and the new
+    key/value rows are bfloat16 bits.
     """
     name: str
-    dtype: str                       # 'f32' | 'bf16'
+    dtype: str                       # 'f32' | 'bf16' | 'fp8'
     num_heads: int
     num_kv_heads: int
     head_size: int
@@ -90,6 +93,8 @@ class Workload:
     slot_mapping: Optional[np.ndarray] = None   # int64 [num_new]
     partition_size: int = 0          # 0 = library default
     sigma: float = 1.0
+    k_scale: Optional[np.ndarray] = None        # fp8: float32 [num_kv_heads]
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -120,6 +125,16 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes of one cached element."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
+    @property
+    def io_dtype(self) -> str:
+        """dtype of q / out / new key and value rows."""
+        return "bf16" if self.dtype == "fp8" else self.dtype
+
+    @property
+    def io_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
 
     def kv_block_bytes(self) -> int:
@@ -141,14 +156,40 @@ class Workload:
 def _poison(shape, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.full(shape, F32_QNAN_BITS, dtype=np.uint32).view(np.float32)
+    if dtype == "fp8":
+        return np.full(shape, E4M3_NAN, dtype=np.uint8)
     return np.full(shape, BF16_QNAN, dtype=np.uint16)
 
 
+def _draw_e4m3_codes(rng: np.random.Generator, n: int) -> np.ndarray:
+    """e4m3 codes drawn directly (no rounding of real values): sign U{0,1},
+    exponent field clip(rint(N(10, 2)), 1, 15), mantissa U{0..7}; the NaN
+    code becomes 0x7E / 0xFE (448)."""
+    e = np.clip(np.rint(rng.normal(10.0, 2.0, n)), 1, 15).astype(np.uint8)
+    m = rng.integers(0, 8, size=n, dtype=np.uint8)
+    sgn = rng.integers(0, 2, size=n, dtype=np.uint8)
+    c = (sgn << 7) | (e << 3) | m
+    nan = (c & 0x7F) == 0x7F
+    c[nan] = (c[nan] & 0x80) | 0x7E
+    return c.astype(np.uint8)
+
+
 def _draw(rng: np.random.Generator, n: int, sigma: float, dtype: str) -> np.ndarray:
+    if dtype == "fp8":
+        return _draw_e4m3_codes(rng, n)
     x = rng.standard_normal(n, dtype=np.float32)
     if sigma != 1.0:
         x *= np.float32(sigma)
     return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def _draw_scales(rng: np.random.Generator, num_kv_heads: int, dtype: str):
+    """fp8 caches: per-kv-head scales U[0.5, 1) / 32 (float32), K then V."""
+    if dtype != "fp8":
+        return None, None
+    k = (rng.uniform(0.5, 1.0, num_kv_heads) / 32).astype(np.float32)
+    v = (rng.uniform(0.5, 1.0, num_kv_heads) / 32).astype(np.float32)
+    return k, v
 
 
 def blocks_needed(seq_len: int, block_size: int) -> int:
@@ -221,8 +262,10 @@ def make_decode(name, seq_lens, num_heads, num_kv_heads, head_size, block_size, 
     num_blocks, bt = build_pool(seq_lens, block_size, meta_rng, num_blocks)
     children = root.spawn(1 + len(seq_lens))
     q_rng = np.random.Generator(np.random.PCG64(children[0]))
-    q = _draw(q_rng, len(seq_lens) * num_heads * head_size, sigma, dtype).reshape(
+    io = "bf16" if dtype == "fp8" else dtype
+    q = _draw(q_rng, len(seq_lens) * num_heads * head_size, sigma, io).reshape(
         len(seq_lens), num_heads, head_size)
+    k_scale, v_scale = _draw_scales(q_rng, num_kv_heads, dtype)
     shape = (num_blocks, block_size, num_kv_heads, head_size)
     k_cache = _poison(shape, dtype)
     v_cache = _poison(shape, dtype)
@@ -230,7 +273,8 @@ def make_decode(name, seq_lens, num_heads, num_kv_heads, head_size, block_size, 
     return Workload(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_kv_heads,
                     head_size=head_size, block_size=block_size, scale=1.0 / math.sqrt(head_size),
                     causal=False, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=bt,
-                    seq_lens=seq_lens, partition_size=partition_size, sigma=sigma)
+                    seq_lens=seq_lens, partition_size=partition_size, sigma=sigma,
+                    k_scale=k_scale, v_scale=v_scale)
 
 
 def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_size, block_size,
@@ -255,9 +299,11 @@ def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_si
     _fill_cache(k_cache, v_cache, bt, context_lens, block_size, children[2:], sigma, dtype)
     T = int(query_lens.sum())
     new_rng = np.random.Generator(np.random.PCG64(children[1]))
-    key_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, dtype).reshape(T, num_kv_heads, head_size)
-    value_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, dtype).reshape(T, num_kv_heads, head_size)
-    q = _draw(new_rng, T * num_heads * head_size, sigma, dtype).reshape(T, num_heads, head_size)
+    io = "bf16" if dtype == "fp8" else dtype
+    key_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, io).reshape(T, num_kv_heads, head_size)
+    value_new = _draw(new_rng, T * num_kv_heads * head_size, sigma, io).reshape(T, num_kv_heads, head_size)
+    q = _draw(new_rng, T * num_heads * head_size, sigma, io).reshape(T, num_heads, head_size)
+    k_scale, v_scale = _draw_scales(new_rng, num_kv_heads, dtype)
     cu = np.zeros(S + 1, dtype=np.int32)
     cu[1:] = np.cumsum(query_lens)
     slot = np.empty(T, dtype=np.int64)
@@ -268,7 +314,8 @@ def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_si
                     head_size=head_size, block_size=block_size, scale=1.0 / math.sqrt(head_size),
                     causal=causal, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=bt,
                     seq_lens=seq_lens, cu_seqlens_q=cu, key_new=key_new, value_new=value_new,
-                    slot_mapping=slot, partition_size=partition_size, sigma=sigma)
+                    slot_mapping=slot, partition_size=partition_size, sigma=sigma,
+                    k_scale=k_scale, v_scale=v_scale)
 
 
 # --------------------------------------------------------------------------
@@ -282,9 +329,11 @@ CONFIG_NAMES = {
     3: "gqa_decode_bf16",
     4: "long_context_splitkv_decode_bf16",
     5: "mixed_chunked_prefill_decode_bf16",
+    6: "llama7b_mha_decode_fp8",
+    7: "gqa_decode_fp8",
 }
 
-DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4}
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2}   # 6, 7: the lengths and pools of 2, 3
 
 
 def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
@@ -311,7 +360,7 @@ def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=No
 def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
                 max_len: Optional[int] = None, num_chunks: Optional[int] = None,
                 chunk_len: Optional[int] = None) -> Workload:
-    """Build workload `cfg` (1..5).  num_seqs / max_len / num_chunks /
+    """Build workload `cfg` (1..7).  num_seqs / max_len / num_chunks /
     chunk_len shrink it for quick parity runs; None keeps the full size."""
     if seed is None:
         seed = DEFAULT_SEEDS[cfg]
@@ -344,6 +393,11 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         qlens = np.concatenate([np.full(nc, cl), np.ones(nd)]).astype(np.int64)
         return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16", seed, causal=True,
                            meta_rng=meta, root=root)
+    if cfg in (6, 7):
+        # the MHA and GQA decode shapes of workloads 2 and 3 over an fp8 cache
+        L = config_lengths(cfg - 4, meta, num_seqs, max_len)
+        hq, hkv = (32, 32) if cfg == 6 else (32, 8)
+        return make_decode(name, L, hq, hkv, 128, 16, "fp8", seed, meta_rng=meta, root=root)
     raise ValueError(cfg)
 
 
@@ -358,14 +412,16 @@ def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
     e = w.elem_bytes
     L = w.seq_lens.astype(np.int64)
     kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * e
-    qo = 2 * w.num_q_rows * w.num_heads * w.head_size * e
+    qo = 2 * w.num_q_rows * w.num_heads * w.head_size * w.io_bytes
     meta = 4 * int(sum(blocks_needed(x, w.block_size) for x in L)) + 4 * w.num_seqs
     if w.cu_seqlens_q is not None:
         meta += 4 * (w.num_seqs + 1)
+    if w.k_scale is not None:
+        meta += 2 * 4 * w.num_kv_heads
     total = kv + qo + meta
     if include_write and w.slot_mapping is not None:
         T = int(w.slot_mapping.shape[0])
-        total += 2 * 2 * T * w.num_kv_heads * w.head_size * e + 8 * T
+        total += 2 * T * w.num_kv_heads * w.head_size * (w.io_bytes + e) + 8 * T
     return total
 
 

@@ -27,6 +27,8 @@ def np_to_dev(x: np.ndarray, dtype: str, device="cuda"):
     t = torch()
     if dtype == "bf16":
         return t.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(t.bfloat16).to(device)
+    if dtype == "fp8":
+        return t.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device).view(t.float8_e4m3fn)
     return t.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
@@ -36,6 +38,8 @@ def dev_to_bits(t_):
     x = t_.detach().cpu()
     if x.dtype == t.bfloat16:
         return x.view(t.int16).numpy().view(np.uint16)
+    if x.dtype == t.float8_e4m3fn:
+        return x.view(t.uint8).numpy()
     return x.numpy()
 
 
@@ -49,14 +53,16 @@ class DevWorkload:
     def __init__(self, w: W.Workload, device="cuda"):
         t = torch()
         self.w = w
-        self.q = np_to_dev(w.q, w.dtype, device)
+        self.q = np_to_dev(w.q, w.io_dtype, device)
         self.k_cache = np_to_dev(w.k_cache, w.dtype, device)
         self.v_cache = np_to_dev(w.v_cache, w.dtype, device)
         self.block_tables = t.from_numpy(w.block_tables).to(device)
         self.seq_lens = t.from_numpy(w.seq_lens).to(device)
         self.cu_seqlens_q = None if w.cu_seqlens_q is None else t.from_numpy(w.cu_seqlens_q).to(device)
-        self.key_new = None if w.key_new is None else np_to_dev(w.key_new, w.dtype, device)
-        self.value_new = None if w.value_new is None else np_to_dev(w.value_new, w.dtype, device)
+        self.key_new = None if w.key_new is None else np_to_dev(w.key_new, w.io_dtype, device)
+        self.value_new = None if w.value_new is None else np_to_dev(w.value_new, w.io_dtype, device)
+        self.k_scale = None if w.k_scale is None else t.from_numpy(w.k_scale).to(device)
+        self.v_scale = None if w.v_scale is None else t.from_numpy(w.v_scale).to(device)
         self.slot_mapping = None if w.slot_mapping is None else t.from_numpy(w.slot_mapping).to(device)
         self.out = t.empty_like(self.q)
         self.lse = t.empty(self.q.shape[0], self.q.shape[1], dtype=t.float32, device=device)
@@ -69,16 +75,19 @@ def run(dw: DevWorkload, partition_size=None, lse=True, write=True):
     w = dw.w
     ps = w.partition_size if partition_size is None else partition_size
     if write and dw.slot_mapping is not None:
-        pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new, dw.slot_mapping)
+        pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new, dw.slot_mapping,
+                               k_scale=dw.k_scale, v_scale=dw.v_scale)
     if w.cu_seqlens_q is None:
         pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                        dw.seq_lens, w.scale, w.max_seq_len, partition_size=ps,
-                                       lse_out=dw.lse if lse else None)
+                                       lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
+                                       v_scale=dw.v_scale)
     else:
         pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
                                        dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
                                        w.max_seq_len, causal=w.causal, partition_size=ps,
-                                       lse_out=dw.lse if lse else None)
+                                       lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
+                                       v_scale=dw.v_scale)
     return dw.out
 
 
@@ -89,7 +98,11 @@ def oracle_inputs(w: W.Workload):
     if w.slot_mapping is None:
         return w.k_cache, w.v_cache
     kc, vc = w.k_cache.copy(), w.v_cache.copy()
-    oracle.kv_cache_write(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size)
+    if w.dtype == "fp8":
+        oracle.kv_cache_write_fp8(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size,
+                                  w.k_scale, w.v_scale)
+    else:
+        oracle.kv_cache_write(kc, vc, w.key_new, w.value_new, w.slot_mapping, w.block_size)
     return kc, vc
 
 
@@ -98,7 +111,7 @@ def reference(w: W.Workload, pairs=None):
     kc, vc = oracle_inputs(w)
     return oracle.paged_attention(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size,
                                   w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
-                                  pairs=pairs)
+                                  pairs=pairs, k_scale=w.k_scale, v_scale=w.v_scale)
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):

@@ -1,0 +1,160 @@
+"""GPU parity of the fp8 (e4m3) KV cache: the quantising slot write against
+the oracle bit for bit, decode attention against the oracle within the
+bfloat16 tolerances, exact needle indexing, and identity with the bfloat16
+path when the scales are powers of two."""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_50_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_50_amd import pagedkv
+    pagedkv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _decode_rows_varlen(seed=21, n=40, max_len=900):
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(0, max_len, size=n)
+    return W.make_varlen("fp8_rows", ctx, np.ones(n, dtype=np.int64), 32, 8, 128, 16, "fp8", seed)
+
+
+def test_fp8_kv_write_bit_exact():
+    torch = G.torch()
+    w = _decode_rows_varlen()
+    key, val = w.key_new.copy(), w.value_new.copy()
+    # special inputs: saturation, NaN, signed zero, tiny values, plus 3 padded rows
+    key[0, 0, :4] = [0x4700, 0xC700, 0x7FC0, 0x8000]        # 32768, -32768, NaN, -0.0
+    key[1, 1, :3] = [0x0001, 0x8001, 0x3A80]                # tiny +-, 9.8e-4
+    val[2, 3, :2] = [0x7F7F, 0xFF7F]                        # +-max bfloat16
+    slots = w.slot_mapping.copy()
+    slots[[5, 17]] = -1
+    pad = np.full((3,) + key.shape[1:], 0x4000, dtype=np.uint16)
+    key = np.concatenate([key, pad])
+    val = np.concatenate([val, pad])
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_cache_write_fp8(kc, vc, key, val, slots, w.block_size, w.k_scale, w.v_scale)
+    _announce(f"fp8 kv_write T={len(slots)}")
+    from paged_kv_cache_50_amd import pagedkv
+    dk = G.np_to_dev(w.k_cache, "fp8")
+    dv = G.np_to_dev(w.v_cache, "fp8")
+    pagedkv.kv_cache_write(dk, dv, G.np_to_dev(key, "bf16"), G.np_to_dev(val, "bf16"),
+                           torch.from_numpy(slots).cuda(), k_scale=torch.from_numpy(w.k_scale).cuda(),
+                           v_scale=torch.from_numpy(w.v_scale).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(G.dev_to_bits(dk), kc)
+    assert np.array_equal(G.dev_to_bits(dv), vc)
+
+
+@pytest.mark.parametrize("cfg", [6, 7])
+@pytest.mark.parametrize("ps", [0, -1, 128])
+def test_fp8_decode_small(cfg, ps):
+    w = W.make_config(cfg, num_seqs=6, max_len=1500)
+    _announce(f"fp8 config{cfg} small ps={ps} seq_lens={list(w.seq_lens)}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=ps)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 config{cfg} ps={ps}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 config{cfg} ps={ps}")
+
+
+@pytest.mark.parametrize("cfg", [6, 7])
+def test_fp8_full_size_sampled(cfg):
+    """Full-size fp8 workloads in the launch configuration the benchmark
+    times; the oracle checks sampled (sequence, kv head) pairs."""
+    w = W.make_config(cfg)
+    rng = np.random.default_rng(cfg)
+    pairs = [(int(s), int(rng.integers(w.num_kv_heads))) for s in
+             rng.choice(w.num_seqs, size=min(12, w.num_seqs), replace=False)]
+    _announce(f"fp8 config{cfg} full, {len(pairs)} sampled pairs")
+    dw = G.DevWorkload(w)
+    G.run(dw)
+    ref, ref_lse = G.reference(w, pairs=pairs)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 config{cfg} full")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 config{cfg} full")
+
+
+@pytest.mark.parametrize("ps", [-1, 128])
+def test_fp8_needle_bit_exact(ps):
+    """q = 64 e0 and one key = 64 e0 (code 0x68, scale 1): the needle's
+    logit dominates by far, every other probability underflows to 0, and
+    the output is that token's V row times a power-of-two scale, exactly."""
+    w = W.make_decode("fp8_needle", [300, 77, 513], 8, 2, 128, 16, "fp8", seed=31)
+    w.k_scale = np.ones(2, dtype=np.float32)
+    w.v_scale = np.full(2, 2.0 ** -5, dtype=np.float32)
+    w.q[:] = 0
+    w.q[:, :, 0] = W.f32_to_bf16_bits(np.float32(64.0))
+    needles = [257, 16, 512]
+    for s, L in enumerate(w.seq_lens):
+        blk = w.block_tables[s, np.arange(L) // 16]
+        off = np.arange(L) % 16
+        w.k_cache[blk, off, :, 0] = 0                          # every key orthogonal to e0
+        j = needles[s]
+        w.k_cache[w.block_tables[s, j // 16], j % 16, :, 0] = 0x68   # 64.0
+    _announce(f"fp8 needle ps={ps}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=ps)
+    out = G.dev_to_bits(dw.out)
+    for s, j in enumerate(needles):
+        blk, off = w.block_tables[s, j // 16], j % 16
+        for h in range(8):
+            v = oracle.e4m3_decode(w.v_cache[blk, off, h // 4]) * 2.0 ** -5
+            assert np.array_equal(out[s, h], W.f32_to_bf16_bits(v.astype(np.float32))), (s, h)
+
+
+def test_fp8_equals_bf16_path_with_power_of_two_scales():
+    """The same values held as e4m3 codes with power-of-two scales or as
+    bfloat16: the two kernels' outputs are bit-identical."""
+    torch = G.torch()
+    w8 = W.make_config(7, num_seqs=10, max_len=2500)
+    w8.k_scale = np.full(w8.num_kv_heads, 2.0 ** -6, dtype=np.float32)
+    w8.v_scale = np.full(w8.num_kv_heads, 2.0 ** -4, dtype=np.float32)
+    kb = W.f32_to_bf16_bits((oracle.e4m3_decode(w8.k_cache) * 2.0 ** -6).astype(np.float32))
+    vb = W.f32_to_bf16_bits((oracle.e4m3_decode(w8.v_cache) * 2.0 ** -4).astype(np.float32))
+    kb[w8.k_cache == 0x7F] = W.BF16_QNAN                       # poison stays poison
+    vb[w8.v_cache == 0x7F] = W.BF16_QNAN
+    import dataclasses
+    wb = dataclasses.replace(w8, dtype="bf16", k_cache=kb, v_cache=vb, k_scale=None, v_scale=None)
+    _announce("fp8 vs bf16 identity")
+    d8, db = G.DevWorkload(w8), G.DevWorkload(wb)
+    G.run(d8, partition_size=256)
+    import os
+    force = os.environ.get("PKV_DECODE_KERNEL")
+    G.run(db, partition_size=256)
+    torch.cuda.synchronize()
+    if force in (None, "", "mfma"):
+        assert np.array_equal(G.dev_to_bits(d8.out), G.dev_to_bits(db.out))
+    G.assert_close(G.dev_to_f64(d8.out), G.dev_to_f64(db.out), "bf16", "fp8 vs bf16")
+
+
+def test_fp8_varlen_decode_rows_with_write():
+    w = _decode_rows_varlen(seed=22, n=30, max_len=2000)
+    _announce(f"fp8 varlen rows + write, {w.num_seqs} seqs")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=256)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", "fp8 varlen rows")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "fp8 varlen rows")
+
+
+def test_fp8_prefill_rows_are_rejected():
+    from paged_kv_cache_50_amd import pagedkv
+    w = W.make_varlen("fp8_chunk", [10, 5], [3, 1], 8, 2, 128, 16, "fp8", seed=23)
+    dw = G.DevWorkload(w)
+    with pytest.raises(pagedkv.PagedKVError) as e:
+        G.run(dw, write=False)
+    assert e.value.status == 3
