@@ -231,15 +231,19 @@ pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks
                                  char* msg, size_t msg_len);
 
 /*
- * Per-launch timing of the main attention kernel, for benchmarks.  When
- * enabled, each attention call records a pair of HIP events on its stream
- * around its main kernel (the decode partition kernel, or the prefill kernel
- * of a varlen call).  pkv_timing_read waits for the recorded events, writes
- * up to `cap` durations in milliseconds (oldest first) and returns how many
- * were written; it then clears the record.  Up to 4096 launches are kept.
- * Not for use under graph capture.  Returns PKV_OK or PKV_ERR_HIP.
+ * Per-launch timing of the main attention kernel, for benchmarks.  With
+ * every_n > 0, one attention call in every_n (the first, then every n-th)
+ * records a pair of HIP events on its stream around its main kernel (the
+ * decode partition kernel, or the prefill kernel of a varlen call); each
+ * record costs a few microseconds of stream time, so sampling keeps the
+ * timed steps close to untimed ones.  every_n = 0 disables timing.
+ * pkv_timing_read waits for the recorded events, writes up to `cap`
+ * durations in milliseconds (oldest first) and returns how many were
+ * written; it then clears the record.  Up to 4096 launches are kept.  Not
+ * for use under graph capture.  Returns PKV_OK, PKV_ERR_SHAPE for
+ * every_n < 0, or PKV_ERR_HIP.
  */
-pkv_status pkv_timing_enable(int32_t enable);
+pkv_status pkv_timing_enable(int32_t every_n);
 int32_t pkv_timing_read(float* ms, int32_t cap);
 
 #ifdef __cplusplus

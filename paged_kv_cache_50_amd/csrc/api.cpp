@@ -9,7 +9,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
 #include <unordered_set>
 
 #include "../../include/pagedkv.h"
@@ -18,6 +17,8 @@
 namespace {
 
 using pkv::AttnArgs;
+using pkv::timing_begin;
+using pkv::timing_end;
 
 constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kPartitionQuantum = 32;
@@ -95,42 +96,6 @@ int heads_per_chunk(int group) {
   for (int gt : {8, 4, 2, 1})
     if (group % gt == 0) return gt;
   return 1;
-}
-
-// ----------------------------------------------------------------- timing
-struct Timing {
-  std::mutex mu;
-  bool enabled = false;
-  static constexpr int kCap = 4096;
-  hipEvent_t start[kCap] = {};
-  hipEvent_t stop[kCap] = {};
-  int64_t head = 0;  // oldest unread record
-  int64_t tail = 0;  // next record
-};
-Timing g_timing;
-
-bool timing_begin(hipStream_t st, int* slot) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
-  if (!g_timing.enabled) return false;
-  const int i = (int)(g_timing.tail % Timing::kCap);
-  if (!g_timing.start[i]) {
-    // timing-only events: without the system-scope fence a record costs no
-    // L2 writeback/invalidate (which would otherwise add a few microseconds
-    // around every timed launch and cool the caches of the next kernel)
-    if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess)
-      return false;
-    if (hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess)
-      return false;
-  }
-  if (g_timing.tail - g_timing.head >= Timing::kCap) g_timing.head++;  // overwrite oldest
-  if (hipEventRecord(g_timing.start[i], st) != hipSuccess) return false;
-  *slot = i;
-  return true;
-}
-
-void timing_end(hipStream_t st, int slot) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
-  if (hipEventRecord(g_timing.stop[slot], st) == hipSuccess) g_timing.tail++;
 }
 
 // ----------------------------------------------------------------- launch helpers
@@ -530,26 +495,5 @@ pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks
   return PKV_OK;
 }
 
-pkv_status pkv_timing_enable(int32_t enable) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
-  g_timing.enabled = enable != 0;
-  g_timing.head = g_timing.tail = 0;
-  return PKV_OK;
-}
-
-int32_t pkv_timing_read(float* ms, int32_t cap) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
-  int32_t n = 0;
-  for (int64_t k = g_timing.head; k < g_timing.tail && n < cap; ++k) {
-    const int i = (int)(k % Timing::kCap);
-    if (hipEventSynchronize(g_timing.stop[i]) != hipSuccess) return -1;
-    float t = 0.f;
-    if (hipEventElapsedTime(&t, g_timing.start[i], g_timing.stop[i]) != hipSuccess) return -1;
-    if (ms) ms[n] = t;
-    ++n;
-  }
-  g_timing.head = g_timing.tail;
-  return n;
-}
 
 }  // extern "C"

@@ -70,6 +70,12 @@ struct KvWriteArgs {
   const float* v_scale;
 };
 
+// Benchmark timing (timing.cpp): timing_begin returns true, with a slot, when
+// this launch is one of the sampled ones and its start event was recorded;
+// timing_end then records the stop event after the launch.
+bool timing_begin(hipStream_t st, int* slot);
+void timing_end(hipStream_t st, int slot);
+
 // Launchers (return the launch error, hipSuccess on success).
 // fp8 = true: bfloat16 key/value quantised into e4m3 caches.
 hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8, hipStream_t stream);

@@ -290,8 +290,10 @@ def validate_metadata(block_tables, seq_lens, max_seq_len, num_blocks, block_siz
     return "" if st == PKV_OK else (msg.value.decode() or "invalid metadata")
 
 
-def timing_enable(enable: bool = True) -> None:
-    _check(lib().pkv_timing_enable(1 if enable else 0), "timing_enable")
+def timing_enable(enable: bool = True, every_n: int = 1) -> None:
+    """Record the main attention kernel's duration for one call in every_n
+    (enable=False turns timing off)."""
+    _check(lib().pkv_timing_enable(int(every_n) if enable else 0), "timing_enable")
 
 
 def timing_read(cap: int = 4096):
