@@ -114,10 +114,12 @@ pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_
 // One-row attention (decode, or the one-row sequences of a varlen batch):
 // picks the kernel, the head chunking and the partitions per workgroup (left
 // in `a` for the split merge that follows), launches over all z.
-pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, int64_t z_total,
-                          hipStream_t st) {
+// Matrix-core decode launch geometry for gy partitions: sets head chunks,
+// partitions per workgroup and the range order in `a`; returns (gx, ranges).
+std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cache* cache,
+                                                   unsigned gy) {
   const int group = a.num_heads / cache->num_kv_heads;
-  if (use_mfma_decode(cache, group)) {
+  {
     a.head_chunks = (group + 15) / 16;
     // a workgroup streams about kMfmaTokensPerWg tokens: consecutive
     // partitions share its queries and block-table row, and its fixed cost
@@ -135,6 +137,15 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
     a.range_desc = a.seq_order ? 1 : 0;
     const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
     const unsigned gparts = (gy + a.parts_per_wg - 1) / a.parts_per_wg;
+    return {gx, gparts};
+  }
+}
+
+pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, int64_t z_total,
+                          hipStream_t st) {
+  const int group = a.num_heads / cache->num_kv_heads;
+  if (use_mfma_decode(cache, group)) {
+    const auto [gx, gparts] = mfma_decode_geometry(a, cache, gy);
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
@@ -164,19 +175,53 @@ size_t order_offset(size_t rows, int32_t head_size) {
   return align16(rows * head_size * sizeof(float) + rows * sizeof(float));
 }
 
+// Workspace tail: the sequence order [num_seqs], then the list of multi-row
+// sequences [num_seqs] and its length [1].
+int32_t* order_area(const AttnArgs& a, const pkv_kv_cache* cache, void* workspace) {
+  const size_t rows = (size_t)a.num_splits * a.num_heads * a.num_seqs;
+  return reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                    order_offset(rows, cache->head_size));
+}
+
 // One-row decode launches with a split workspace order their sequences
-// longest first (the planner writes the order into the workspace).
+// longest first (the planner writes the order into the workspace).  With
+// `multi`, the planner also lists the multi-row sequences (mixed launch).
 pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspace,
-                          hipStream_t st) {
+                          hipStream_t st, bool multi = false) {
   if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads))
     return PKV_OK;
-  const size_t rows = (size_t)a.num_splits * a.num_heads * a.num_seqs;
-  int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                              order_offset(rows, cache->head_size));
-  if (pkv::launch_seq_order(a.seq_lens, a.num_seqs, a.max_seq_len, order, st) != hipSuccess)
+  int32_t* order = order_area(a, cache, workspace);
+  if (pkv::launch_seq_order(a.seq_lens, a.num_seqs, a.max_seq_len, order,
+                            multi ? a.cu_seqlens_q : nullptr, a.num_tokens,
+                            multi ? order + a.num_seqs : nullptr,
+                            multi ? order + 2 * a.num_seqs : nullptr,
+                            multi ? order + 2 * a.num_seqs + 1 : nullptr, st) != hipSuccess)
     return PKV_ERR_HIP;
   a.seq_order = order;
   return PKV_OK;
+}
+
+// Compute units of the current device (cached per device).
+int32_t device_cus() {
+  static int32_t cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Mixed batches (prefill chunks and decode rows) run as one interleaved
+// launch when both kinds use the matrix-core kernels and a split workspace
+// holds the planner's lists.  PKV_MIXED=0 keeps two launches (A/B runs).
+bool use_mixed_launch(const AttnArgs& a, const pkv_kv_cache* cache) {
+  static const char* env = std::getenv("PKV_MIXED");
+  if (env && std::strcmp(env, "0") == 0) return false;
+  return a.num_splits > 1 && use_mfma_prefill(cache) && !is_fp8(cache) &&
+         use_mfma_decode(cache, a.num_heads / cache->num_kv_heads);
 }
 
 int32_t num_splits_for(int32_t max_seq_len, int32_t P) {
@@ -280,7 +325,7 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
   const int32_t ns = num_splits_for(max_seq_len, P);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)ns * num_heads * num_seqs;
-  return order_offset(rows, head_size) + align16((size_t)num_seqs * sizeof(int32_t));
+  return order_offset(rows, head_size) + align16((size_t)(2 * num_seqs + 3) * sizeof(int32_t));
 }
 
 pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
@@ -396,6 +441,44 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
   a.head_chunks = group / gt;
   const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
 
+  // Prefill chunks and decode rows of one batch: a single interleaved launch.
+  if (max_query_len > 1 && use_mixed_launch(a, cache)) {
+    AttnArgs r = a;
+    r.mode = pkv::kModeVarlenRows;
+    r.partition_size = 0;
+    r.ws_o = nullptr;
+    r.ws_lse = nullptr;
+    int gc = 8;
+    while (group % gc) gc >>= 1;
+    r.head_chunks_gc = gc;
+    const int rows_per_wg = 16 * (8 / gc);
+    AttnArgs d = a;
+    d.mode = pkv::kModeVarlenOne;
+    d.seq_order = order_area(d, cache, workspace);   // written by the planner below
+    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
+    pkv::MixedGrid g{};
+    g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
+    g.pre_y = cache->num_kv_heads * (group / gc);
+    g.dec_x = (int32_t)gx_d;
+    g.dec_y = num_seqs;
+    g.dec_z = (int32_t)gparts;
+    g.n_dec = (int64_t)g.dec_x * g.dec_y * g.dec_z;
+    g.pre_list = d.seq_order + num_seqs;
+    g.pre_count = d.seq_order + 2 * num_seqs;
+    g.queues = order_area(d, cache, workspace) + 2 * num_seqs + 1;
+    g.workgroups = 2 * device_cus();                // two per CU (LDS and registers allow two)
+    const int64_t n_pre_max = (int64_t)g.pre_x * g.pre_y * num_seqs;
+    if (g.workgroups > 0 && n_pre_max < (int64_t)INT32_MAX && g.n_dec < (int64_t)INT32_MAX) {
+      st = plan_seq_order(d, cache, workspace, s, /*multi=*/true);
+      if (st != PKV_OK) return st;
+      int tslot = 0;
+      const bool timed = timing_begin(s, &tslot);
+      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, s) != hipSuccess) st = PKV_ERR_HIP;
+      if (timed) timing_end(s, tslot);
+      if (st != PKV_OK) return st;
+      return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+    }
+  }
   // Rows of sequences with several query rows (chunked prefill).
   if (max_query_len > 1) {
     AttnArgs r = a;

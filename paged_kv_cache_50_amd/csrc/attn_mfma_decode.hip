@@ -1,360 +1,25 @@
-// Grouped-query paged decode attention on the matrix cores (gfx950 MFMA).
-//
-// With GQA the query heads of one kv-head group read the same K/V rows, so
-// for each tile of cached tokens the work is a small dense contraction: the
-// logits of g query heads against 32 keys, then the g probability rows
-// against the 32 value rows (vLLM book, ch. 6 "Flux des paramètres du chemin
-// non-cascadé": one kernel gathering K/V through the block table).  Each kv
-// head's K/V tile is loaded once and shared by the group's query heads.
-//
-// Layout (v_mfma_f32_16x16x32_bf16, N = 16 query-head columns, g <= 16 used):
-//   S^T[32 tok x 16 heads] = K[32 x 128] . Q^T[128 x 16]: the K tile is read
-//     from HBM as whole 256-byte token rows (16 lanes x 16 bytes per row, the
-//     most efficient gather pattern), staged in LDS with an XOR swizzle of the
-//     16-byte slots and read back as A operands (lane = token row, 8 dims),
-//     conflict-free on both sides; Q^T is a B operand held in registers.
-//   The S^T accumulator gives each lane 8 logits of ONE head column, so the
-//   online-softmax max/sum need only two cross-lane steps (permlane swaps
-//   across the 4 token groups), and the probabilities are already laid out as
-//   the B operand P^T of the second product.
-//   O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16]: the V tile is written to LDS
-//   in its natural token-major layout and read back transposed with
-//   ds_read_b64_tr_b16, two reads per 16-dim tile.
-//   O^T's accumulator column is again the lane's head, so the rescale by
-//   exp(m_old - m_new) is a plain per-lane multiply.
-// A workgroup (4 waves) owns one (sequence, kv-head chunk, range of
-// consecutive key partitions); the grid puts ranges on its slowest axis so
-// that the workgroups of ranges a short sequence does not have are dispatched
-// last.  Either wave w owns partition w of a full 4-partition range, or the
-// waves take the range's 32-token tiles round-robin.  A wave copies its tile
-// from registers into its LDS area, issues the next tile's loads into the
-// same registers (block ids run one tile further ahead) and computes from LDS
-// while they are in flight; the 4 waves merge their softmax states through
-// LDS at the end and write the row, or the range's partial result.
-// Tokens past the partition end are loaded from an in-bounds slot of the last
-// valid block; their logits are replaced by -inf and their V rows by zeros
-// (select, never multiply), so stale NaNs in unused cache slots cannot reach
-// the result.
-#include "attn_common.h"
-#include "device_common.h"
-#include "pkv_internal.h"
+// Grouped-query (and fp8) decode kernel on the matrix cores: one workgroup per
+// (kv-head chunk, row item, key range); the work itself is dec::decode_block.
+#include "attn_mfma_decode.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kD = 128;
-constexpr int kTile = 32;                 // tokens per wave step
-constexpr int kKTileBytes = kTile * kD * 2;
-constexpr int kVPitch = kD * 2 + 16;      // LDS bytes per V token row (padded)
-constexpr int kVTileBytes = kTile * kVPitch;
-constexpr int kWaveLds = kKTileBytes + kVTileBytes;
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ float xmax16_32(float x) {
-  // max over the 4 lanes {l, l^16, l^32, l^48}: the token groups of a column
-  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
-  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
-}
-
-__device__ __forceinline__ float xsum16_32(float x) {
-  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = __int_as_float(p16[0]) + __int_as_float(p16[1]);
-  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(p32[0]) + __int_as_float(p32[1]);
-}
-
-// LDS byte offset of 16-byte chunk c (0..15) of token row t in a K tile:
-// slots are XOR-swizzled by the row so that 16 lanes reading the same chunk
-// of 16 different rows hit 16 different bank groups.
-__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + ((c ^ (t & 15)) << 4); }
-
-// FP8: the caches hold e4m3 codes with per-kv-head scales; a token row is
-// then 128 bytes, read by 8 lanes, and converted (exactly) to bfloat16 while
-// it is staged in LDS, so the matrix-core part is the same.  The K scale is
-// folded into the logit scale and the V scale into the output.
 template <int BS, bool FP8>
-__global__ void __launch_bounds__(kThreads, 2) attn_mfma_decode_kernel(const AttnArgs a) {
-  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
-  constexpr int kBlkPerTile = kTile / BS;
-  constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
-  constexpr int kRowsPerLoad = FP8 ? 8 : 4;          // token rows per wave load
-  constexpr int kLoads = kTile / kRowsPerLoad;       // loads per tile (K and V each)
-
-  __shared__ __attribute__((aligned(16))) char s_lds[kWaves * kWaveLds];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-
-  Item it;
-  const int zi = blockIdx.y + a.z_base;
-  if (!resolve_item(a, a.seq_order ? load_uniform_i32(a.seq_order, zi) : zi, it)) return;
-  // This workgroup covers partitions [part_first, part_end) of the row (one
-  // "range"); ranges sit on the slowest grid axis so that the workgroups of
-  // ranges a short sequence does not have dispatch last.
-  const int rz = a.range_desc ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
-  const int part_first = rz * a.parts_per_wg;
-  if (rz >= it.nranges) return;
-  const int part_end = min(part_first + a.parts_per_wg, it.nparts);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;     // MFMA column (query head) / A row (token or dim)
-  const int kg = lane >> 4;    // k group / token row of a natural load
-  const int group = a.num_heads / a.num_kv_heads;
-  const int kvh = blockIdx.x / a.head_chunks;
-  const int chunk = blockIdx.x % a.head_chunks;
-  const int h0 = kvh * group + chunk * 16;
-  const int G = min(16, group - chunk * 16);
-
-  const int pstart = part_first * it.P;
-  const int pend = min(part_end * it.P, it.L_end);
-
-  // Q^T B operands: lane (kg, n) holds q[h0+n][(4j+kg)*8 .. +8] for k-step j.
-  bf16x8_t qb[4];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((int64_t)it.row * a.num_heads + h0 + n) * kD;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < G) v = *reinterpret_cast<const u32x4*>(qrow + (4 * j + kg) * 8);
-      qb[j] = as_bf16x8(v);
-    }
-  }
-
-  f32x4 o[8];
-#pragma unroll
-  for (int jd = 0; jd < 8; ++jd) o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-
-  const int32_t* __restrict__ bt = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
-  const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
-  const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
-  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD * kEB;   // bytes
-  const uint32_t head_off = (uint32_t)kvh * kD * kEB;
-  const int64_t blk_stride = a.block_stride * kEB;
-  float logit_scale = a.scale_log2, out_scale = 1.f;
-  if constexpr (FP8) {
-    logit_scale *= a.k_scale[kvh];
-    out_scale = a.v_scale[kvh];
-  }
-  // lane's place in a natural load: token row within the load, byte offset
-  const int lrow = FP8 ? (lane >> 3) : kg;
-  const int lbyte = FP8 ? (lane & 7) * 16 : n * 16;
-  const int64_t max_blk = a.num_blocks - 1;
-  const int ntiles = (pend > pstart) ? (pend - pstart + kTile - 1) / kTile : 0;
-  const int last_bi = (pend - 1) / BS;
-
-  char* klds = s_lds + wave * kWaveLds;
-  char* vlds = klds + kKTileBytes;
-
-  // Block ids of one tile (wave uniform, scalar loads), fetched a step early.
-  auto fetch_ids = [&](int tile, int64_t* ids) {
-    const int tbase = pstart + tile * kTile;
-#pragma unroll
-    for (int b = 0; b < kBlkPerTile; ++b) {
-      const int bi = __builtin_amdgcn_readfirstlane(min(tbase / BS + b, last_bi));
-      ids[b] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * blk_stride;
-    }
-  };
-
-  // K and V loads of one tile: kLoads + kLoads natural loads, each
-  // kRowsPerLoad whole token rows (row kRowsPerLoad * i + lrow, 16 bytes at
-  // lbyte).  Each such group of rows lies in one block.
-  auto issue = [&](const int64_t* ids, u32x4* K, u32x4* V) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int tok = kRowsPerLoad * i + lrow;
-      const int64_t boff = ids[(kRowsPerLoad * i) / BS];
-      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off + lbyte;
-      K[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + boff + lo));
-      V[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + boff + lo));
-    }
-  };
-
-  // Stage a tile in LDS (V rows of tokens past the end become zeros).
-  auto stage = [&](int tile, const u32x4* K, const u32x4* V) {
-    const int tbase = pstart + tile * kTile;
-    const bool full = tbase + kTile <= pend;
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int tok = kRowsPerLoad * i + lrow;
-      const bool dead = !full && tbase + tok >= pend;
-      if constexpr (FP8) {
-        // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
-        const int c = lane & 7;
-        u32x4 k0, k1, v0, v1;
-        e4m3x16_to_bf16x16(K[i], k0, k1);
-        e4m3x16_to_bf16x16(V[i], v0, v1);
-        if (dead) v0 = v1 = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
-        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32) = v0;
-        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32 + 16) = v1;
-      } else {
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
-        u32x4 v = V[i];
-        if (dead) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + n * 16) = v;
-      }
-    }
-    __asm__ volatile("" ::: "memory");
-  };
-
-  // One staged tile of the online softmax: logits, running max/sum, PV.
-  auto compute = [&](int tile) {
-    const int tbase = pstart + tile * kTile;
-    const bool full = tbase + kTile <= pend;
-
-    // logits S^T: A operand = K rows (token tt*16 + n, chunk 4j + kg)
-    f32x4 sacc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(klds + ktile_off(tt * 16 + n, 4 * j + kg));
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], sacc[tt], 0, 0, 0);
-      }
-    }
-    // lane holds tokens tt*16 + 4kg + i of head column n
-    float s[8];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tbase + tt * 16 + 4 * kg + i;
-        s[tt * 4 + i] = (full || tok < pend) ? sacc[tt][i] * logit_scale : -INFINITY;
-      }
-    float mx = s[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-    mx = xmax16_32(mx);
-    const float mn = fmaxf(m, mx);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
-    bf16x8_t pb;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(s[e] - mref);
-      psum += p;
-      pb[e] = (__bf16)p;
-    }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) o[jd] *= alpha;
-
-    // O^T += V^T P^T, one 16-dim tile at a time; the transposed reads give
-    // lane (kg, n) V[4kg + jj][16jd + n] and V[16 + 4kg + jj][16jd + n].
-    {
-      const int jj = n >> 2, q4 = n & 3;
-      const char* r0 = vlds + (4 * kg + jj) * kVPitch + q4 * 8;
-      const char* r1 = r0 + 16 * kVPitch;
-#pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
-        bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r0 + jd * 32));
-        bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r1 + jd * 32));
-        bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[jd], 0, 0, 0);
-      }
-    }
-    __asm__ volatile("" ::: "memory");
-  };
-
-  // The tile stream of this wave.  Tile t is waited for and copied into LDS;
-  // the loads of the wave's next tile are then issued into the same
-  // registers and stay in flight while t is computed from LDS.  Block ids run
-  // one tile further ahead.  Either wave w owns partition w of the range
-  // (long rows: waves never wait for each other), or the waves take the
-  // range's tiles round-robin (short rows: every wave gets work).
-  const int tpp = it.P / kTile;                      // tiles per partition (split rows)
-  int tile, tstep, tend;
-  if (a.wave_per_part && it.nparts > 1 && part_end - part_first == kWaves) {
-    tile = wave * tpp;
-    tend = min(ntiles, (wave + 1) * tpp);
-    tstep = 1;
-  } else {
-    tile = wave;
-    tend = ntiles;
-    tstep = kWaves;
-  }
-  u32x4 kr[kLoads], vr[kLoads];
-  int64_t ids[kBlkPerTile];
-  if (tile < tend) {
-    fetch_ids(tile, ids);
-    issue(ids, kr, vr);
-    if (tile + tstep < tend) fetch_ids(tile + tstep, ids);
-  }
-  while (tile < tend) {
-    stage(tile, kr, vr);
-    const int nt = tile + tstep;
-    if (nt < tend) {
-      issue(ids, kr, vr);
-      if (nt + tstep < tend) fetch_ids(nt + tstep, ids);
-    }
-    compute(tile);
-    tile = nt;
-  }
-
-  // Merge the 4 waves (log-sum-exp rule) and write the row, or this range's
-  // partial result.  Each wave stages its state inside its own LDS area.
-  lsum = xsum16_32(lsum);
-  float* so = reinterpret_cast<float*>(klds);       // [16 heads][128]
-#pragma unroll
-  for (int jd = 0; jd < 8; ++jd)
-    *reinterpret_cast<f32x4*>(so + n * kD + 16 * jd + 4 * kg) = o[jd];
-  if (kg == 0) {
-    s_m[wave][n] = m;
-    s_l[wave][n] = lsum;
-  }
-  __syncthreads();
-  const int range = rz;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int h = idx / kD;
-    const int d = idx % kD;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float Mref = (M == -INFINITY) ? 0.f : M;
-    float O = 0.f, Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][h] - Mref);
-      O = fmaf(reinterpret_cast<const float*>(s_lds + w * kWaveLds)[h * kD + d], f, O);
-      Ls = fmaf(s_l[w][h], f, Ls);
-    }
-    const int head = h0 + h;
-    if (it.nranges == 1) {
-      const float v = Ls > 0.f ? O / Ls * out_scale : 0.f;
-      static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * kD + d] =
-          static_cast<uint16_t>(f32_to_bf16_rne(v));
-      if (d == 0 && a.lse_out)
-        a.lse_out[(int64_t)it.row * a.num_heads + head] =
-            Ls > 0.f ? (M + acc_log2(Ls)) * kLn2 : -INFINITY;
-    } else {
-      const int64_t widx = ((int64_t)range * a.num_heads + head) * a.num_seqs + it.seq;
-      a.ws_o[widx * kD + d] = Ls > 0.f ? O / Ls * out_scale : 0.f;
-      if (d == 0) a.ws_lse[widx] = Ls > 0.f ? M + acc_log2(Ls) : -INFINITY;
-    }
-  }
+__global__ void __launch_bounds__(dec::kThreads, 2) attn_mfma_decode_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char s_lds[dec::kLdsBytes];
+  __shared__ float s_m[dec::kWaves][16];
+  __shared__ float s_l[dec::kWaves][16];
+  dec::decode_block<BS, FP8>(a, blockIdx.x, blockIdx.y + a.z_base, blockIdx.z, gridDim.z, s_lds,
+                             s_m, s_l);
 }
 
 template <bool FP8>
 hipError_t launch_typed(const AttnArgs& a, int block_size, dim3 grid, hipStream_t stream) {
   switch (block_size) {
-    case 8: hipLaunchKernelGGL((attn_mfma_decode_kernel<8, FP8>), grid, dim3(kThreads), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((attn_mfma_decode_kernel<16, FP8>), grid, dim3(kThreads), 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((attn_mfma_decode_kernel<32, FP8>), grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((attn_mfma_decode_kernel<8, FP8>), grid, dim3(dec::kThreads), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((attn_mfma_decode_kernel<16, FP8>), grid, dim3(dec::kThreads), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((attn_mfma_decode_kernel<32, FP8>), grid, dim3(dec::kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,0 +1,343 @@
+// Chunked-prefill paged attention on the matrix cores (gfx950 MFMA).
+//
+// Rows of sequences with several query rows: a prefill chunk of q_len new
+// tokens attends to the sequence's seq_len cached tokens (its own new tokens
+// already written by the slot write), query row i sitting at absolute
+// position i + seq_len - q_len and, when causal, seeing keys j <= that
+// position (vLLM book, ch. 6 "Branche de masque" for the bottom-right
+// alignment; "Structure des métadonnées" for query_start_loc / seq_lens;
+// «Khám phá vLLM», "Chạy forward pass", for the flattened batch).
+//
+// Work decomposition: a workgroup of 4 waves owns 8 column tiles of one kv
+// head's query-head group, a column tile being 16 consecutive query rows of
+// one query head; wave w owns column tiles 2w and 2w+1.  With g query heads
+// per kv head (chunks of GC <= 8 heads), the workgroup covers 8 / GC row
+// blocks of 16 rows.  Several workgroups share a CU, so their MFMA and
+// softmax phases interleave.  The key range [0, kv_end) is walked in 32-token
+// tiles that the 256 threads load cooperatively (two 16-byte chunks of K and
+// two of V per thread: whole 256-byte token rows) straight into a 4-stage LDS
+// ring with global_load_lds (no registers held), one barrier per tile, three
+// tiles in flight ahead of the one being computed.  The direct loads write
+// lane l's 16 bytes at offset 16*l, so the swizzled LDS layouts (16-byte slot
+// c ^ f(row)) are produced by choosing which chunk each lane fetches.  Tokens
+// past the key range load the last valid token (finite data; their
+// probabilities are exactly 0).  Per wave and tile:
+//   S^T[32 tok x 16 rows] = K . Q^T        (8 A reads from LDS, 8 MFMAs per column tile)
+//   online softmax per column (= query row), causal mask by select
+//   O^T[128 x 16] += V^T . P^T             (V^T via ds_read_b64_tr_b16, shared by both tiles)
+// Tiles lying wholly above a wave's rows on the causal diagonal are skipped,
+// and masks are applied only to tiles that cross a diagonal or the range end.
+// The running max used as the exponent reference is raised only when a
+// column's max grows by more than 2^8 (then the accumulators are rescaled);
+// otherwise probabilities up to 2^8 are accumulated against the old
+// reference.  The result is unchanged: output and log-sum-exp are formed
+// from the same reference.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_common.h"
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace pf {
+
+
+constexpr int kWaves = 4;
+constexpr int kColTiles = 2 * kWaves;          // column tiles per workgroup
+constexpr float kRescaleSlack = 8.f;            // log2 of the largest unscaled probability
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = 128;
+constexpr int kTile = 32;
+constexpr int kKBytes = kTile * kD * 2;          // 8 KiB
+constexpr int kVBytes = kTile * kD * 2;
+constexpr int kStageBytes = kKBytes + kVBytes;   // 16 KiB
+constexpr int kStages = 4;                       // LDS ring depth
+constexpr int kLdsBytes = kStages * kStageBytes;
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+// 16-byte slot of chunk c of token row t: K rows are swizzled so 16 lanes
+// reading one chunk of 16 rows (MFMA A operand) hit distinct bank groups; V
+// rows so the transposed reads (16 rows x 32 bytes) spread over all banks.
+__device__ __forceinline__ int kslot(int t, int c) { return c ^ (t & 15); }
+__device__ __forceinline__ int vslot(int t, int c) { return c ^ ((t & 7) << 1); }
+__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (kslot(t, c) << 4); }
+
+// NaN-propagating max (v_maximum3_f32): unlike fmaxf it needs no
+// canonicalisation of its operands.
+__device__ __forceinline__ float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+__device__ __forceinline__ float xmax16_32(float x) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = vmax(__int_as_float(p16[0]), __int_as_float(p16[1]));
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return vmax(__int_as_float(p32[0]), __int_as_float(p32[1]));
+}
+__device__ __forceinline__ float xsum16_32(float x) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(p16[0]) + __int_as_float(p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p32[0]) + __int_as_float(p32[1]);
+}
+
+// One workgroup's work: query tile bx, head group by of sequence seq.  The
+// caller provides the LDS ring (kLdsBytes, 16-byte aligned).
+template <int BS>
+__device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
+                                              char* __restrict__ s_lds) {
+  const int qs = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq), 0, a.num_tokens);
+  const int qe = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq + 1), 0, a.num_tokens);
+  const int q_len = min(qe - qs, a.max_query_len);
+  if (qe - qs <= 1) return;                          // one-row sequences: decode kernels
+  const int GC = a.head_chunks_gc;                   // query heads per column group (<= 8)
+  const int R = kColTiles / GC;                      // row blocks per workgroup
+  const int q0 = bx * 16 * R;
+  if (q0 >= q_len) return;
+  const int group = a.num_heads / a.num_kv_heads;
+  const int chunks = group / GC;
+  const int kvh = by / chunks;
+  const int hbase = kvh * group + (by % chunks) * GC;
+  const int L = clamp_seq_len(load_uniform_i32(a.seq_lens, seq), a.max_seq_len,
+                              a.max_blocks_per_seq, BS);
+  const int off = L - (qe - qs);                     // absolute position of row i = i + off
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int kg = lane >> 4;
+
+  // key range of the workgroup
+  const int q_last = min(q0 + 16 * R, q_len) - 1;
+  const int kv_end = a.causal ? max(0, min(L, q_last + off + 1)) : L;
+  const int ntiles = (kv_end + kTile - 1) / kTile;
+
+  // this wave's two column tiles: (row block, head)
+  int rowb[2], head[2];
+  bool live[2];
+  int wave_last_pos = -1;                            // largest key position this wave may see
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ct = 2 * wave + c;
+    rowb[c] = q0 + (ct / GC) * 16;
+    head[c] = hbase + ct % GC;
+    live[c] = rowb[c] < q_len;
+    if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
+  }
+  if (!a.causal) wave_last_pos = L - 1;
+
+  // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
+  bf16x8_t qb[2][4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int row = rowb[c] + n;
+    const bool ok = live[c] && row < q_len;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(qp + (4 * j + kg) * 8);
+      qb[c][j] = as_bf16x8(v);
+    }
+  }
+  // the queries must be resident before any tile load is issued: otherwise
+  // the first use of them inside the tile loop would wait for every load in
+  // flight on each iteration
+  __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+
+  f32x4 o[2][8];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) o[c][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = -INFINITY;
+    lsum[c] = 0.f;
+  }
+
+  // cooperative tile loads: load u (0, 1) of thread tid fills LDS row
+  // r = 16u + tid/16, slot tid%16, with the chunk of token r that belongs
+  // there; each wave covers 4 consecutive tokens per load, inside one block
+  // (block ids wave uniform).
+  const int lrow = tid >> 4;
+  const int lslot = tid & 15;
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
+  const uint32_t head_off = (uint32_t)kvh * kD;
+  const int64_t max_blk = a.num_blocks - 1;
+  const int last_tok = max(0, kv_end - 1);
+
+  // block offsets of tile t's two 16-token halves for this wave (scalar
+  // loads, fetched one iteration before they are used)
+  auto fetch_ids = [&](int t, int64_t* ids) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tw = min(t * kTile + 16 * u + 4 * wave, last_tok);       // wave's first token
+      const int bi = __builtin_amdgcn_readfirstlane(tw / BS);
+      ids[u] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+    }
+  };
+  // issue the direct-to-LDS loads of tile t into stage buf (4 per thread);
+  // tokens clamped to the last valid one stay in the block of the wave's
+  // first token
+  auto issue = [&](int t, const int64_t* ids, char* buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int r = 16 * u + lrow;
+      const int tok = min(t * kTile + r, last_tok);
+      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off;
+      const int kch = kslot(r, lslot);   // slot s holds chunk s ^ f(r): involution
+      const int vch = vslot(r, lslot);
+      char* kdst = buf + u * 4096 + wave * 1024;
+      char* vdst = buf + kKBytes + u * 4096 + wave * 1024;
+      __builtin_amdgcn_global_load_lds(kc + ids[u] + lo + kch * 8, (lds_void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vc + ids[u] + lo + vch * 8, (lds_void*)vdst, 16, 0, 0);
+    }
+  };
+
+  // MASKED: the tile may hold keys past a row's causal limit or the range
+  // end, or lie wholly above this wave's rows (skipped).
+  auto compute = [&](int t, const char* buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int j0 = t * kTile;
+    if (MASKED && j0 > wave_last_pos) return;        // wholly above this wave's diagonal
+    const char* kl = buf;
+    const char* vl = buf + kKBytes;
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) sacc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + ktile_off(tt * 16 + n, 4 * j + kg)));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][j], sacc[c][tt], 0, 0, 0);
+      }
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int qpos = rowb[c] + n + off;            // this lane's column = query row
+      const int lim = a.causal ? min(qpos, kv_end - 1) : kv_end - 1;
+      // raw logits; the scale is applied inside the exponent (one FMA)
+      float s[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + tt * 16 + 4 * kg + i;
+          s[tt * 4 + i] = (!MASKED || j <= lim) ? sacc[c][tt][i] : -INFINITY;
+        }
+      float mx = vmax(vmax(vmax(s[0], s[1]), vmax(s[2], s[3])), vmax(vmax(s[4], s[5]), vmax(s[6], s[7])));
+      mx = xmax16_32(mx) * a.scale_log2;             // scale > 0 preserves the max
+      // raise the reference only when the max outgrows it by the slack; the
+      // accumulators are then rescaled (alpha = 1 for columns that keep it)
+      const bool raise = mx > m[c] + kRescaleSlack;
+      const float mn = raise ? mx : m[c];
+      const float alpha = (m[c] == -INFINITY) ? 0.f : fast_exp2(m[c] - mn);
+      m[c] = mn;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
+      }
+      const float mref = (m[c] == -INFINITY) ? 0.f : m[c];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(s[e], a.scale_log2, -mref));
+        psum += p;
+        pb[c][e] = (__bf16)p;
+      }
+      lsum[c] += psum;
+    }
+    // lane (kg, n) reads 8 bytes of row 4kg + n/4 (and row + 16): dims
+    // 16jd + 4(n%4) .. +3, i.e. half (n%4)&1 of chunk 2jd + (n%4)/2
+    const int jj = n >> 2, q4 = n & 3;
+    const int t0 = 4 * kg + jj, t1 = t0 + 16;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const int ch = 2 * jd + (q4 >> 1);
+      const char* p0 = vl + t0 * (kD * 2) + (vslot(t0, ch) << 4) + (q4 & 1) * 8;
+      const char* p1 = vl + t1 * (kD * 2) + (vslot(t1, ch) << 4) + (q4 & 1) * 8;
+      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
+      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+      bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        o[c][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[c], o[c][jd], 0, 0, 0);
+    }
+  };
+
+  // LDS ring: tile t lives in stage t % kStages.  Before computing tile t a
+  // thread waits for its own loads of t (the loads of up to kStages - 2 later
+  // tiles may stay in flight), then the barrier makes t visible to all and
+  // guarantees every wave has finished tile t - 1, whose stage is refilled.
+  constexpr int kLoadsPerTile = 4;
+  int64_t ids[2];
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) {
+      fetch_ids(t, ids);
+      issue(t, ids, s_lds + t * kStageBytes);
+    }
+  if (kStages - 1 < ntiles) fetch_ids(kStages - 1, ids);
+  auto step = [&](int t, auto masked_tag) {
+    const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    // a bare barrier: __syncthreads() would add a fence that drains the
+    // loads of the tiles still in flight.  Each thread has waited for its own
+    // loads of tile t above; LDS reads of tile t - 1 were consumed before.
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int tn = t + kStages - 1;
+    if (tn < ntiles) {
+      issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
+      if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
+    }
+    compute(t, s_lds + (t % kStages) * kStageBytes, masked_tag);
+  };
+  // Tiles wholly at or below the workgroup's first row position and inside
+  // the key range need no mask for any wave; the rest (the diagonal band and
+  // the range end) take the masked path.  Every wave runs both loops over
+  // the same tiles, so the barriers stay matched.
+  const int unmasked_end = a.causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
+  const int tm = min(ntiles, max(0, (unmasked_end + 1) / kTile));
+  for (int t = 0; t < tm; ++t) step(t, std::false_type{});
+  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{});
+
+  // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float ls = xsum16_32(lsum[c]);
+    const int row = rowb[c] + n;
+    if (!live[c] || row >= q_len) continue;
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const uint32_t w0 = pack_bf16x2(o[c][jd][0] * inv, o[c][jd][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[c][jd][2] * inv, o[c][jd][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * jd + 4 * kg) = make_uint2(w0, w1);
+    }
+    if (kg == 0 && a.lse_out)
+      a.lse_out[(int64_t)(qs + row) * a.num_heads + head[c]] =
+          ls > 0.f ? (m[c] + acc_log2(ls)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace pf
+}  // namespace pkv

@@ -1,0 +1,87 @@
+// Mixed step in one launch: the chunked-prefill tiles and the decode rows of
+// a varlen batch run in one persistent grid (vLLM book, ch. 6 "Structure des
+// métadonnées": one forward over a batch that mixes prefill chunks and
+// decode rows).
+//
+// The prefill tiles keep the matrix cores and vector ALUs busy while the
+// decode rows stream the cache from HBM, so the two kinds of work should
+// overlap instead of running one after the other.  The hardware refills a
+// freed slot with the next workgroup in grid order, so a plain interleaved
+// grid ends up with every slot holding prefill work; here the grid has two
+// workgroups per CU, each starting on one kind and taking items from that
+// kind's queue (an atomic counter the planner zeroes before the launch),
+// moving to the other queue when its own is empty.  Every workgroup leaves
+// once both queues are exhausted.
+#include "attn_mfma_decode.h"
+#include "attn_mfma_prefill.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kLdsBytes = pf::kLdsBytes > dec::kLdsBytes ? pf::kLdsBytes : dec::kLdsBytes;
+static_assert(pf::kThreads == dec::kThreads, "one block shape");
+
+template <int BS>
+__global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const AttnArgs pre,
+                                                                       const AttnArgs dcd,
+                                                                       const MixedGrid g) {
+  __shared__ __attribute__((aligned(16))) char s_lds[kLdsBytes];
+  __shared__ float s_m[dec::kWaves][16];
+  __shared__ float s_l[dec::kWaves][16];
+  __shared__ int s_item;
+
+  // prefill items of the listed multi-row sequences; decode items as in the
+  // decode kernel's grid (kv-head chunk fastest, then row item, then range)
+  const int64_t n_pre = (int64_t)load_uniform_i32(g.pre_count, 0) * g.pre_x * g.pre_y;
+  const int64_t n_dec = g.n_dec;
+  // three workgroups in four start on the prefill queue, the fourth on the
+  // decode queue (of the splits tried, 1:1 and 1:3 were slower, and all on
+  // prefill first gave no overlap); a workgroup whose queue is empty moves
+  // to the other one, and stops when both are
+  int role = (blockIdx.x & 3) == 3 ? 1 : 0;
+  bool switched = false;
+  while (true) {
+    __syncthreads();                       // the previous item's LDS use is over
+    if (threadIdx.x == 0) s_item = atomicAdd(&g.queues[role], 1);
+    __syncthreads();
+    const int64_t item = s_item;
+    if (item >= (role == 0 ? n_pre : n_dec)) {
+      if (switched) break;
+      switched = true;
+      role ^= 1;
+      continue;
+    }
+    if (role == 0) {
+      // the last query tiles of a chunk see the most keys: they go first
+      const int bx = g.pre_x - 1 - (int)(item % g.pre_x);
+      const int64_t t = item / g.pre_x;
+      const int by = (int)(t % g.pre_y);
+      const int li = (int)(t / g.pre_y);
+      pf::prefill_block<BS>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
+    } else {
+      const int bx = (int)(item % g.dec_x);
+      const int64_t t = item / g.dec_x;
+      const int zi = (int)(t % g.dec_y);
+      const int bz = (int)(t / g.dec_y);
+      dec::decode_block<BS, false>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
+                             int block_size, hipStream_t stream) {
+  if (g.workgroups <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)g.workgroups);
+  switch (block_size) {
+    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -99,9 +99,27 @@ hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, dim3 grid
                                     hipStream_t stream);
 
 // Permutation of 0..num_seqs-1 ordering sequences longest first (one
-// workgroup; seq_lens clamped to max_len).
+// workgroup; seq_lens clamped to max_len).  With cu_seqlens_q, also the list
+// of sequences with more than one query row (any order) and its length.
 hipError_t launch_seq_order(const int32_t* seq_lens, int32_t num_seqs, int32_t max_len,
-                            int32_t* order, hipStream_t stream);
+                            int32_t* order, const int32_t* cu_seqlens_q, int32_t num_tokens,
+                            int32_t* multi_list, int32_t* multi_count, int32_t* queues,
+                            hipStream_t stream);
+
+// One launch for a mixed varlen batch: prefill tiles (args `pre`, mode
+// kModeVarlenRows) over the listed multi-row sequences, and decode rows
+// (args `dcd`, mode kModeVarlenOne, grouped bfloat16 decode), interleaved.
+struct MixedGrid {
+  int64_t n_dec;                   // decode items: dec_x * dec_y * dec_z
+  int32_t pre_x, pre_y;            // prefill items per listed sequence: query tiles x head groups
+  int32_t dec_x, dec_y, dec_z;     // kv-head chunks, row items, key ranges
+  int32_t workgroups;              // persistent grid size
+  const int32_t* pre_list;         // [num_seqs] multi-row sequences (planner)
+  const int32_t* pre_count;        // [1] how many
+  int32_t* queues;                 // [2] item counters (prefill, decode), zeroed by the planner
+};
+hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
+                             int block_size, hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,

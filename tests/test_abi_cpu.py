@@ -68,12 +68,13 @@ def test_partition_choice_and_workspace(L):
     assert pagedkv.choose_partition_size(64, 32, 32, 4096, 0) == 512
     assert pagedkv.choose_partition_size(64, 32, 32, 300, 0) == 0
     # split buffer: [num_splits, num_heads, num_seqs, head_size] + lse [num_splits, num_heads,
-    # num_seqs] fp32, then the sequence order int32 [num_seqs], each part 16-byte aligned
+    # num_seqs] fp32, then int32 planner lists: the sequence order [num_seqs], the multi-row
+    # sequences [num_seqs], their count and two work counters; each part 16-byte aligned
     ns = 131072 // 512
     a16 = lambda n: (n + 15) // 16 * 16
     assert pagedkv.workspace_bytes(8, 64, 8, 128, 131072, 512) == \
-        a16(ns * 64 * 8 * (128 + 1) * 4) + a16(8 * 4)
-    assert pagedkv.workspace_bytes(3, 5, 1, 64, 1000, 256) == a16(4 * 5 * 3 * 65 * 4) + a16(3 * 4)
+        a16(ns * 64 * 8 * (128 + 1) * 4) + a16((2 * 8 + 3) * 4)
+    assert pagedkv.workspace_bytes(3, 5, 1, 64, 1000, 256) == a16(4 * 5 * 3 * 65 * 4) + a16((2 * 3 + 3) * 4)
     assert pagedkv.workspace_bytes(8, 64, 8, 128, 131072, -1) == 0
     assert pagedkv.workspace_bytes(8, 64, 8, 128, 500, 512) == 0
     with pytest.raises(pagedkv.PagedKVError):
