@@ -246,6 +246,55 @@ pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks
 pkv_status pkv_timing_enable(int32_t every_n);
 int32_t pkv_timing_read(float* ms, int32_t cap);
 
+/*
+ * Host KV block pool: the step before the attention calls, which hands out
+ * the cache's physical blocks to requests and produces their block tables
+ * and slot mappings (vLLM book, ch. 4.1 and 4.4; «Khám phá vLLM»,
+ * "Scheduler", allocate_slots).  Host memory only; thread safe per pool.
+ *   - Block 0 is the null block: never handed out, used to pad block tables.
+ *   - A request of n tokens owns ceil(n / block_size) blocks.  Free blocks
+ *     are reused last-freed first when they hold no prefix-cache entry, and
+ *     least recently used first when they do.
+ *   - With prefix caching, full blocks entered with pkv_pool_cache_full_blocks
+ *     are found again by later requests with the same leading tokens
+ *     (hash chained over the block's token ids; at most num_tokens - 1 tokens
+ *     of a new request come from the cache).
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* num_blocks >= 2 (the pool size of the cache), block_size > 0.  NULL on bad
+ * arguments or out of memory. */
+pkv_block_pool* pkv_pool_create(int64_t num_blocks, int32_t block_size, int32_t prefix_caching);
+void pkv_pool_destroy(pkv_block_pool* pool);
+/* Free blocks (the null block excluded). */
+int64_t pkv_pool_num_free(pkv_block_pool* pool);
+/* Make request `req` own blocks for num_tokens tokens (growing it if it
+ * exists).  token_ids (host int32 [num_tokens], may be NULL) lets a new
+ * request reuse cached full blocks.  Returns the number of leading tokens
+ * found in the cache (0 for an existing request), -1 when the pool cannot
+ * provide every block needed (nothing changes), -2 on bad arguments. */
+int64_t pkv_pool_allocate(pkv_block_pool* pool, int64_t req, int64_t num_tokens,
+                          const int32_t* token_ids);
+/* Enter the request's full blocks among its first num_tokens tokens (host
+ * int32 token_ids) into the prefix cache. */
+pkv_status pkv_pool_cache_full_blocks(pkv_block_pool* pool, int64_t req, const int32_t* token_ids,
+                                      int64_t num_tokens);
+/* Release a request's blocks. */
+pkv_status pkv_pool_free(pkv_block_pool* pool, int64_t req);
+/* Blocks the request owns, or -1 if unknown. */
+int64_t pkv_pool_num_blocks_of(pkv_block_pool* pool, int64_t req);
+/* Host int32 [n, max_blocks] block table of the listed requests, padded with
+ * the null block; PKV_ERR_SHAPE if a request is unknown or owns more blocks. */
+pkv_status pkv_pool_block_table(pkv_block_pool* pool, const int64_t* reqs, int32_t n,
+                                int32_t max_blocks, int32_t* out);
+/* Host int64 [count] slots (block * block_size + offset) of token positions
+ * first_pos .. first_pos + count - 1 of a request (inside its blocks). */
+pkv_status pkv_pool_slot_mapping(pkv_block_pool* pool, int64_t req, int64_t first_pos,
+                                 int64_t count, int64_t* out);
+/* The free queue, head first, written up to cap entries; returns its length
+ * (inspection and tests). */
+int64_t pkv_pool_free_queue(pkv_block_pool* pool, int32_t* out, int64_t cap);
+
 #ifdef __cplusplus
 }
 #endif

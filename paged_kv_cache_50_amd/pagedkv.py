@@ -63,6 +63,16 @@ _SIGS = {
                                      _i32, ctypes.c_char_p, _sz]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_read": (_i32, [ctypes.POINTER(ctypes.c_float), _i32]),
+    "pkv_pool_create": (_vp, [_i64, _i32, _i32]),
+    "pkv_pool_destroy": (None, [_vp]),
+    "pkv_pool_num_free": (_i64, [_vp]),
+    "pkv_pool_allocate": (_i64, [_vp, _i64, _i64, _vp]),
+    "pkv_pool_cache_full_blocks": (_i32, [_vp, _i64, _vp, _i64]),
+    "pkv_pool_free": (_i32, [_vp, _i64]),
+    "pkv_pool_num_blocks_of": (_i64, [_vp, _i64]),
+    "pkv_pool_block_table": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "pkv_pool_slot_mapping": (_i32, [_vp, _i64, _i64, _i64, _vp]),
+    "pkv_pool_free_queue": (_i64, [_vp, _vp, _i64]),
 }
 
 
@@ -308,3 +318,83 @@ def timing_read(cap: int = 4096):
 
 def default_scale(head_size: int) -> float:
     return 1.0 / math.sqrt(head_size)
+
+
+# ------------------------------------------------------------------ block pool
+
+class BlockPool:
+    """Host KV block pool of the library (pkv_pool_*): allocation of cache
+    blocks to requests, prefix caching, block tables and slot mappings."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = True):
+        self._p = lib().pkv_pool_create(int(num_blocks), int(block_size), 1 if prefix_caching else 0)
+        if not self._p:
+            raise PagedKVError(2, "pool_create")
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._p:
+            lib().pkv_pool_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(token_ids):
+        import numpy as np
+        if token_ids is None:
+            return None, None
+        a = np.ascontiguousarray(token_ids, dtype=np.int32)
+        return a, a.ctypes.data
+
+    def num_free(self) -> int:
+        return int(lib().pkv_pool_num_free(self._p))
+
+    def allocate(self, req: int, num_tokens: int, token_ids=None) -> int:
+        """Cached leading tokens (>= 0) or -1 when the pool is short of blocks."""
+        keep, ptr = self._ids(token_ids)
+        if keep is not None and len(keep) < num_tokens:
+            raise ValueError("token_ids shorter than num_tokens")
+        r = int(lib().pkv_pool_allocate(self._p, int(req), int(num_tokens), ptr))
+        if r == -2:
+            raise PagedKVError(2, "pool_allocate")
+        return r
+
+    def cache_full_blocks(self, req: int, token_ids, num_tokens: int) -> None:
+        keep, ptr = self._ids(token_ids)
+        if len(keep) < num_tokens:
+            raise ValueError("token_ids shorter than num_tokens")
+        _check(lib().pkv_pool_cache_full_blocks(self._p, int(req), ptr, int(num_tokens)),
+               "pool_cache_full_blocks")
+
+    def free(self, req: int) -> None:
+        _check(lib().pkv_pool_free(self._p, int(req)), "pool_free")
+
+    def num_blocks_of(self, req: int) -> int:
+        return int(lib().pkv_pool_num_blocks_of(self._p, int(req)))
+
+    def block_table(self, reqs, max_blocks: int):
+        import numpy as np
+        r = np.ascontiguousarray(reqs, dtype=np.int64)
+        out = np.empty((len(r), int(max_blocks)), dtype=np.int32)
+        _check(lib().pkv_pool_block_table(self._p, r.ctypes.data, len(r), int(max_blocks),
+                                          out.ctypes.data), "pool_block_table")
+        return out
+
+    def slot_mapping(self, req: int, first_pos: int, count: int):
+        import numpy as np
+        out = np.empty(int(count), dtype=np.int64)
+        _check(lib().pkv_pool_slot_mapping(self._p, int(req), int(first_pos), int(count),
+                                           out.ctypes.data if count else None), "pool_slot_mapping")
+        return out
+
+    def free_queue(self):
+        import numpy as np
+        n = int(lib().pkv_pool_free_queue(self._p, None, 0))
+        out = np.empty(n, dtype=np.int32)
+        lib().pkv_pool_free_queue(self._p, out.ctypes.data, n)
+        return out
