@@ -23,7 +23,12 @@ Sources (the vLLM pages):
   * causal alignment: query index i of a chunk of q_len rows sits at absolute
     position i + seq_len - q_len: ch. 6, "Branche de masque";
   * partial results of a split key range are merged: ch. 6, "forward()"
-    (merge_attn_states) and "build() étape par étape" (the split buffer).
+    (merge_attn_states) and "build() étape par étape" (the split buffer);
+  * sliding window: a causal window (w, 0) becomes (w, w) when the
+    attention is not causal: ch. 6, "forward()" (the window symmetrisation);
+    the cache still holds every token, only the computation is windowed
+    (ch. 2, "Le système de spécifications du KV Cache": conservative
+    allocation, exact computation).
 
 Readings where the pages are silent (each is pinned by a test):
   * slot = physical_block * block_size + offset;
@@ -120,10 +125,13 @@ def attention_seq_kvhead(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray
                          kv_head: int, num_heads: int, scale: float, block_size: int,
                          dtype: str, causal: bool,
                          key_range: Optional[Tuple[int, int]] = None,
-                         k_scale=None, v_scale=None):
+                         k_scale=None, v_scale=None, window_left: int = -1):
     """Attention of query rows row0..row1-1 of one sequence for the query
     heads of one kv head.  key_range=(a, b) restricts the keys to logical
-    positions a..b-1 (used to express a split).  dtype is the cache's; with
+    positions a..b-1 (used to express a split).  window_left >= 0 is a
+    sliding window: a row at position p sees keys p - w .. p when causal and
+    p - w .. p + w otherwise (the causal window made symmetric).  dtype is
+    the cache's; with
     an fp8 cache the queries are bfloat16 and cached values are
     decode(code) * k_scale[kv_head] (v_scale for V).  Returns out
     [q_len, g, D] and lse [q_len, g] in float64."""
@@ -143,9 +151,13 @@ def attention_seq_kvhead(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray
     S = S.reshape(q_len, g, L)
     j = np.arange(L)
     allowed = np.ones((q_len, L), dtype=bool)
+    qpos = np.arange(q_len) + L - q_len              # absolute position of each query row
     if causal:
-        qpos = np.arange(q_len) + L - q_len          # absolute position of each query row
         allowed &= j[None, :] <= qpos[:, None]
+    if window_left is not None and window_left >= 0:
+        allowed &= j[None, :] >= qpos[:, None] - window_left
+        if not causal:
+            allowed &= j[None, :] <= qpos[:, None] + window_left
     if key_range is not None:
         allowed &= (j >= key_range[0]) & (j < key_range[1])
     S = np.where(allowed[:, None, :], S, -np.inf)
@@ -158,7 +170,7 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                     block_size: int, dtype: str, cu_seqlens_q: Optional[np.ndarray] = None,
                     causal: bool = False,
                     pairs: Optional[Sequence[Tuple[int, int]]] = None,
-                    k_scale=None, v_scale=None):
+                    k_scale=None, v_scale=None, window_left: int = -1):
     """Attention over a paged KV cache, as defined above.
 
     q: [num_rows, num_heads, D]; decode when cu_seqlens_q is None (row s is
@@ -183,7 +195,7 @@ def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             continue
         o, l = attention_seq_kvhead(q, k_cache, v_cache, block_tables[s], int(seq_lens[s]),
                                     r0, r1, kvh, num_heads, scale, block_size, dtype, causal,
-                                    k_scale=k_scale, v_scale=v_scale)
+                                    k_scale=k_scale, v_scale=v_scale, window_left=window_left)
         out[r0:r1, kvh * g:(kvh + 1) * g] = o
         lse[r0:r1, kvh * g:(kvh + 1) * g] = l
     return out, lse

@@ -16,15 +16,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
 
 # ---------------------------------------------------------------- helpers
 
-def brute_attention(Q, K, V, scale, causal):
+def brute_attention(Q, K, V, scale, causal, window=-1):
     """Pure-Python attention on contiguous K/V (no pool, no numpy math).
-    Q: list[q_len][D], K/V: list[L][D].  Row i sees keys j <= i + L - q_len
-    when causal."""
+    Q: list[q_len][D], K/V: list[L][D].  Row i sits at position
+    p = i + L - q_len and sees keys j <= p when causal; with a window w >= 0
+    also j >= p - w, and j <= p + w when not causal."""
     q_len, L = len(Q), len(K)
     outs, lses = [], []
     for i in range(q_len):
-        lim = i + L - q_len if causal else L - 1
-        keys = [j for j in range(L) if j <= lim]
+        pos = i + L - q_len
+        lim = pos if causal else L - 1
+        if window >= 0 and not causal:
+            lim = min(lim, pos + window)
+        low = pos - window if window >= 0 else 0
+        keys = [j for j in range(L) if low <= j <= lim]
         if not keys:
             outs.append([0.0] * len(V[0]) if V else [])
             lses.append(-math.inf)
@@ -110,6 +115,48 @@ def test_oracle_matches_bruteforce(bs, causal):
             bo, bl = brute_attention(Q, K, V, scale, causal)
             np.testing.assert_allclose(out[cu[s]:cu[s + 1], h], np.array(bo), rtol=0, atol=1e-12)
             np.testing.assert_allclose(lse[cu[s]:cu[s + 1], h], np.array(bl), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bs", [4, 16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [0, 3, 10, 100])
+def test_oracle_window_matches_bruteforce(bs, causal, window):
+    rng = np.random.default_rng(300 + bs + 7 * causal + window)
+    Hq, Hkv, D = 4, 2, 8
+    seq_lens = [1, 5, 17, 40]
+    qlens = [1, 3, 17, 6] if causal else [1, 2, 1, 9]
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, seq_lens, Hkv, D, bs)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), Hq, D)).astype(np.float32)
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.37, bs, "f32",
+                                      cu_seqlens_q=cu, causal=causal, window_left=window)
+    for s, L in enumerate(seq_lens):
+        for h in range(Hq):
+            Q = [list(map(float, q[r, h])) for r in range(cu[s], cu[s + 1])]
+            K = [list(map(float, Kseq[s][j, h // 2])) for j in range(L)]
+            V = [list(map(float, Vseq[s][j, h // 2])) for j in range(L)]
+            bo, bl = brute_attention(Q, K, V, 0.37, causal, window)
+            np.testing.assert_allclose(out[cu[s]:cu[s + 1], h], np.array(bo), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[cu[s]:cu[s + 1], h], np.array(bl), rtol=0, atol=1e-12)
+
+
+def test_oracle_window_closed_forms():
+    rng = np.random.default_rng(9)
+    seq_lens = [7, 33, 64]
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, seq_lens, 2, 8, 8)
+    q = rng.standard_normal((3, 4, 8)).astype(np.float32)
+    L = np.array(seq_lens)
+    full, full_lse = oracle.paged_attention(q, Kc, Vc, bt, L, 0.5, 8, "f32")
+    # a window reaching the first key is no window at all
+    wide, wide_lse = oracle.paged_attention(q, Kc, Vc, bt, L, 0.5, 8, "f32", window_left=63)
+    assert np.array_equal(full, wide) and np.array_equal(full_lse, wide_lse)
+    # window 0: each row sees its own key only -> its value exactly, lse = its logit
+    one, one_lse = oracle.paged_attention(q, Kc, Vc, bt, L, 0.5, 8, "f32", window_left=0)
+    for s, n in enumerate(seq_lens):
+        for h in range(4):
+            assert np.array_equal(one[s, h], Vseq[s][n - 1, h // 2].astype(np.float64))
+            k = Kseq[s][n - 1, h // 2].astype(np.float64)
+            assert abs(one_lse[s, h] - 0.5 * float(q[s, h].astype(np.float64) @ k)) < 1e-12
 
 
 def test_bruteforce_hand_example():
