@@ -164,6 +164,10 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
  *   seq_lens      device int32 [num_seqs]
  *   max_seq_len   host upper bound of seq_lens (sizes the launch and the split)
  *   scale         logit scale (usually 1/sqrt(head_size))
+ *   window_left   sliding window (vLLM book, ch. 6 "forward()": the window
+ *                 symmetrisation): the row at position p = seq_len - 1 sees
+ *                 keys p - window_left .. p; -1 = no window.  Blocks wholly
+ *                 outside the window are never read.
  *   partition_size see pkv_choose_partition_size
  *   lse_out       optional device float32 [num_seqs, num_heads]
  *   workspace     device, >= pkv_attention_workspace_bytes(...) bytes, 16-byte
@@ -173,9 +177,9 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
 pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cache* cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                      int32_t max_seq_len, float scale, int32_t partition_size,
-                                      float* lse_out, void* workspace, size_t workspace_bytes,
-                                      void* stream);
+                                      int32_t max_seq_len, float scale, int32_t window_left,
+                                      int32_t partition_size, float* lse_out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /*
  * Variable-length attention over a flattened batch (ch. 6 "Structure des
@@ -190,6 +194,10 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
  *   cu_seqlens_q  device int32 [num_seqs + 1], non-decreasing, from 0
  *   seq_lens      device int32 [num_seqs]
  *   max_query_len host upper bound of the query lengths
+ *   window_left   sliding window, -1 = none: a row at absolute position p sees
+ *                 keys p - window_left .. p when causal, and
+ *                 p - window_left .. p + window_left when not (the causal
+ *                 window (w, 0) made symmetric, ch. 6 "forward()")
  *   lse_out       optional device float32 [num_tokens, num_heads]
  */
 pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cache* cache,
@@ -197,8 +205,9 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                                       int32_t max_query_len, int32_t max_seq_len, float scale,
-                                      int32_t causal, int32_t partition_size, float* lse_out,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      int32_t causal, int32_t window_left, int32_t partition_size,
+                                      float* lse_out, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * Capability check in the spirit of supports_combination (ch. 6 "Matrice de

@@ -270,6 +270,7 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.mode = pkv::kModeDecode;
   a.causal = 0;
   a.skip_multi_row = 0;
+  a.window_left = -1;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.k_scale = cache->k_scale;
   a.v_scale = cache->v_scale;
@@ -360,11 +361,12 @@ pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const 
 pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cache* cache,
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
-                                      int32_t max_seq_len, float scale, int32_t partition_size,
-                                      float* lse_out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      int32_t max_seq_len, float scale, int32_t window_left,
+                                      int32_t partition_size, float* lse_out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   pkv_status st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
+  if (window_left < -1) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
@@ -388,6 +390,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                          num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
   a.mode = pkv::kModeDecode;
+  a.window_left = window_left;
   st = plan_seq_order(a, cache, workspace, s);
   if (st != PKV_OK) return st;
   int tslot = 0;
@@ -404,10 +407,12 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
                                       int32_t max_query_len, int32_t max_seq_len, float scale,
-                                      int32_t causal, int32_t partition_size, float* lse_out,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+                                      int32_t causal, int32_t window_left, int32_t partition_size,
+                                      float* lse_out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   pkv_status st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
+  if (window_left < -1) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
       max_query_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
@@ -435,6 +440,7 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                          num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, P,
                          ns, lse_out, workspace);
   a.cu_seqlens_q = cu_seqlens_q;
+  a.window_left = window_left;
   a.causal = causal ? 1 : 0;
   const int group = num_heads / cache->num_kv_heads;
   const int gt = heads_per_chunk(group);

@@ -12,7 +12,9 @@ namespace pkv {
 struct Item {
   int seq;
   int row;       // query row in q / out
-  int L_end;     // keys 0 .. L_end-1 are visible to this row
+  int L_begin;   // keys L_begin .. L_end-1 are visible to this row
+  int L_end;
+  int base;      // L_begin rounded down to 32: partition p covers base + [pP, (p+1)P)
   int nparts;    // partitions the row's key range is split into
   int nranges;   // workgroup ranges of parts_per_wg partitions (one partial each)
   int P;         // partition size in tokens
@@ -50,18 +52,28 @@ __device__ __forceinline__ bool resolve_item(const AttnArgs& a, int z, Item& it)
     if (qidx >= a.max_query_len) return false;         // beyond the host bound: not computed
   }
   int L = clamp_seq_len(a.seq_lens[seq], a.max_seq_len, a.max_blocks_per_seq, a.block_size);
+  // absolute position of the row: L - 1 for one-row sequences
+  const int pos = qidx + L - qlen;
   int L_end = L;
-  if (a.causal && a.mode == kModeVarlenRows) L_end = min(L, max(0, qidx + L - qlen + 1));
+  if (a.causal && a.mode == kModeVarlenRows) L_end = min(L, max(0, pos + 1));
+  int L_begin = 0;
+  if (a.window_left >= 0) {
+    // sliding window: keys pos - w .. pos (causal); pos - w .. pos + w otherwise
+    L_begin = min(max(0, pos - a.window_left), L_end);
+    if (!(a.causal || a.mode != kModeVarlenRows)) L_end = min(L_end, max(0, pos + a.window_left + 1));
+  }
   it.seq = seq;
   it.row = row;
+  it.L_begin = L_begin;
   it.L_end = L_end;
+  it.base = L_begin & ~31;
   if (a.partition_size > 0 && a.mode != kModeVarlenRows) {
     it.P = a.partition_size;
-    it.nparts = max(1, (L_end + it.P - 1) / it.P);
+    it.nparts = max(1, (L_end - it.base + it.P - 1) / it.P);
     // partials are kept per workgroup range of parts_per_wg partitions
     it.nranges = (it.nparts + a.parts_per_wg - 1) / a.parts_per_wg;
   } else {
-    it.P = max(L_end, 1);
+    it.P = max(L_end - it.base, 1);
     it.nparts = 1;
     it.nranges = 1;
   }

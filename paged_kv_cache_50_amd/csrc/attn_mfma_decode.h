@@ -117,8 +117,9 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int h0 = kvh * group + chunk * 16;
   const int G = min(16, group - chunk * 16);
 
-  const int pstart = part_first * it.P;
-  const int pend = min(part_end * it.P, it.L_end);
+  const int pstart = it.base + part_first * it.P;
+  const int pend = min(it.base + part_end * it.P, it.L_end);
+  const int pbegin = it.L_begin;                 // first visible key (sliding window)
 
   // Q^T B operands: lane (kg, n) holds q[h0+n][(4j+kg)*8 .. +8] for k-step j.
   bf16x8_t qb[4];
@@ -186,12 +187,12 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   // Stage a tile in LDS (V rows of tokens past the end become zeros).
   auto stage = [&](int tile, const u32x4* K, const u32x4* V) {
     const int tbase = pstart + tile * kTile;
-    const bool full = tbase + kTile <= pend;
+    const bool full = tbase + kTile <= pend && tbase >= pbegin;
     __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int tok = kRowsPerLoad * i + lrow;
-      const bool dead = !full && tbase + tok >= pend;
+      const bool dead = !full && (tbase + tok >= pend || tbase + tok < pbegin);
       if constexpr (FP8) {
         // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
         const int c = lane & 7;
@@ -216,7 +217,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   // One staged tile of the online softmax: logits, running max/sum, PV.
   auto compute = [&](int tile) {
     const int tbase = pstart + tile * kTile;
-    const bool full = tbase + kTile <= pend;
+    const bool full = tbase + kTile <= pend && tbase >= pbegin;
 
     // logits S^T: A operand = K rows (token tt*16 + n, chunk 4j + kg)
     f32x4 sacc[2];
@@ -236,7 +237,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tbase + tt * 16 + 4 * kg + i;
-        s[tt * 4 + i] = (full || tok < pend) ? sacc[tt][i] * logit_scale : -INFINITY;
+        s[tt * 4 + i] = (full || (tok < pend && tok >= pbegin)) ? sacc[tt][i] * logit_scale : -INFINITY;
       }
     float mx = s[0];
 #pragma unroll

@@ -114,8 +114,14 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 
   // key range of the workgroup
   const int q_last = min(q0 + 16 * R, q_len) - 1;
-  const int kv_end = a.causal ? max(0, min(L, q_last + off + 1)) : L;
-  const int ntiles = (kv_end + kTile - 1) / kTile;
+  // sliding window w: row at position p sees keys p - w .. p (causal) or
+  // p - w .. p + w (not causal)
+  const int win = a.window_left;
+  int kv_end = a.causal ? max(0, min(L, q_last + off + 1)) : L;
+  if (win >= 0 && !a.causal) kv_end = max(0, min(kv_end, q_last + off + win + 1));
+  const int kv_begin = win >= 0 ? min(max(0, q0 + off - win), kv_end) : 0;
+  const int ntiles = (kv_end + kTile - 1) / kTile;   // tiles t_begin .. ntiles - 1
+  const int t_begin = kv_begin / kTile;
 
   // this wave's two column tiles: (row block, head)
   int rowb[2], head[2];
@@ -129,7 +135,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     live[c] = rowb[c] < q_len;
     if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
   }
-  if (!a.causal) wave_last_pos = L - 1;
+  if (!a.causal) wave_last_pos = win >= 0 ? min(L - 1, wave_last_pos + win) : L - 1;
+  // smallest key position this wave may see (sliding window)
+  const int wave_first_key = win >= 0 ? min(rowb[0], rowb[1]) + off - win : 0;
 
   // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
   bf16x8_t qb[2][4];
@@ -207,7 +215,8 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   auto compute = [&](int t, const char* buf, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = t * kTile;
-    if (MASKED && j0 > wave_last_pos) return;        // wholly above this wave's diagonal
+    // wholly above this wave's diagonal, or below its window
+    if (MASKED && (j0 > wave_last_pos || j0 + kTile - 1 < wave_first_key)) return;
     const char* kl = buf;
     const char* vl = buf + kKBytes;
     f32x4 sacc[2][2];
@@ -228,7 +237,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qpos = rowb[c] + n + off;            // this lane's column = query row
-      const int lim = a.causal ? min(qpos, kv_end - 1) : kv_end - 1;
+      const int lim = a.causal ? min(qpos, kv_end - 1)
+                                : (win >= 0 ? min(qpos + win, kv_end - 1) : kv_end - 1);
+      const int lo = win >= 0 ? qpos - win : 0;
       // raw logits; the scale is applied inside the exponent (one FMA)
       float s[8];
 #pragma unroll
@@ -236,7 +247,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + tt * 16 + 4 * kg + i;
-          s[tt * 4 + i] = (!MASKED || j <= lim) ? sacc[c][tt][i] : -INFINITY;
+          s[tt * 4 + i] = (!MASKED || (j <= lim && j >= lo)) ? sacc[c][tt][i] : -INFINITY;
         }
       float mx = vmax(vmax(vmax(s[0], s[1]), vmax(s[2], s[3])), vmax(vmax(s[4], s[5]), vmax(s[6], s[7])));
       mx = xmax16_32(mx) * a.scale_log2;             // scale > 0 preserves the max
@@ -286,12 +297,12 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   constexpr int kLoadsPerTile = 4;
   int64_t ids[2];
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
+  for (int t = t_begin; t < t_begin + kStages - 1; ++t)
     if (t < ntiles) {
       fetch_ids(t, ids);
-      issue(t, ids, s_lds + t * kStageBytes);
+      issue(t, ids, s_lds + (t % kStages) * kStageBytes);
     }
-  if (kStages - 1 < ntiles) fetch_ids(kStages - 1, ids);
+  if (t_begin + kStages - 1 < ntiles) fetch_ids(t_begin + kStages - 1, ids);
   auto step = [&](int t, auto masked_tag) {
     const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
     if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
@@ -314,9 +325,14 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // the key range need no mask for any wave; the rest (the diagonal band and
   // the range end) take the masked path.  Every wave runs both loops over
   // the same tiles, so the barriers stay matched.
-  const int unmasked_end = a.causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
-  const int tm = min(ntiles, max(0, (unmasked_end + 1) / kTile));
-  for (int t = 0; t < tm; ++t) step(t, std::false_type{});
+  // With a window, tiles below the last row's window start are masked too.
+  int unmasked_end = a.causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
+  if (win >= 0 && !a.causal) unmasked_end = min(unmasked_end, q0 + off + win);
+  const int unmasked_begin = win >= 0 ? max(0, q_last + off - win) : 0;
+  const int tu = min(ntiles, max(t_begin, (unmasked_begin + kTile - 1) / kTile));
+  const int tm = min(ntiles, max(tu, (unmasked_end + 1) / kTile));
+  for (int t = t_begin; t < tu; ++t) step(t, std::true_type{});
+  for (int t = tu; t < tm; ++t) step(t, std::false_type{});
   for (int t = tm; t < ntiles; ++t) step(t, std::true_type{});
 
   // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]

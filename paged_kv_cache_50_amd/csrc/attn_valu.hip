@@ -126,8 +126,9 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   const int kvh = blockIdx.x / a.head_chunks;
   const int h0 = kvh * group + (blockIdx.x % a.head_chunks) * GT;
 
-  const int pstart = part * it.P;
+  const int pstart = it.base + part * it.P;
   const int pend = min(pstart + it.P, it.L_end);
+  const int pbegin = it.L_begin;                 // first visible key (sliding window)
 
   // query fragments of the chunk's heads
   u32x4 qf[GT];
@@ -183,7 +184,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
     float s[kNls][GT];
 #pragma unroll
     for (int i = 0; i < kNls; ++i) {
-      const bool valid = tbase + i * RPW < pend;
+      const bool valid = tbase + i * RPW < pend && tbase + i * RPW >= pbegin;
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         float d = group_sum<LPR>(frag_dot<T>(K[i], qf[h]));
@@ -193,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
     float vf[kNls][EPL];
 #pragma unroll
     for (int i = 0; i < kNls; ++i) {
-      const bool valid = tbase + i * RPW < pend;
+      const bool valid = tbase + i * RPW < pend && tbase + i * RPW >= pbegin;
       frag_widen<T>(V[i], vf[i]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) vf[i][e] = valid ? vf[i][e] : 0.f;

@@ -48,6 +48,8 @@ struct AttnArgs {
   int32_t range_desc;              // 1: grid.z runs over key ranges from the last one down
   int32_t mode;                    // AttnMode
   int32_t causal;
+  int32_t window_left;             // sliding window (keys >= pos - window_left; symmetric
+                                   // when not causal), -1 = none
   int32_t skip_multi_row;          // kModeVarlenRows: 1 if another kernel owns multi-row seqs
   float scale_log2;                // scale * log2(e)
   const float* k_scale;            // fp8 caches: per-kv-head scales (value = code * scale)

@@ -53,9 +53,9 @@ _SIGS = {
     "pkv_choose_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _i32, _vp,
-                                          _i32, _i32, _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
+                                          _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attention_varlen": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp,
-                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
                                           _vp, _vp, _sz, _vp]),
     "pkv_unsupported_reason": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -222,9 +222,10 @@ def _meta(t, name):
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                            max_seq_len: int, partition_size: int = 0, workspace=None,
-                           lse_out=None, k_scale=None, v_scale=None):
+                           lse_out=None, k_scale=None, v_scale=None, window_left: int = -1):
     """Decode attention, one query row per sequence.  out/q: [S, Hq, D].
-    max_seq_len is a host-side upper bound of seq_lens (no device sync)."""
+    max_seq_len is a host-side upper bound of seq_lens (no device sync).
+    window_left >= 0: sliding window (keys seq_len - 1 - window_left ..)."""
     _require_gpu(out, q, block_tables, seq_lens, workspace, lse_out)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     _meta(block_tables, "block_tables")
@@ -241,7 +242,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
     _check(lib().pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), ctypes.byref(desc), block_tables.data_ptr(),
         block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
-        int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
+        int(window_left), int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
         "paged_attention_decode")
     return out
 
@@ -249,8 +250,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
 def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
                            scale: float, max_query_len: int, max_seq_len: int, causal: bool = True,
                            partition_size: int = 0, workspace=None, lse_out=None,
-                           k_scale=None, v_scale=None):
-    """Variable-length attention over a flattened batch (q/out [T, Hq, D])."""
+                           k_scale=None, v_scale=None, window_left: int = -1):
+    """Variable-length attention over a flattened batch (q/out [T, Hq, D]).
+    window_left >= 0: sliding window (symmetric when not causal)."""
     _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
@@ -268,7 +270,7 @@ def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, blo
     _check(lib().pkv_paged_attention_varlen(
         out.data_ptr(), q.data_ptr(), ctypes.byref(desc), cu_seqlens_q.data_ptr(),
         seq_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], S, T, Hq,
-        int(max_query_len), int(max_seq_len), float(scale), 1 if causal else 0,
+        int(max_query_len), int(max_seq_len), float(scale), 1 if causal else 0, int(window_left),
         int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
         "paged_attention_varlen")
     return out

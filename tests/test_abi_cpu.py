@@ -92,9 +92,9 @@ def cache(k=A16, v=A16 + 4096, dtype=1, nb=100, bs=16, hkv=8, d=128, stride=0):
 
 
 def decode(L, c, out=A16, q=A16, bt=A16, sl=A16, S=4, Hq=32, max_len=1000, ps=0, ws=None, wsb=0,
-           mb=64):
+           mb=64, win=-1):
     return L.pkv_paged_attention_decode(out, q, ctypes.byref(c), bt, mb, sl, S, Hq, max_len, 0.1,
-                                        ps, None, ws, wsb, None)
+                                        win, ps, None, ws, wsb, None)
 
 
 def test_decode_error_codes(L):
@@ -111,6 +111,7 @@ def test_decode_error_codes(L):
     assert decode(L, cache(), mb=0) == 2
     assert decode(L, cache(stride=100)) == 2                     # stride smaller than a block
     assert decode(L, cache(), ps=100) == 2                       # partition not a multiple of 32
+    assert decode(L, cache(), win=-2) == 2                       # window below -1
     need = pagedkv.workspace_bytes(4, 32, 8, 128, 1000, 0)
     assert need > 0
     assert decode(L, cache(), ws=None, wsb=0) == 5               # split needs a workspace
@@ -122,11 +123,11 @@ def test_decode_error_codes(L):
 def test_varlen_and_write_error_codes(L):
     c = cache()
     f = L.pkv_paged_attention_varlen
-    assert f(A16, A16, ctypes.byref(c), None, A16, A16, 64, 4, 10, 32, 5, 1000, 0.1, 1, 0,
+    assert f(A16, A16, ctypes.byref(c), None, A16, A16, 64, 4, 10, 32, 5, 1000, 0.1, 1, -1, 0,
              None, None, 0, None) == 1                           # NULL cu_seqlens_q
-    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, -1, 1000, 0.1, 1, 0,
+    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, -1, 1000, 0.1, 1, -1, 0,
              None, None, 0, None) == 2                           # negative max_query_len
-    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 0, 32, 5, 1000, 0.1, 1, 0,
+    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 0, 32, 5, 1000, 0.1, 1, -1, 0,
              None, None, 0, None) == 0                           # no tokens: no-op
     w = L.pkv_kv_cache_write
     assert w(ctypes.byref(c), None, A16, A16, 10, None) == 1
