@@ -39,6 +39,7 @@ WORKLOAD_DESC = {
     5: "slot write + varlen: 4 causal chunks of 512 (context U[0,4096]) + 128 decode rows (U[64,4096]), 32/8 heads, head 128, block 32, bf16, seed 4",
     6: "workload 2 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
     7: "workload 3 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
+    8: "workload 4 (same lengths and pool) with a 4096-key sliding window (window_left 4095)",
 }
 
 
@@ -120,8 +121,10 @@ def cpu_baseline(w, budget_s: float = 12.0):
         s, h = pairs[i % len(pairs)]
         oracle.paged_attention(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size,
                                w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
-                               pairs=[(s, h)], k_scale=w.k_scale, v_scale=w.v_scale)
-        done_bytes += (int(w.seq_lens[s]) * 2 * w.head_size * e
+                               pairs=[(s, h)], k_scale=w.k_scale, v_scale=w.v_scale,
+                               window_left=w.window_left)
+        keys = int(w.seq_lens[s]) if w.window_left < 0 else min(int(w.seq_lens[s]), w.window_left + 1)
+        done_bytes += (keys * 2 * w.head_size * e
                        + 2 * int(ql[s]) * g * w.head_size * w.io_bytes)
         done_pairs += 1
         i += 1
@@ -140,7 +143,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -195,12 +198,13 @@ def main() -> int:
             pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                            dw.seq_lens, w.scale, w.max_seq_len,
                                            partition_size=ps, workspace=ws, k_scale=dw.k_scale,
-                                           v_scale=dw.v_scale)
+                                           v_scale=dw.v_scale, window_left=w.window_left)
         else:
             pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
                                            dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
                                            w.max_seq_len, causal=w.causal, partition_size=ps,
-                                           workspace=ws, k_scale=dw.k_scale, v_scale=dw.v_scale)
+                                           workspace=ws, k_scale=dw.k_scale, v_scale=dw.v_scale,
+                                           window_left=w.window_left)
 
     for _ in range(args.warmup):
         step()

@@ -73,6 +73,7 @@ int64_t block_stride_elems(const pkv_kv_cache* c) {
 // PKV_DECODE_KERNEL=valu|mfma forces one variant (for A/B measurements).
 constexpr int kMfmaMinGroup = 4;
 constexpr int kMfmaTokensPerWg = 2048;
+constexpr int64_t kMfmaTargetWgs = 2048;   // about four rounds of 512 workgroup slots
 
 bool use_mfma_decode(const pkv_kv_cache* c, int group) {
   if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
@@ -121,16 +122,24 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
   const int group = a.num_heads / cache->num_kv_heads;
   {
     a.head_chunks = (group + 15) / 16;
+    // Tokens one workgroup streams: about kMfmaTokensPerWg for large batches,
+    // fewer (down to 256) when the whole launch has too little work to give
+    // the 512 workgroup slots several rounds (few rows, or a short window).
+    const int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
+                                               : a.max_seq_len;
+    const int64_t work = (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks * eff_len;
+    int tpw = kMfmaTokensPerWg;
+    while (tpw > 256 && work / tpw < kMfmaTargetWgs) tpw >>= 1;
     // a workgroup streams about kMfmaTokensPerWg tokens: consecutive
     // partitions share its queries and block-table row, and its fixed cost
     // (queries, first loads, merge) is paid once per stream
     // Small partitions: a workgroup covers 4 of them, one per wave (merged in
     // LDS, then across workgroups by the split merge); larger ones: the waves
     // share the workgroup's partitions tile by tile.
-    a.wave_per_part = (a.partition_size > 0 && a.partition_size <= kMfmaTokensPerWg / 4) ? 1 : 0;
+    a.wave_per_part = (a.partition_size > 0 && a.partition_size <= tpw / 4) ? 1 : 0;
     a.parts_per_wg = a.partition_size <= 0 ? 1
                      : a.wave_per_part ? 4
-                     : std::max(1, kMfmaTokensPerWg / a.partition_size);
+                     : std::max(1, tpw / a.partition_size);
     // With the sequences ordered longest first, the last key ranges (which
     // only long sequences have) are dispatched first and the first ranges of
     // the shortest sequences last: close to longest-processing-time first.

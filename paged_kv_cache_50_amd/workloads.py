@@ -95,6 +95,7 @@ class Workload:
     sigma: float = 1.0
     k_scale: Optional[np.ndarray] = None        # fp8: float32 [num_kv_heads]
     v_scale: Optional[np.ndarray] = None
+    window_left: int = -1            # sliding window (keys pos - window_left .. pos), -1 none
 
     @property
     def num_seqs(self) -> int:
@@ -331,9 +332,10 @@ CONFIG_NAMES = {
     5: "mixed_chunked_prefill_decode_bf16",
     6: "llama7b_mha_decode_fp8",
     7: "gqa_decode_fp8",
+    8: "long_context_sliding_window_decode_bf16",
 }
 
-DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2}   # 6, 7: the lengths and pools of 2, 3
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3}   # 6, 7: the lengths and pools of 2, 3
 
 
 def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
@@ -360,7 +362,7 @@ def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=No
 def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
                 max_len: Optional[int] = None, num_chunks: Optional[int] = None,
                 chunk_len: Optional[int] = None) -> Workload:
-    """Build workload `cfg` (1..7).  num_seqs / max_len / num_chunks /
+    """Build workload `cfg` (1..8).  num_seqs / max_len / num_chunks /
     chunk_len shrink it for quick parity runs; None keeps the full size."""
     if seed is None:
         seed = DEFAULT_SEEDS[cfg]
@@ -393,6 +395,13 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         qlens = np.concatenate([np.full(nc, cl), np.ones(nd)]).astype(np.int64)
         return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16", seed, causal=True,
                            meta_rng=meta, root=root)
+    if cfg == 8:
+        # the shapes, lengths and pool of workload 4 with a 4096-key window
+        L = config_lengths(4, meta, num_seqs, max_len)
+        w = make_decode(name, L, 64, 8, 128, 16, "bf16", seed, sigma=0.5,
+                        partition_size=512, meta_rng=meta, root=root)
+        w.window_left = 4095
+        return w
     if cfg in (6, 7):
         # the MHA and GQA decode shapes of workloads 2 and 3 over an fp8 cache
         L = config_lengths(cfg - 4, meta, num_seqs, max_len)
@@ -411,9 +420,18 @@ def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
     and the slot_mapping read."""
     e = w.elem_bytes
     L = w.seq_lens.astype(np.int64)
-    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * e
+    if w.window_left >= 0 and w.cu_seqlens_q is None:
+        # a decode row reads only the keys of its window, and the table
+        # entries of the blocks they lie in
+        first = np.maximum(L - 1 - w.window_left, 0)
+        keys = L - first
+        blocks = (L + w.block_size - 1) // w.block_size - first // w.block_size
+    else:
+        keys = L
+        blocks = np.array([blocks_needed(x, w.block_size) for x in L], dtype=np.int64)
+    kv = int(keys.sum()) * 2 * w.num_kv_heads * w.head_size * e
     qo = 2 * w.num_q_rows * w.num_heads * w.head_size * w.io_bytes
-    meta = 4 * int(sum(blocks_needed(x, w.block_size) for x in L)) + 4 * w.num_seqs
+    meta = 4 * int(blocks.sum()) + 4 * w.num_seqs
     if w.cu_seqlens_q is not None:
         meta += 4 * (w.num_seqs + 1)
     if w.k_scale is not None:

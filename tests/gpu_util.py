@@ -81,13 +81,13 @@ def run(dw: DevWorkload, partition_size=None, lse=True, write=True):
         pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                        dw.seq_lens, w.scale, w.max_seq_len, partition_size=ps,
                                        lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
-                                       v_scale=dw.v_scale)
+                                       v_scale=dw.v_scale, window_left=w.window_left)
     else:
         pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
                                        dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
                                        w.max_seq_len, causal=w.causal, partition_size=ps,
                                        lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
-                                       v_scale=dw.v_scale)
+                                       v_scale=dw.v_scale, window_left=w.window_left)
     return dw.out
 
 
@@ -111,7 +111,8 @@ def reference(w: W.Workload, pairs=None):
     kc, vc = oracle_inputs(w)
     return oracle.paged_attention(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size,
                                   w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
-                                  pairs=pairs, k_scale=w.k_scale, v_scale=w.v_scale)
+                                  pairs=pairs, k_scale=w.k_scale, v_scale=w.v_scale,
+                                  window_left=w.window_left)
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
