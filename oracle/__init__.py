@@ -9,3 +9,4 @@ from .attention import (widen, kv_cache_write, gather_kv, attention_seq_kvhead, 
                         blocks_for_tokens)
 from .fp8 import (E4M3_MAX, e4m3_decode, e4m3_encode, quantize,  # noqa: F401
                   kv_cache_write_fp8)
+from .cascade import cascade_attention, check_cascade_metadata, cascade_traffic_bytes  # noqa: F401

@@ -96,6 +96,14 @@ class Workload:
     k_scale: Optional[np.ndarray] = None        # fp8: float32 [num_kv_heads]
     v_scale: Optional[np.ndarray] = None
     window_left: int = -1            # sliding window (keys pos - window_left .. pos), -1 none
+    common_prefix_len: int = 0       # tokens of a prefix shared by every non-empty sequence
+                                     # (its blocks start every table)
+
+    @property
+    def prefix_blocks(self) -> np.ndarray:
+        """int32 [common_prefix_len / block_size]: the shared prefix's blocks."""
+        owner = int(np.argmax(self.seq_lens > 0)) if self.seq_lens.size else 0
+        return self.block_tables[owner, :self.common_prefix_len // self.block_size].copy()
 
     @property
     def num_seqs(self) -> int:
@@ -198,11 +206,15 @@ def blocks_needed(seq_len: int, block_size: int) -> int:
 
 
 def build_pool(seq_lens, block_size: int, rng: np.random.Generator,
-               num_blocks: Optional[int] = None, extra_frac: float = 0.10):
-    """Shuffle physical block ids 1..num_blocks-1 and hand them out to the
-    sequences in order.  Returns (num_blocks, block_tables int32)."""
+               num_blocks: Optional[int] = None, extra_frac: float = 0.10,
+               shared_blocks: int = 0):
+    """Shuffle physical block ids 1..num_blocks-1 and hand them out in order:
+    first `shared_blocks` blocks that start every sequence's table (a shared
+    prefix), then each sequence's own blocks.  Returns (num_blocks,
+    block_tables int32)."""
     nb = [blocks_needed(L, block_size) for L in seq_lens]
-    total = int(sum(nb))
+    own = [max(0, n - shared_blocks) for n in nb]
+    total = int(shared_blocks + sum(own))
     if num_blocks is None:
         num_blocks = 1 + int(math.ceil((1.0 + extra_frac) * total))
     if num_blocks - 1 < total:
@@ -210,10 +222,13 @@ def build_pool(seq_lens, block_size: int, rng: np.random.Generator,
     perm = rng.permutation(np.arange(1, num_blocks, dtype=np.int64))
     max_blocks = max(nb) if nb else 0
     bt = np.zeros((len(seq_lens), max(max_blocks, 1)), dtype=np.int32)
-    pos = 0
+    pos = shared_blocks
     for s, n in enumerate(nb):
-        bt[s, :n] = perm[pos:pos + n]
-        pos += n
+        if n == 0:
+            continue
+        bt[s, :shared_blocks] = perm[:shared_blocks]
+        bt[s, shared_blocks:n] = perm[pos:pos + own[s]]
+        pos += own[s]
     return num_blocks, bt
 
 
@@ -223,9 +238,11 @@ def slots_of(block_table_row: np.ndarray, positions: np.ndarray, block_size: int
     return block_table_row[positions // block_size].astype(np.int64) * block_size + positions % block_size
 
 
-def _fill_cache(k_cache, v_cache, block_tables, fill_lens, block_size, child_seeds, sigma, dtype):
-    """Write fill_lens[s] leading tokens of every sequence into the pool,
-    K then V, each sequence from its own stream."""
+def _fill_cache(k_cache, v_cache, block_tables, fill_lens, block_size, child_seeds, sigma, dtype,
+                fill_from=None):
+    """Write tokens fill_from[s] .. fill_lens[s]-1 (fill_from defaults to 0)
+    of every sequence into the pool, K then V, each sequence from its own
+    stream."""
     Hkv, D = k_cache.shape[2], k_cache.shape[3]
     kf = k_cache.reshape(-1, Hkv, D)
     vf = v_cache.reshape(-1, Hkv, D)
@@ -233,11 +250,12 @@ def _fill_cache(k_cache, v_cache, block_tables, fill_lens, block_size, child_see
 
     def one(s):
         L = int(fill_lens[s])
-        if L <= 0:
+        lo = 0 if fill_from is None else int(fill_from[s])
+        if L <= lo:
             return
         rng = np.random.Generator(np.random.PCG64(child_seeds[s]))
         for cache in (kf, vf):
-            for t0 in range(0, L, chunk_tokens):
+            for t0 in range(lo, L, chunk_tokens):
                 t1 = min(L, t0 + chunk_tokens)
                 vals = _draw(rng, (t1 - t0) * Hkv * D, sigma, dtype).reshape(t1 - t0, Hkv, D)
                 cache[slots_of(block_tables[s], np.arange(t0, t1), block_size)] = vals
@@ -280,10 +298,15 @@ def make_decode(name, seq_lens, num_heads, num_kv_heads, head_size, block_size, 
 
 def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_size, block_size,
                 dtype, seed, sigma=1.0, causal=True, num_blocks=None, partition_size=0,
-                meta_rng=None, root=None) -> Workload:
+                meta_rng=None, root=None, common_prefix_len: int = 0) -> Workload:
     """Mixed step: sequence s has context_lens[s] tokens already cached and
     query_lens[s] new tokens whose K/V must first be scattered through
-    slot_mapping; seq_lens = context + query."""
+    slot_mapping; seq_lens = context + query.
+
+    common_prefix_len > 0 (a whole number of blocks, at most every non-empty
+    sequence's context): the first common_prefix_len tokens of every
+    non-empty sequence are one shared prefix, held once in blocks that start
+    every table and drawn from a stream of their own (spawned child 2 + S)."""
     context_lens = np.asarray(context_lens, dtype=np.int64)
     query_lens = np.asarray(query_lens, dtype=np.int64)
     seq_lens = (context_lens + query_lens).astype(np.int32)
@@ -291,13 +314,24 @@ def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_si
         root = np.random.SeedSequence(seed)
     if meta_rng is None:
         meta_rng = np.random.Generator(np.random.PCG64(root))
-    num_blocks, bt = build_pool(seq_lens, block_size, meta_rng, num_blocks)
+    cpl = int(common_prefix_len)
+    if cpl % block_size or cpl < 0:
+        raise ValueError("common_prefix_len must be a non-negative multiple of block_size")
+    if cpl and np.any((seq_lens > 0) & (context_lens < cpl)):
+        raise ValueError("the shared prefix must lie in every sequence's context")
+    num_blocks, bt = build_pool(seq_lens, block_size, meta_rng, num_blocks,
+                                shared_blocks=cpl // block_size)
     S = len(seq_lens)
-    children = root.spawn(2 + S)
+    children = root.spawn(2 + S + (1 if cpl else 0))
     shape = (num_blocks, block_size, num_kv_heads, head_size)
     k_cache = _poison(shape, dtype)
     v_cache = _poison(shape, dtype)
-    _fill_cache(k_cache, v_cache, bt, context_lens, block_size, children[2:], sigma, dtype)
+    if cpl:
+        owner = int(np.argmax(seq_lens > 0))           # any sequence holding the prefix
+        _fill_cache(k_cache, v_cache, bt[owner:owner + 1], [cpl], block_size, children[2 + S:],
+                    sigma, dtype)
+    _fill_cache(k_cache, v_cache, bt, context_lens, block_size, children[2:2 + S], sigma, dtype,
+                fill_from=np.where(seq_lens > 0, cpl, 0))
     T = int(query_lens.sum())
     new_rng = np.random.Generator(np.random.PCG64(children[1]))
     io = "bf16" if dtype == "fp8" else dtype
@@ -316,7 +350,7 @@ def make_varlen(name, context_lens, query_lens, num_heads, num_kv_heads, head_si
                     causal=causal, q=q, k_cache=k_cache, v_cache=v_cache, block_tables=bt,
                     seq_lens=seq_lens, cu_seqlens_q=cu, key_new=key_new, value_new=value_new,
                     slot_mapping=slot, partition_size=partition_size, sigma=sigma,
-                    k_scale=k_scale, v_scale=v_scale)
+                    k_scale=k_scale, v_scale=v_scale, common_prefix_len=cpl)
 
 
 # --------------------------------------------------------------------------
@@ -333,9 +367,10 @@ CONFIG_NAMES = {
     6: "llama7b_mha_decode_fp8",
     7: "gqa_decode_fp8",
     8: "long_context_sliding_window_decode_bf16",
+    9: "shared_prefix_cascade_decode_bf16",
 }
 
-DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3}   # 6, 7: the lengths and pools of 2, 3
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3, 9: 5}   # 6, 7: the lengths and pools of 2, 3
 
 
 def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
@@ -362,7 +397,7 @@ def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=No
 def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
                 max_len: Optional[int] = None, num_chunks: Optional[int] = None,
                 chunk_len: Optional[int] = None) -> Workload:
-    """Build workload `cfg` (1..8).  num_seqs / max_len / num_chunks /
+    """Build workload `cfg` (1..9).  num_seqs / max_len / num_chunks /
     chunk_len shrink it for quick parity runs; None keeps the full size."""
     if seed is None:
         seed = DEFAULT_SEEDS[cfg]
@@ -402,6 +437,17 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
                         partition_size=512, meta_rng=meta, root=root)
         w.window_left = 4095
         return w
+    if cfg == 9:
+        # decode rows of requests that share one prefix (a long system
+        # prompt): the GQA shapes of workload 3, a 4096-token prefix, then
+        # U{0..1023} tokens of each request's own context and its new token
+        n = 256 if num_seqs is None else num_seqs
+        cpl = 4096 if max_len is None else max(16, min(4096, (max_len // 2) // 16 * 16))
+        own_hi = 1023 if max_len is None else max(0, min(1023, max_len - cpl - 1))
+        own = meta.integers(0, own_hi, size=n, endpoint=True)
+        context = (cpl + own).astype(np.int64)
+        return make_varlen(name, context, np.ones(n, dtype=np.int64), 32, 8, 128, 16, "bf16",
+                           seed, causal=True, meta_rng=meta, root=root, common_prefix_len=cpl)
     if cfg in (6, 7):
         # the MHA and GQA decode shapes of workloads 2 and 3 over an fp8 cache
         L = config_lengths(cfg - 4, meta, num_seqs, max_len)
