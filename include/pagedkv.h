@@ -210,6 +210,84 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       void* stream);
 
 /*
+ * Cascade (shared-prefix) attention (vLLM book, ch. 6: "Structure des
+ * métadonnées" for the cascade fields common_prefix_len and the prefix query
+ * lengths; "forward()" for the cascade branch, a prefix call and a suffix
+ * call merged by merge_attn_states; "Réflexion de conception" for when to
+ * use it).  The result is that of pkv_paged_attention_varlen on the same
+ * arguments (no window); only the work is regrouped:
+ *   1. every query row of the batch attends to the shared prefix (keys
+ *      0 .. common_prefix_len-1 read through prefix_blocks, no mask), on the
+ *      matrix cores, the prefix split into key partitions with fp32 partials
+ *      in the workspace: the prefix is read once for the whole batch instead
+ *      of once per request;
+ *   2. each row attends to its own keys common_prefix_len .. seq_len-1 under
+ *      the usual mask (the varlen kernels; out and a suffix lse written);
+ *   3. a log-sum-exp merge combines the two results in place in out.
+ * Preconditions (not checked on this path; see pkv_validate_cascade):
+ * common_prefix_len is a multiple of block_size, every sequence with
+ * seq_len > 0 has its block table start with the prefix_blocks entries and
+ * holds the prefix in its context (common_prefix_len <= seq_len - query
+ * length).  Sequences with seq_len 0 are batch padding: zeros, lse -inf.
+ *   prefix_blocks  device int32 [common_prefix_len / block_size] (row 0 of
+ *                  block_tables will do)
+ *   other arguments as for pkv_paged_attention_varlen
+ *   workspace      >= pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned
+ * Needs a bfloat16 cache with head_size 128 (PKV_ERR_UNSUPPORTED otherwise);
+ * common_prefix_len 0 is the plain varlen call.  Asynchronous on `stream`.
+ * The suffix result is rounded to bfloat16 before the merge, as the output of
+ * the pages' suffix call is; the prefix partials stay fp32.
+ */
+pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* cache,
+                                 const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* prefix_blocks, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t common_prefix_len, float scale,
+                                 int32_t causal, int32_t partition_size, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of pkv_cascade_attention: the prefix partials
+ * [parts, num_heads, num_tokens, head_size] fp32 and their lse, the suffix
+ * lse [num_tokens, num_heads] fp32, then the suffix pass's split workspace
+ * (pkv_attention_workspace_bytes over the keys past the prefix).  The number
+ * of prefix partitions depends only on these arguments.  (size_t)-1 for
+ * invalid arguments.
+ */
+size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_size, int32_t max_seq_len,
+                                   int32_t common_prefix_len, int32_t partition_size);
+
+/*
+ * Should a batch use cascade attention?  NULL when it is advised, else a
+ * static string saying why not.  The pages' thresholds come first (ch. 6
+ * "Réflexion de conception": a shared prefix of at least 256 tokens, at least
+ * 8 requests, no sliding window), then a rough cost model of this library
+ * for the prefix's share of the work: the plain form takes the longer of
+ * num_seqs reads of the prefix from HBM and the rows' prefix flops on the
+ * matrix cores; the cascade the longer of one read and the same flops, plus
+ * writing and reading its fp32 partials.  dtype is a pkv_dtype;
+ * window_left -1 = none.
+ */
+const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t dtype, int32_t window_left);
+
+/*
+ * Debug check of HOST copies of a cascade batch's metadata: common_prefix_len
+ * a whole number of blocks, distinct prefix blocks, every sequence with
+ * seq_len > 0 starting its table with them and holding the prefix in its
+ * context, and its other blocks neither prefix blocks nor another sequence's.
+ * Returns PKV_OK or PKV_ERR_METADATA (message as pkv_validate_metadata).
+ */
+pkv_status pkv_validate_cascade(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs,
+                                const int32_t* cu_seqlens_q, const int32_t* prefix_blocks,
+                                int32_t common_prefix_len, int32_t block_size, char* msg,
+                                size_t msg_len);
+
+/*
  * Capability check in the spirit of supports_combination (ch. 6 "Matrice de
  * capacités"): NULL when the combination is supported, else a static string
  * saying why not.

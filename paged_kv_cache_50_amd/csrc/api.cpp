@@ -125,8 +125,9 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // Tokens one workgroup streams: about kMfmaTokensPerWg for large batches,
     // fewer (down to 256) when the whole launch has too little work to give
     // the 512 workgroup slots several rounds (few rows, or a short window).
-    const int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
-                                               : a.max_seq_len;
+    int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
+                                         : a.max_seq_len;
+    eff_len = std::max<int64_t>(1, std::min<int64_t>(eff_len, a.max_seq_len - a.kv_start));
     const int64_t work = (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks * eff_len;
     int tpw = kMfmaTokensPerWg;
     while (tpw > 256 && work / tpw < kMfmaTargetWgs) tpw >>= 1;
@@ -280,10 +281,195 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
   a.causal = 0;
   a.skip_multi_row = 0;
   a.window_left = -1;
+  a.kv_start = 0;
+  a.prefix_len = 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.k_scale = cache->k_scale;
   a.v_scale = cache->v_scale;
   return a;
+}
+
+// ----------------------------------------------------------------- cascade
+// Prefix pass geometry: the query tiles and head groups of the prefill
+// kernel over all rows of the batch, and enough key partitions (of at least
+// kPrefixMinPart tokens, at most kMaxPrefixParts) to give about
+// kPrefixTargetWgs workgroups.  Depends only on the call's sizes, so the
+// workspace size is known without a device.
+constexpr int32_t kMaxPrefixParts = 16;
+constexpr int32_t kPrefixMinPart = 256;
+constexpr int64_t kPrefixTargetWgs = 512;
+
+struct PrefixGeometry {
+  int32_t gc = 1;        // query heads per column group
+  unsigned qtiles = 0;   // query tiles over all rows
+  unsigned gy = 0;       // head groups
+  int32_t parts = 0;     // key partitions of the prefix
+  int32_t P = 0;         // tokens per partition (multiple of 32)
+};
+
+PrefixGeometry prefix_geometry(int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t cpl) {
+  PrefixGeometry g;
+  if (cpl <= 0 || num_tokens <= 0) return g;
+  const int group = num_heads / num_kv_heads;
+  int gc = 8;
+  while (group % gc) gc >>= 1;
+  g.gc = gc;
+  const int rows_per_wg = 16 * (8 / gc);
+  g.qtiles = (unsigned)((num_tokens + rows_per_wg - 1) / rows_per_wg);
+  g.gy = (unsigned)(num_kv_heads * (group / gc));
+  const int64_t base = (int64_t)g.qtiles * g.gy;
+  const int64_t most = std::min<int64_t>(kMaxPrefixParts, (cpl + kPrefixMinPart - 1) / kPrefixMinPart);
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(most, (kPrefixTargetWgs + base - 1) / base));
+  g.P = (int32_t)((((cpl + want - 1) / want) + 31) / 32 * 32);
+  g.parts = (cpl + g.P - 1) / g.P;
+  return g;
+}
+
+// Cascade workspace: prefix partial outputs [parts, heads, rows, D] fp32 and
+// their lse [parts, heads, rows], the suffix pass's lse [rows, heads], then
+// the suffix pass's own split workspace.
+struct CascadeLayout {
+  size_t pre_o = 0, pre_lse = 0, suf_lse = 0, varlen = 0, total = 0;
+};
+
+CascadeLayout cascade_layout(const PrefixGeometry& g, int32_t num_tokens, int32_t num_heads,
+                             int32_t head_size, size_t varlen_bytes) {
+  CascadeLayout l;
+  const size_t rows = (size_t)g.parts * num_heads * num_tokens;
+  l.pre_o = 0;
+  l.pre_lse = rows * head_size * sizeof(float);
+  l.suf_lse = align16(l.pre_lse + rows * sizeof(float));
+  l.varlen = align16(l.suf_lse + (size_t)num_tokens * num_heads * sizeof(float));
+  l.total = l.varlen + varlen_bytes;
+  return l;
+}
+
+// The varlen call; keys before kv_start are left out for every row (the
+// suffix pass of a cascade, arguments already checked; 0 otherwise).  The
+// split partitions and the workspace cover the span max_seq_len - (kv_start
+// rounded down to 32) that a row's partitions can reach.
+pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
+                       const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                       int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
+                       int32_t max_seq_len, float scale, int32_t causal, int32_t window_left,
+                       int32_t partition_size, float* lse_out, void* workspace,
+                       size_t workspace_bytes, void* stream, int32_t kv_start) {
+  pkv_status st = check_cache(cache, num_heads);
+  if (st != PKV_OK) return st;
+  if (window_left < -1) return PKV_ERR_SHAPE;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
+      max_query_len < 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
+    return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  // fp8 caches have the one-row (decode) kernel only
+  if (is_fp8(cache) && max_query_len > 1) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
+  const int32_t span = max_seq_len - (kv_start & ~31);
+  const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads, span,
+                                              partition_size);
+  if (P < 0) return PKV_ERR_SHAPE;
+  const int32_t ns = num_splits_for(span, P);
+  if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
+  if (ns > 1) {
+    const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
+                                                      cache->head_size, span, P);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                         num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, P,
+                         ns, lse_out, workspace);
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.window_left = window_left;
+  a.causal = causal ? 1 : 0;
+  a.kv_start = kv_start;
+  const int group = num_heads / cache->num_kv_heads;
+  const int gt = heads_per_chunk(group);
+  a.head_chunks = group / gt;
+  const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
+
+  // Prefill chunks and decode rows of one batch: a single interleaved launch.
+  if (max_query_len > 1 && use_mixed_launch(a, cache)) {
+    AttnArgs r = a;
+    r.mode = pkv::kModeVarlenRows;
+    r.partition_size = 0;
+    r.ws_o = nullptr;
+    r.ws_lse = nullptr;
+    int gc = 8;
+    while (group % gc) gc >>= 1;
+    r.head_chunks_gc = gc;
+    const int rows_per_wg = 16 * (8 / gc);
+    AttnArgs d = a;
+    d.mode = pkv::kModeVarlenOne;
+    d.seq_order = order_area(d, cache, workspace);   // written by the planner below
+    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
+    pkv::MixedGrid g{};
+    g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
+    g.pre_y = cache->num_kv_heads * (group / gc);
+    g.dec_x = (int32_t)gx_d;
+    g.dec_y = num_seqs;
+    g.dec_z = (int32_t)gparts;
+    g.n_dec = (int64_t)g.dec_x * g.dec_y * g.dec_z;
+    g.pre_list = d.seq_order + num_seqs;
+    g.pre_count = d.seq_order + 2 * num_seqs;
+    g.queues = order_area(d, cache, workspace) + 2 * num_seqs + 1;
+    g.workgroups = 2 * device_cus();                // two per CU (LDS and registers allow two)
+    const int64_t n_pre_max = (int64_t)g.pre_x * g.pre_y * num_seqs;
+    if (g.workgroups > 0 && n_pre_max < (int64_t)INT32_MAX && g.n_dec < (int64_t)INT32_MAX) {
+      st = plan_seq_order(d, cache, workspace, s, /*multi=*/true);
+      if (st != PKV_OK) return st;
+      int tslot = 0;
+      const bool timed = timing_begin(s, &tslot);
+      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, s) != hipSuccess) st = PKV_ERR_HIP;
+      if (timed) timing_end(s, tslot);
+      if (st != PKV_OK) return st;
+      return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+    }
+  }
+  // Rows of sequences with several query rows (chunked prefill).
+  if (max_query_len > 1) {
+    AttnArgs r = a;
+    r.mode = pkv::kModeVarlenRows;
+    r.partition_size = 0;
+    r.ws_o = nullptr;
+    r.ws_lse = nullptr;
+    int tslot = 0;
+    const bool timed = timing_begin(s, &tslot);
+    if (use_mfma_prefill(cache)) {
+      int gc = 8;
+      while (group % gc) gc >>= 1;
+      r.head_chunks_gc = gc;
+      const int rows_per_wg = 16 * (8 / gc);
+      const unsigned qtiles = (unsigned)((max_query_len + rows_per_wg - 1) / rows_per_wg);
+      const unsigned gy = (unsigned)(cache->num_kv_heads * (group / gc));
+      for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
+        r.z_base = (int32_t)z0;
+        const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, num_seqs - z0);
+        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, dim3(qtiles, gy, gz), s) != hipSuccess)
+          st = PKV_ERR_HIP;
+      }
+    } else {
+      st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
+                                num_tokens, s);
+    }
+    if (timed) timing_end(s, tslot);
+    if (st != PKV_OK) return st;
+  }
+  // Sequences with one query row (decode rows), split over the key range.
+  a.mode = pkv::kModeVarlenOne;
+  st = plan_seq_order(a, cache, workspace, s);
+  if (st != PKV_OK) return st;
+  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
+  if (st != PKV_OK) return st;
+  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
+  return st;
 }
 
 }  // namespace
@@ -419,118 +605,167 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       int32_t causal, int32_t window_left, int32_t partition_size,
                                       float* lse_out, void* workspace, size_t workspace_bytes,
                                       void* stream) {
+  return varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
+                     num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
+                     window_left, partition_size, lse_out, workspace, workspace_bytes, stream, 0);
+}
+
+size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_size, int32_t max_seq_len,
+                                   int32_t common_prefix_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_seq_len < 0 || common_prefix_len < 0 || common_prefix_len > max_seq_len ||
+      num_heads % num_kv_heads != 0)
+    return (size_t)-1;
+  const int32_t span = max_seq_len - (common_prefix_len & ~31);
+  const size_t vw = pkv_attention_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size,
+                                                  span, partition_size);
+  if (vw == (size_t)-1) return vw;
+  if (common_prefix_len == 0) return vw;
+  const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, num_kv_heads, common_prefix_len);
+  return cascade_layout(g, num_tokens, num_heads, head_size, vw).total;
+}
+
+const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int32_t num_tokens,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t dtype, int32_t window_left) {
+  if (dtype != PKV_BF16 || head_size != 128)
+    return "cascade attention needs bfloat16 caches with head_size 128";
+  if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return "num_heads must be a positive multiple of num_kv_heads";
+  if (window_left >= 0) return "sliding-window attention does not use the cascade";
+  if (common_prefix_len < 256) return "common prefix shorter than 256 tokens";
+  if (num_seqs < 8) return "fewer than 8 requests";
+  if (num_tokens <= 0) return "no query rows";
+  // Rough cost model of the prefix's share of the work.  The plain form
+  // streams the prefix once per request and does the rows' prefix flops in
+  // the shadow of that stream (or on the matrix cores for prefill rows):
+  // max(requests x prefix bytes / HBM, flops / MFMA).  The cascade streams it
+  // once, does the same flops on the matrix cores, and writes and reads the
+  // fp32 partials: max(prefix bytes / HBM, flops / MFMA) + partials / HBM.
+  const double kv_bytes = 2.0 * common_prefix_len * num_kv_heads * head_size * 2;
+  const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, num_kv_heads, common_prefix_len);
+  const double partial_bytes = 2.0 * g.parts * num_heads * (double)num_tokens * (head_size + 1) * 4;
+  const double flops = 4.0 * num_tokens * num_heads * (double)head_size * common_prefix_len;
+  const double hbm = 8.0e12 * 0.7, mfma = 2.5e15 * 0.3;   // sustained rates assumed
+  const double t_plain = std::max(num_seqs * kv_bytes / hbm, flops / mfma);
+  const double t_cascade = std::max(kv_bytes / hbm, flops / mfma) + partial_bytes / hbm;
+  if (t_cascade >= t_plain)
+    return "the prefix pass would cost more than re-reading the prefix per request";
+  return nullptr;
+}
+
+pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* cache,
+                                 const int32_t* cu_seqlens_q, const int32_t* seq_lens,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* prefix_blocks, int32_t num_seqs,
+                                 int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t common_prefix_len, float scale,
+                                 int32_t causal, int32_t partition_size, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   pkv_status st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
-  if (window_left < -1) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
       max_query_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
+  if (cache->dtype != PKV_BF16 || cache->head_size != 128) return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
-  // fp8 caches have the one-row (decode) kernel only
-  if (is_fp8(cache) && max_query_len > 1) return PKV_ERR_UNSUPPORTED;
+  const int32_t cpl = common_prefix_len;
+  if (cpl < 0 || cpl % cache->block_size != 0 || cpl > max_seq_len ||
+      (int64_t)cpl > (int64_t)max_blocks_per_seq * cache->block_size)
+    return PKV_ERR_SHAPE;
+  if (cpl == 0)
+    return varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
+                       num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
+                       -1, partition_size, lse_out, workspace, workspace_bytes, stream, 0);
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
-  if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
+  if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q || !prefix_blocks)
+    return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
-  const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads,
-                                              max_seq_len, partition_size);
-  if (P < 0) return PKV_ERR_SHAPE;
-  const int32_t ns = num_splits_for(max_seq_len, P);
-  if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
-  if (ns > 1) {
-    const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
-                                                      cache->head_size, max_seq_len, P);
-    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-  }
+  const int32_t span = max_seq_len - (cpl & ~31);
+  const size_t vw = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
+                                                  cache->head_size, span, partition_size);
+  if (vw == (size_t)-1) return PKV_ERR_SHAPE;
+  const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, cache->num_kv_heads, cpl);
+  if (g.parts < 1 || g.parts > kMaxPrefixParts || g.qtiles > (unsigned)INT32_MAX) return PKV_ERR_SHAPE;
+  const CascadeLayout lay = cascade_layout(g, num_tokens, num_heads, cache->head_size, vw);
+  if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
-                         num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, P,
-                         ns, lse_out, workspace);
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.window_left = window_left;
-  a.causal = causal ? 1 : 0;
-  const int group = num_heads / cache->num_kv_heads;
-  const int gt = heads_per_chunk(group);
-  a.head_chunks = group / gt;
-  const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
 
-  // Prefill chunks and decode rows of one batch: a single interleaved launch.
-  if (max_query_len > 1 && use_mixed_launch(a, cache)) {
-    AttnArgs r = a;
-    r.mode = pkv::kModeVarlenRows;
-    r.partition_size = 0;
-    r.ws_o = nullptr;
-    r.ws_lse = nullptr;
-    int gc = 8;
-    while (group % gc) gc >>= 1;
-    r.head_chunks_gc = gc;
-    const int rows_per_wg = 16 * (8 / gc);
-    AttnArgs d = a;
-    d.mode = pkv::kModeVarlenOne;
-    d.seq_order = order_area(d, cache, workspace);   // written by the planner below
-    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
-    pkv::MixedGrid g{};
-    g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
-    g.pre_y = cache->num_kv_heads * (group / gc);
-    g.dec_x = (int32_t)gx_d;
-    g.dec_y = num_seqs;
-    g.dec_z = (int32_t)gparts;
-    g.n_dec = (int64_t)g.dec_x * g.dec_y * g.dec_z;
-    g.pre_list = d.seq_order + num_seqs;
-    g.pre_count = d.seq_order + 2 * num_seqs;
-    g.queues = order_area(d, cache, workspace) + 2 * num_seqs + 1;
-    g.workgroups = 2 * device_cus();                // two per CU (LDS and registers allow two)
-    const int64_t n_pre_max = (int64_t)g.pre_x * g.pre_y * num_seqs;
-    if (g.workgroups > 0 && n_pre_max < (int64_t)INT32_MAX && g.n_dec < (int64_t)INT32_MAX) {
-      st = plan_seq_order(d, cache, workspace, s, /*multi=*/true);
-      if (st != PKV_OK) return st;
-      int tslot = 0;
-      const bool timed = timing_begin(s, &tslot);
-      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, s) != hipSuccess) st = PKV_ERR_HIP;
-      if (timed) timing_end(s, tslot);
-      if (st != PKV_OK) return st;
-      return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+  // 1. prefix pass: every row against the shared prefix, fp32 partials
+  AttnArgs p = base_args(out, q, cache, prefix_blocks, cpl / cache->block_size, seq_lens, num_seqs,
+                         num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, 0,
+                         1, nullptr, nullptr);
+  p.mode = pkv::kModePrefix;
+  p.prefix_len = cpl;
+  p.partition_size = g.P;
+  p.num_splits = g.parts;
+  p.head_chunks_gc = g.gc;
+  p.ws_o = reinterpret_cast<float*>(ws + lay.pre_o);
+  p.ws_lse = reinterpret_cast<float*>(ws + lay.pre_lse);
+  if (pkv::launch_attn_mfma_prefix(p, cache->block_size, dim3(g.qtiles, g.gy, (unsigned)g.parts),
+                                   s) != hipSuccess)
+    return PKV_ERR_HIP;
+  // 2. suffix pass: each row against its own keys (from the prefix end on)
+  float* lse_suffix = reinterpret_cast<float*>(ws + lay.suf_lse);
+  st = varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
+                   num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal, -1,
+                   partition_size, lse_suffix, vw ? ws + lay.varlen : nullptr, vw, stream, cpl);
+  if (st != PKV_OK) return st;
+  // 3. merge of the two results, in place in out
+  AttnArgs m = p;
+  m.cu_seqlens_q = cu_seqlens_q;
+  m.lse_out = lse_out;
+  if (pkv::launch_cascade_merge(m, lse_suffix, g.parts, s) != hipSuccess) return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+pkv_status pkv_validate_cascade(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t num_seqs,
+                                const int32_t* cu_seqlens_q, const int32_t* prefix_blocks,
+                                int32_t common_prefix_len, int32_t block_size, char* msg,
+                                size_t msg_len) {
+  auto fail = [&](const char* fmt, ...) {
+    if (msg && msg_len) {
+      va_list ap;
+      va_start(ap, fmt);
+      vsnprintf(msg, msg_len, fmt, ap);
+      va_end(ap);
+    }
+    return PKV_ERR_METADATA;
+  };
+  if (msg && msg_len) msg[0] = '\0';
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0) return fail("bad sizes");
+  const int32_t cpl = common_prefix_len;
+  if (cpl < 0 || cpl % block_size) return fail("common_prefix_len %d is not a whole number of blocks", cpl);
+  const int32_t nb = cpl / block_size;
+  if (nb > max_blocks_per_seq) return fail("prefix of %d blocks exceeds max_blocks_per_seq", nb);
+  if (num_seqs > 0 && (!block_tables || !seq_lens || !cu_seqlens_q))
+    return fail("NULL block_tables, seq_lens or cu_seqlens_q");
+  if (nb > 0 && !prefix_blocks) return fail("NULL prefix_blocks");
+  std::unordered_set<int32_t> pre(prefix_blocks, prefix_blocks + nb);
+  if ((int32_t)pre.size() != nb) return fail("a prefix block is listed twice");
+  std::unordered_set<int32_t> own;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = seq_lens[s];
+    if (L == 0) continue;
+    const int32_t ql = cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+    if (cpl > L - ql) return fail("sequence %d: prefix of %d tokens reaches its query rows", s, cpl);
+    const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int32_t i = 0; i < nb; ++i)
+      if (row[i] != prefix_blocks[i])
+        return fail("sequence %d: block_tables[%d] = %d, prefix block %d", s, i, row[i], prefix_blocks[i]);
+    const int32_t n = (int32_t)std::min<int64_t>(((int64_t)L + block_size - 1) / block_size, max_blocks_per_seq);
+    for (int32_t i = nb; i < n; ++i) {
+      if (pre.count(row[i])) return fail("sequence %d: own block %d is a prefix block", s, row[i]);
+      if (!own.insert(row[i]).second) return fail("block %d owned twice (seq %d)", row[i], s);
     }
   }
-  // Rows of sequences with several query rows (chunked prefill).
-  if (max_query_len > 1) {
-    AttnArgs r = a;
-    r.mode = pkv::kModeVarlenRows;
-    r.partition_size = 0;
-    r.ws_o = nullptr;
-    r.ws_lse = nullptr;
-    int tslot = 0;
-    const bool timed = timing_begin(s, &tslot);
-    if (use_mfma_prefill(cache)) {
-      int gc = 8;
-      while (group % gc) gc >>= 1;
-      r.head_chunks_gc = gc;
-      const int rows_per_wg = 16 * (8 / gc);
-      const unsigned qtiles = (unsigned)((max_query_len + rows_per_wg - 1) / rows_per_wg);
-      const unsigned gy = (unsigned)(cache->num_kv_heads * (group / gc));
-      for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
-        r.z_base = (int32_t)z0;
-        const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, num_seqs - z0);
-        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, dim3(qtiles, gy, gz), s) != hipSuccess)
-          st = PKV_ERR_HIP;
-      }
-    } else {
-      st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
-                                num_tokens, s);
-    }
-    if (timed) timing_end(s, tslot);
-    if (st != PKV_OK) return st;
-  }
-  // Sequences with one query row (decode rows), split over the key range.
-  a.mode = pkv::kModeVarlenOne;
-  st = plan_seq_order(a, cache, workspace, s);
-  if (st != PKV_OK) return st;
-  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
-  if (st != PKV_OK) return st;
-  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
-  return st;
+  return PKV_OK;
 }
 
 pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks_per_seq,

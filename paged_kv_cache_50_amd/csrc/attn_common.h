@@ -62,6 +62,8 @@ __device__ __forceinline__ bool resolve_item(const AttnArgs& a, int z, Item& it)
     L_begin = min(max(0, pos - a.window_left), L_end);
     if (!(a.causal || a.mode != kModeVarlenRows)) L_end = min(L_end, max(0, pos + a.window_left + 1));
   }
+  // keys before kv_start are left out (cascade suffix pass)
+  L_begin = max(L_begin, min(a.kv_start, L_end));
   it.seq = seq;
   it.row = row;
   it.L_begin = L_begin;

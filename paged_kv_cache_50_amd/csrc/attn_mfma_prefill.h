@@ -87,13 +87,29 @@ __device__ __forceinline__ float xsum16_32(float x) {
 
 // One workgroup's work: query tile bx, head group by of sequence seq.  The
 // caller provides the LDS ring (kLdsBytes, 16-byte aligned).
-template <int BS>
+// PREFIX (cascade prefix pass): the rows are all num_tokens query rows of
+// the batch, the keys are partition `seq` (partition_size tokens) of the
+// shared prefix read through block_tables row 0, no mask applies, and the
+// result is a normalised fp32 partial with its log2-domain log-sum-exp.
+template <int BS, bool PREFIX = false>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
-  const int qs = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq), 0, a.num_tokens);
-  const int qe = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq + 1), 0, a.num_tokens);
-  const int q_len = min(qe - qs, a.max_query_len);
-  if (qe - qs <= 1) return;                          // one-row sequences: decode kernels
+  int qs, q_len, L, off;
+  const int part = PREFIX ? seq : 0;
+  if constexpr (PREFIX) {
+    seq = 0;
+    qs = 0;
+    q_len = a.num_tokens;
+    L = a.prefix_len;
+    off = 0;
+  } else {
+    qs = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq), 0, a.num_tokens);
+    const int qe = clamp_i(load_uniform_i32(a.cu_seqlens_q, seq + 1), 0, a.num_tokens);
+    q_len = min(qe - qs, a.max_query_len);
+    if (qe - qs <= 1) return;                        // one-row sequences: decode kernels
+    L = clamp_seq_len(load_uniform_i32(a.seq_lens, seq), a.max_seq_len, a.max_blocks_per_seq, BS);
+    off = L - (qe - qs);                             // absolute position of row i = i + off
+  }
   const int GC = a.head_chunks_gc;                   // query heads per column group (<= 8)
   const int R = kColTiles / GC;                      // row blocks per workgroup
   const int q0 = bx * 16 * R;
@@ -102,9 +118,6 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int chunks = group / GC;
   const int kvh = by / chunks;
   const int hbase = kvh * group + (by % chunks) * GC;
-  const int L = clamp_seq_len(load_uniform_i32(a.seq_lens, seq), a.max_seq_len,
-                              a.max_blocks_per_seq, BS);
-  const int off = L - (qe - qs);                     // absolute position of row i = i + off
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,10 +129,15 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int q_last = min(q0 + 16 * R, q_len) - 1;
   // sliding window w: row at position p sees keys p - w .. p (causal) or
   // p - w .. p + w (not causal)
-  const int win = a.window_left;
-  int kv_end = a.causal ? max(0, min(L, q_last + off + 1)) : L;
-  if (win >= 0 && !a.causal) kv_end = max(0, min(kv_end, q_last + off + win + 1));
-  const int kv_begin = win >= 0 ? min(max(0, q0 + off - win), kv_end) : 0;
+  const int win = PREFIX ? -1 : a.window_left;
+  const bool causal = PREFIX ? false : a.causal != 0;
+  // first key of the range for every row: the prefix partition's start, or
+  // kv_start (keys before it belong to a cascade's prefix pass)
+  const int key_lo = PREFIX ? min(part * a.partition_size, L) : a.kv_start;
+  int kv_end = causal ? max(0, min(L, q_last + off + 1)) : L;
+  if (PREFIX) kv_end = min(L, key_lo + a.partition_size);
+  if (win >= 0 && !causal) kv_end = max(0, min(kv_end, q_last + off + win + 1));
+  const int kv_begin = min(max(win >= 0 ? max(0, q0 + off - win) : 0, key_lo), kv_end);
   const int ntiles = (kv_end + kTile - 1) / kTile;   // tiles t_begin .. ntiles - 1
   const int t_begin = kv_begin / kTile;
 
@@ -135,9 +153,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     live[c] = rowb[c] < q_len;
     if (live[c]) wave_last_pos = max(wave_last_pos, min(rowb[c] + 15, q_len - 1) + off);
   }
-  if (!a.causal) wave_last_pos = win >= 0 ? min(L - 1, wave_last_pos + win) : L - 1;
-  // smallest key position this wave may see (sliding window)
-  const int wave_first_key = win >= 0 ? min(rowb[0], rowb[1]) + off - win : 0;
+  if (!causal) wave_last_pos = win >= 0 ? min(L - 1, wave_last_pos + win) : L - 1;
+  // smallest key position this wave may see (sliding window, range start)
+  const int wave_first_key = max(win >= 0 ? min(rowb[0], rowb[1]) + off - win : 0, key_lo);
 
   // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
   bf16x8_t qb[2][4];
@@ -237,9 +255,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qpos = rowb[c] + n + off;            // this lane's column = query row
-      const int lim = a.causal ? min(qpos, kv_end - 1)
-                                : (win >= 0 ? min(qpos + win, kv_end - 1) : kv_end - 1);
-      const int lo = win >= 0 ? qpos - win : 0;
+      const int lim = causal ? min(qpos, kv_end - 1)
+                              : (win >= 0 ? min(qpos + win, kv_end - 1) : kv_end - 1);
+      const int lo = max(win >= 0 ? qpos - win : 0, key_lo);
       // raw logits; the scale is applied inside the exponent (one FMA)
       float s[8];
 #pragma unroll
@@ -326,9 +344,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // the range end) take the masked path.  Every wave runs both loops over
   // the same tiles, so the barriers stay matched.
   // With a window, tiles below the last row's window start are masked too.
-  int unmasked_end = a.causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
-  if (win >= 0 && !a.causal) unmasked_end = min(unmasked_end, q0 + off + win);
-  const int unmasked_begin = win >= 0 ? max(0, q_last + off - win) : 0;
+  int unmasked_end = causal ? min(q0 + off, kv_end - 1) : kv_end - 1;
+  if (win >= 0 && !causal) unmasked_end = min(unmasked_end, q0 + off + win);
+  const int unmasked_begin = max(win >= 0 ? max(0, q_last + off - win) : 0, key_lo);
   const int tu = min(ntiles, max(t_begin, (unmasked_begin + kTile - 1) / kTile));
   const int tm = min(ntiles, max(tu, (unmasked_end + 1) / kTile));
   for (int t = t_begin; t < tu; ++t) step(t, std::true_type{});
@@ -342,6 +360,15 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     const int row = rowb[c] + n;
     if (!live[c] || row >= q_len) continue;
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    if constexpr (PREFIX) {
+      const int64_t e = ((int64_t)part * a.num_heads + head[c]) * a.num_tokens + row;
+      float* op = a.ws_o + e * kD;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        *reinterpret_cast<f32x4*>(op + 16 * jd + 4 * kg) = o[c][jd] * inv;
+      if (kg == 0) a.ws_lse[e] = ls > 0.f ? m[c] + acc_log2(ls) : -INFINITY;
+      continue;
+    }
     uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {

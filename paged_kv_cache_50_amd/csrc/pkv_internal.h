@@ -11,7 +11,10 @@ namespace pkv {
 enum AttnMode : int32_t {
   kModeDecode = 0,     // z = sequence; one query row per sequence (row = sequence)
   kModeVarlenOne = 1,  // z = sequence; only sequences with exactly one query row
-  kModeVarlenRows = 2  // z = query row; only rows of sequences with > 1 query rows, no split
+  kModeVarlenRows = 2, // z = query row; only rows of sequences with > 1 query rows, no split
+  kModePrefix = 3      // cascade prefix pass: every query row of the batch against the shared
+                       // prefix (keys 0 .. prefix_len-1 through block_tables row 0), no mask;
+                       // z = key partition of partition_size tokens, fp32 partials out
 };
 
 // Arguments of the attention kernels (passed by value).
@@ -51,6 +54,9 @@ struct AttnArgs {
   int32_t window_left;             // sliding window (keys >= pos - window_left; symmetric
                                    // when not causal), -1 = none
   int32_t skip_multi_row;          // kModeVarlenRows: 1 if another kernel owns multi-row seqs
+  int32_t kv_start;                // keys before this position are left out for every row
+                                   // (cascade suffix pass; 0 otherwise)
+  int32_t prefix_len;              // kModePrefix: keys of the shared prefix
   float scale_log2;                // scale * log2(e)
   const float* k_scale;            // fp8 caches: per-kv-head scales (value = code * scale)
   const float* v_scale;
@@ -122,6 +128,21 @@ struct MixedGrid {
 };
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                              int block_size, hipStream_t stream);
+
+// Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16, head
+// size 128): grid = (query tiles of 128 / head_chunks_gc rows over all
+// num_tokens rows, num_kv_heads * group / head_chunks_gc, key partitions).
+// Writes normalised fp32 partials to ws_o [part][head][row][D] and their
+// log2-domain log-sum-exps to ws_lse [part][head][row].
+hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, dim3 grid,
+                                   hipStream_t stream);
+
+// Cascade merge: out (the suffix result, in place) and its natural-log lse
+// `lse_suffix` [rows, heads] are combined with `num_parts` prefix partials
+// (layout of launch_attn_mfma_prefix); rows of sequences with seq_len 0 keep
+// the suffix result (zeros).  bfloat16 out, head size 128.
+hipError_t launch_cascade_merge(const AttnArgs& a, const float* lse_suffix, int num_parts,
+                                hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,

@@ -57,6 +57,13 @@ _SIGS = {
     "pkv_paged_attention_varlen": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
                                           _vp, _vp, _sz, _vp]),
+    "pkv_cascade_attention": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp, _i32,
+                                     _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                     _vp, _vp, _sz, _vp]),
+    "pkv_cascade_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_cascade_reason": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_validate_cascade": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, ctypes.c_char_p,
+                                    _sz]),
     "pkv_unsupported_reason": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_validate_metadata": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _i64, _i64,
@@ -274,6 +281,78 @@ def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, blo
         int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
         "paged_attention_varlen")
     return out
+
+
+def cascade_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads, head_size,
+                            max_seq_len, common_prefix_len, partition_size=0) -> int:
+    n = lib().pkv_cascade_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                          head_size, max_seq_len, common_prefix_len,
+                                          partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(2, "cascade_workspace_bytes")
+    return int(n)
+
+
+def cascade_reason(common_prefix_len, num_seqs, num_tokens, num_heads, num_kv_heads, head_size,
+                   dtype=PKV_BF16, window_left=-1) -> Optional[str]:
+    """None when cascade attention is advised for the batch, else why not."""
+    r = lib().pkv_cascade_reason(common_prefix_len, num_seqs, num_tokens, num_heads, num_kv_heads,
+                                 head_size, dtype, window_left)
+    return None if r is None else r.decode()
+
+
+def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
+                      prefix_blocks, common_prefix_len: int, scale: float, max_query_len: int,
+                      max_seq_len: int, causal: bool = True, partition_size: int = 0,
+                      workspace=None, lse_out=None):
+    """Cascade (shared-prefix) attention over a flattened batch (q/out
+    [T, Hq, D]): the result of paged_attention_varlen on the same arguments,
+    with the prefix blocks (int32 [common_prefix_len / block_size], shared
+    by every sequence's table) read once for the whole batch."""
+    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, prefix_blocks, workspace, lse_out)
+    desc = cache_descriptor(k_cache, v_cache)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"),
+                 (block_tables, "block_tables"), (prefix_blocks, "prefix_blocks")):
+        _meta(t, n)
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache dtype")
+    T, Hq, D = q.shape
+    S = seq_lens.shape[0]
+    if out.shape != q.shape or cu_seqlens_q.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("shape mismatch")
+    if prefix_blocks.shape[0] * k_cache.shape[1] < common_prefix_len:
+        raise ValueError("prefix_blocks shorter than the prefix")
+    if lse_out is not None and (tuple(lse_out.shape) != (T, Hq) or not lse_out.is_contiguous()):
+        raise ValueError("lse_out must be a contiguous float32 [num_tokens, num_heads]")
+    need = cascade_workspace_bytes(S, T, Hq, desc.num_kv_heads, D, max_seq_len, common_prefix_len,
+                                   partition_size)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    _check(lib().pkv_cascade_attention(
+        out.data_ptr(), q.data_ptr(), ctypes.byref(desc), cu_seqlens_q.data_ptr(),
+        seq_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        prefix_blocks.data_ptr(), S, T, Hq, int(max_query_len), int(max_seq_len),
+        int(common_prefix_len), float(scale), 1 if causal else 0, int(partition_size),
+        _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)), "cascade_attention")
+    return out
+
+
+def validate_cascade(block_tables, seq_lens, cu_seqlens_q, prefix_blocks, common_prefix_len,
+                     block_size):
+    """Check host copies of a cascade batch's metadata.  Returns "" when
+    valid, else the first problem found."""
+    import numpy as np
+
+    def arr(x):
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(x, dtype=np.int32)
+
+    bt, sl, cu, pb = arr(block_tables), arr(seq_lens), arr(cu_seqlens_q), arr(prefix_blocks)
+    msg = ctypes.create_string_buffer(256)
+    st = lib().pkv_validate_cascade(bt.ctypes.data, bt.shape[1], sl.ctypes.data, sl.shape[0],
+                                    cu.ctypes.data, pb.ctypes.data if pb.size else None,
+                                    int(common_prefix_len), int(block_size), msg, 256)
+    return "" if st == PKV_OK else (msg.value.decode() or "invalid metadata")
 
 
 def validate_metadata(block_tables, seq_lens, max_seq_len, num_blocks, block_size,
