@@ -3,7 +3,9 @@
 A step is one pass of the hot path over one batch of synthetic input: for a
 decode workload one paged_attention_decode call (partition kernel + split
 merge) for one attention layer; for the mixed workload the slot write plus
-one paged_attention_varlen call.  Inputs are resident in HBM before timing.
+one paged_attention_varlen call; for the shared-prefix workload the slot
+write plus one cascade_attention call.  Inputs are resident in HBM before
+timing.
 
 Prints ONE JSON line (rank 0).  `value` is achieved HBM GB/s of the whole step
 (algorithmic bytes / step time); `roofline` is the dominant kernel's achieved
@@ -11,7 +13,7 @@ rate against the MI355X peak, from per-launch HIP events recorded by the
 library inside the timed region; `cpu_baseline` times the fp64 CPU oracle on
 the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2..5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..9]
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ WORKLOAD_DESC = {
     6: "workload 2 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
     7: "workload 3 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
     8: "workload 4 (same lengths and pool) with a 4096-key sliding window (window_left 4095)",
+    9: "slot write + cascade attention: 256 decode requests sharing a 4096-token prefix, own context U[0,1023] + 1 new token, 32/8 heads, head 128, block 16, bf16, seed 5",
 }
 
 
@@ -51,6 +54,7 @@ KERNEL_SOURCES = {
     "attn_mfma_prefill_kernel": ["attn_mfma_prefill.hip", "attn_mfma_prefill.h"],
     "attn_mixed_kernel": ["attn_mixed.hip", "attn_mfma_decode.h", "attn_mfma_prefill.h",
                           "seq_order.hip"],
+    "attn_mfma_prefix_kernel": ["attn_mfma_prefill.hip", "attn_mfma_prefill.h"],
 }
 COMMON_SOURCES = ["device_common.h", "attn_common.h", "api.cpp"]
 
@@ -124,6 +128,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
                                pairs=[(s, h)], k_scale=w.k_scale, v_scale=w.v_scale,
                                window_left=w.window_left)
         keys = int(w.seq_lens[s]) if w.window_left < 0 else min(int(w.seq_lens[s]), w.window_left + 1)
+        if w.common_prefix_len and keys:
+            # the cascade's bytes: the shared prefix is credited once per batch
+            keys += w.common_prefix_len // w.num_seqs - w.common_prefix_len
         done_bytes += (keys * 2 * w.head_size * e
                        + 2 * int(ql[s]) * g * w.head_size * w.io_bytes)
         done_pairs += 1
@@ -201,7 +208,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -248,16 +255,26 @@ def main() -> int:
     print(f"[bench] generated {w.name} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
     ps = w.partition_size if args.partition_size is None else args.partition_size
     dw = G.DevWorkload(w, device=dev)
+    S, T = w.num_seqs, w.num_q_rows
+    cascade = w.common_prefix_len > 0
     ws_bytes = pagedkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
                                        w.max_seq_len, ps)
+    if cascade:
+        ws_bytes = max(ws_bytes, pagedkv.cascade_workspace_bytes(
+            S, T, w.num_heads, w.num_kv_heads, w.head_size, w.max_seq_len, w.common_prefix_len, ps))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    S, T = w.num_seqs, w.num_q_rows
 
-    def step():
+    def step(plain=False):
         if w.slot_mapping is not None:
             pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new,
                                    dw.slot_mapping, k_scale=dw.k_scale, v_scale=dw.v_scale)
-        if w.cu_seqlens_q is None:
+        if cascade and not plain:
+            pagedkv.cascade_attention(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
+                                      dw.seq_lens, dw.block_tables, dw.prefix_blocks,
+                                      w.common_prefix_len, w.scale, w.max_query_len,
+                                      w.max_seq_len, causal=w.causal, partition_size=ps,
+                                      workspace=ws)
+        elif w.cu_seqlens_q is None:
             pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                            dw.seq_lens, w.scale, w.max_seq_len,
                                            partition_size=ps, workspace=ws, k_scale=dw.k_scale,
@@ -326,12 +343,57 @@ def main() -> int:
     except Exception as exc:                        # reported, never fatal
         print(f"[bench] graph replay unavailable: {exc}", file=sys.stderr, flush=True)
 
+    plain_us = None
+    if cascade:
+        # the same step without the cascade (the plain varlen call), for
+        # comparison; outside the timed region
+        for _ in range(3):
+            step(plain=True)
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        n_plain = max(1, args.steps // 5)
+        p0.record()
+        for _ in range(n_plain):
+            step(plain=True)
+        p1.record()
+        torch.cuda.synchronize()
+        plain_us = p0.elapsed_time(p1) * 1e3 / n_plain
+
     B = W.algorithmic_bytes(w)
     e = w.elem_bytes
     out_bytes = T * w.num_heads * w.head_size * w.io_bytes
     gbs = B / (ms_per_step * 1e-3) / 1e9
     kavg = float(np.mean(kern_ms)) if kern_ms else None
-    if w.cu_seqlens_q is None:
+    if cascade:
+        # the dominant launch is the suffix pass (decode rows streaming each
+        # request's own keys): its own KV, q in, the suffix result out, and
+        # the table entries past the prefix
+        L = w.seq_lens.astype(np.int64)
+        own = np.where(L > 0, L - w.common_prefix_len, 0)
+        nb_own = np.where(L > 0, (L + w.block_size - 1) // w.block_size
+                          - w.common_prefix_len // w.block_size, 0)
+        main_bytes = (int(own.sum()) * 2 * w.num_kv_heads * w.head_size * e + 2 * out_bytes
+                      + 4 * int(nb_own.sum()) + 4 * (2 * S + 1))
+        fused = (os.environ.get("PKV_CASCADE_FUSED", "1") != "0" and w.max_query_len <= 1
+                 and w.num_heads // w.num_kv_heads >= 4)
+        if fused:
+            # one launch also runs the prefix pass: the prefix's keys and
+            # values once
+            main_bytes += (w.common_prefix_len * 2 * w.num_kv_heads * w.head_size * e
+                           + 4 * (w.common_prefix_len // w.block_size))
+        achieved = main_bytes / (kavg * 1e-3) / 1e9 if kavg else None
+        roof = {"bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                "traffic": load_traffic(w.name),
+                "kernel_ms": round(kavg, 5) if kavg else None, "launches": len(kern_ms),
+                "kernel_bytes": int(main_bytes),
+                "kernel": ("cascade launch (prefix pass + decode rows of the suffix pass)"
+                           if fused else "cascade suffix pass (decode rows)"),
+                "prefix_flops": W.prefix_flops(w),
+                "prefix_tflops_over_kernel_time":
+                    round(W.prefix_flops(w) / (kavg * 1e-3) / 1e12, 2) if kavg and fused else None}
+    elif w.cu_seqlens_q is None:
         # the partition kernel reads every KV token, q and the metadata; the
         # merge kernel writes out (charged to the merge, not here)
         main_bytes = B - out_bytes
@@ -407,6 +469,12 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if cascade:
+        rec["cascade"] = {"common_prefix_len": w.common_prefix_len,
+                          "plain_form_bytes": int(W.algorithmic_bytes(w, shared_prefix=False)),
+                          "plain_call_us_per_step": round(plain_us, 2) if plain_us else None,
+                          "speedup_over_plain_call": round(plain_us / (ms_per_step * 1e3), 2)
+                          if plain_us else None}
     del dw
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

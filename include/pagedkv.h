@@ -321,7 +321,9 @@ pkv_status pkv_validate_metadata(const int32_t* block_tables, int32_t max_blocks
  * Per-launch timing of the main attention kernel, for benchmarks.  With
  * every_n > 0, one attention call in every_n (the first, then every n-th)
  * records a pair of HIP events on its stream around its main kernel (the
- * decode partition kernel, or the prefill kernel of a varlen call); each
+ * decode partition kernel; for a varlen call the mixed or prefill launch,
+ * or the decode-row launch when every query range is one row; for a cascade
+ * call that of its suffix pass); each
  * record costs a few microseconds of stream time, so sampling keeps the
  * timed steps close to untimed ones.  every_n = 0 disables timing.
  * pkv_timing_read waits for the recorded events, writes up to `cap`

@@ -173,6 +173,10 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
 }
 
 pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
+  // with a single workgroup range per row (every partition of a row in one
+  // workgroup) the attention kernel wrote every row itself
+  const int max_ranges = a.partition_size > 0 ? (a.num_splits + a.parts_per_wg - 1) / a.parts_per_wg : 1;
+  if (max_ranges <= 1) return PKV_OK;
   if (pkv::launch_splitkv_reduce(a, dtype, head_size, st) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
@@ -292,12 +296,32 @@ AttnArgs base_args(void* out, const void* q, const pkv_kv_cache* cache,
 // ----------------------------------------------------------------- cascade
 // Prefix pass geometry: the query tiles and head groups of the prefill
 // kernel over all rows of the batch, and enough key partitions (of at least
-// kPrefixMinPart tokens, at most kMaxPrefixParts) to give about
-// kPrefixTargetWgs workgroups.  Depends only on the call's sizes, so the
-// workspace size is known without a device.
+// kPrefixMinPart tokens, at most kMaxPrefixParts) to give about target_wgs
+// workgroups.  Depends only on the call's sizes, so the workspace size is
+// known without a device; the workspace holds the partitions of the default
+// target, which the one-launch form's smaller target never exceeds.
 constexpr int32_t kMaxPrefixParts = 16;
 constexpr int32_t kPrefixMinPart = 256;
+// Target workgroups of the prefix pass: a launch of its own fills the chip;
+// beside the decode rows of the one-launch form fewer, longer items do
+// better (they share the chip with the decode rows, and fewer partitions
+// mean fewer fp32 partials to write and merge).  Measured on the 256-request
+// shared-prefix decode batch: 512 alone, 128 in the one-launch form.
 constexpr int64_t kPrefixTargetWgs = 512;
+constexpr int64_t kPrefixTargetWgsFused = 128;
+
+// A cascade whose rows are all decode rows runs the prefix pass and the
+// suffix pass as one persistent launch when the decode rows use the
+// matrix-core kernel.  PKV_CASCADE_FUSED=0 keeps separate launches (A/B runs).
+bool use_cascade_launch(const pkv_kv_cache* cache, int group) {
+  static const char* env = std::getenv("PKV_CASCADE_FUSED");
+  if (env && std::strcmp(env, "0") == 0) return false;
+  return use_mfma_decode(cache, group) && device_cus() > 0;
+}
+
+// Workgroups in four of the one-launch cascade that start on prefix items
+// (of 1, 2 and 3 tried, 1 was fastest).
+constexpr int32_t kCascadeShare = 1;
 
 struct PrefixGeometry {
   int32_t gc = 1;        // query heads per column group
@@ -308,7 +332,7 @@ struct PrefixGeometry {
 };
 
 PrefixGeometry prefix_geometry(int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
-                               int32_t cpl) {
+                               int32_t cpl, int64_t target_wgs = kPrefixTargetWgs) {
   PrefixGeometry g;
   if (cpl <= 0 || num_tokens <= 0) return g;
   const int group = num_heads / num_kv_heads;
@@ -320,7 +344,7 @@ PrefixGeometry prefix_geometry(int32_t num_tokens, int32_t num_heads, int32_t nu
   g.gy = (unsigned)(num_kv_heads * (group / gc));
   const int64_t base = (int64_t)g.qtiles * g.gy;
   const int64_t most = std::min<int64_t>(kMaxPrefixParts, (cpl + kPrefixMinPart - 1) / kPrefixMinPart);
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(most, (kPrefixTargetWgs + base - 1) / base));
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(most, (target_wgs + base - 1) / base));
   g.P = (int32_t)((((cpl + want - 1) / want) + 31) / 32 * 32);
   g.parts = (cpl + g.P - 1) / g.P;
   return g;
@@ -330,17 +354,20 @@ PrefixGeometry prefix_geometry(int32_t num_tokens, int32_t num_heads, int32_t nu
 // their lse [parts, heads, rows], the suffix pass's lse [rows, heads], then
 // the suffix pass's own split workspace.
 struct CascadeLayout {
-  size_t pre_o = 0, pre_lse = 0, suf_lse = 0, varlen = 0, total = 0;
+  size_t pre_o = 0, pre_lse = 0, suf_lse = 0, plan = 0, varlen = 0, total = 0;
 };
 
-CascadeLayout cascade_layout(const PrefixGeometry& g, int32_t num_tokens, int32_t num_heads,
-                             int32_t head_size, size_t varlen_bytes) {
+// ... then the plan of the one-launch form (sequence order [num_seqs] and two
+// work-queue counters), then the suffix pass's split workspace.
+CascadeLayout cascade_layout(const PrefixGeometry& g, int32_t num_seqs, int32_t num_tokens,
+                             int32_t num_heads, int32_t head_size, size_t varlen_bytes) {
   CascadeLayout l;
   const size_t rows = (size_t)g.parts * num_heads * num_tokens;
   l.pre_o = 0;
   l.pre_lse = rows * head_size * sizeof(float);
   l.suf_lse = align16(l.pre_lse + rows * sizeof(float));
-  l.varlen = align16(l.suf_lse + (size_t)num_tokens * num_heads * sizeof(float));
+  l.plan = align16(l.suf_lse + (size_t)num_tokens * num_heads * sizeof(float));
+  l.varlen = align16(l.plan + (size_t)(num_seqs + 2) * sizeof(int32_t));
   l.total = l.varlen + varlen_bytes;
   return l;
 }
@@ -413,6 +440,8 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     pkv::MixedGrid g{};
     g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
     g.pre_y = cache->num_kv_heads * (group / gc);
+    g.pre_z = 1;
+    g.pre_share = 3;
     g.dec_x = (int32_t)gx_d;
     g.dec_y = num_seqs;
     g.dec_z = (int32_t)gparts;
@@ -462,11 +491,15 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     if (timed) timing_end(s, tslot);
     if (st != PKV_OK) return st;
   }
-  // Sequences with one query row (decode rows), split over the key range.
+  // Sequences with one query row (decode rows), split over the key range;
+  // the main launch when the batch has no longer query ranges.
   a.mode = pkv::kModeVarlenOne;
   st = plan_seq_order(a, cache, workspace, s);
   if (st != PKV_OK) return st;
+  int tslot = 0;
+  const bool timed = max_query_len <= 1 && timing_begin(s, &tslot);
   st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
+  if (timed) timing_end(s, tslot);
   if (st != PKV_OK) return st;
   if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
   return st;
@@ -623,7 +656,7 @@ size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t
   if (vw == (size_t)-1) return vw;
   if (common_prefix_len == 0) return vw;
   const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, num_kv_heads, common_prefix_len);
-  return cascade_layout(g, num_tokens, num_heads, head_size, vw).total;
+  return cascade_layout(g, num_seqs, num_tokens, num_heads, head_size, vw).total;
 }
 
 const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int32_t num_tokens,
@@ -690,7 +723,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   if (vw == (size_t)-1) return PKV_ERR_SHAPE;
   const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, cache->num_kv_heads, cpl);
   if (g.parts < 1 || g.parts > kMaxPrefixParts || g.qtiles > (unsigned)INT32_MAX) return PKV_ERR_SHAPE;
-  const CascadeLayout lay = cascade_layout(g, num_tokens, num_heads, cache->head_size, vw);
+  const CascadeLayout lay = cascade_layout(g, num_seqs, num_tokens, num_heads, cache->head_size, vw);
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
@@ -707,20 +740,68 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   p.head_chunks_gc = g.gc;
   p.ws_o = reinterpret_cast<float*>(ws + lay.pre_o);
   p.ws_lse = reinterpret_cast<float*>(ws + lay.pre_lse);
-  if (pkv::launch_attn_mfma_prefix(p, cache->block_size, dim3(g.qtiles, g.gy, (unsigned)g.parts),
-                                   s) != hipSuccess)
-    return PKV_ERR_HIP;
-  // 2. suffix pass: each row against its own keys (from the prefix end on)
   float* lse_suffix = reinterpret_cast<float*>(ws + lay.suf_lse);
-  st = varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
-                   num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal, -1,
-                   partition_size, lse_suffix, vw ? ws + lay.varlen : nullptr, vw, stream, cpl);
-  if (st != PKV_OK) return st;
+  const int group = num_heads / cache->num_kv_heads;
+  if (max_query_len <= 1 && use_cascade_launch(cache, group)) {
+    // 1 + 2 in one persistent launch: prefix items on the matrix cores beside
+    // the decode rows of the suffix pass
+    const PrefixGeometry gf = prefix_geometry(num_tokens, num_heads, cache->num_kv_heads, cpl,
+                                              kPrefixTargetWgsFused);
+    p.partition_size = gf.P;
+    p.num_splits = gf.parts;
+    const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads, span,
+                                                partition_size);
+    const int32_t ns = num_splits_for(span, P);
+    if (P < 0) return PKV_ERR_SHAPE;
+    if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
+    AttnArgs d = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                           num_tokens, num_heads, max_seq_len, 1, scale, P, ns, lse_suffix,
+                           vw ? ws + lay.varlen : nullptr);
+    d.cu_seqlens_q = cu_seqlens_q;
+    d.mode = pkv::kModeVarlenOne;
+    d.causal = causal ? 1 : 0;
+    d.kv_start = cpl;
+    int32_t* plan = reinterpret_cast<int32_t*>(ws + lay.plan);
+    d.seq_order = plan;
+    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
+    pkv::MixedGrid mg{};
+    mg.pre_x = (int32_t)gf.qtiles;
+    mg.pre_y = (int32_t)gf.gy;
+    mg.pre_z = gf.parts;
+    mg.pre_share = kCascadeShare;
+    mg.dec_x = (int32_t)gx_d;
+    mg.dec_y = num_seqs;
+    mg.dec_z = (int32_t)gparts;
+    mg.n_dec = (int64_t)mg.dec_x * mg.dec_y * mg.dec_z;
+    mg.queues = plan + num_seqs;
+    mg.workgroups = 2 * device_cus();
+    if (mg.workgroups <= 0 || mg.n_dec >= (int64_t)INT32_MAX) return PKV_ERR_HIP;
+    if (pkv::launch_seq_order(seq_lens, num_seqs, max_seq_len, plan, nullptr, num_tokens, nullptr,
+                              nullptr, mg.queues, s) != hipSuccess)
+      return PKV_ERR_HIP;
+    int tslot = 0;
+    const bool timed = timing_begin(s, &tslot);
+    if (pkv::launch_attn_cascade(p, d, mg, cache->block_size, s) != hipSuccess) st = PKV_ERR_HIP;
+    if (timed) timing_end(s, tslot);
+    if (st != PKV_OK) return st;
+    if (ns > 1) st = launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+    if (st != PKV_OK) return st;
+  } else {
+    if (pkv::launch_attn_mfma_prefix(p, cache->block_size,
+                                     dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
+      return PKV_ERR_HIP;
+    // 2. suffix pass: each row against its own keys (from the prefix end on)
+    st = varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
+                     num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
+                     -1, partition_size, lse_suffix, vw ? ws + lay.varlen : nullptr, vw, stream,
+                     cpl);
+    if (st != PKV_OK) return st;
+  }
   // 3. merge of the two results, in place in out
   AttnArgs m = p;
   m.cu_seqlens_q = cu_seqlens_q;
   m.lse_out = lse_out;
-  if (pkv::launch_cascade_merge(m, lse_suffix, g.parts, s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, s) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 

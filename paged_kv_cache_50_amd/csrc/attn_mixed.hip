@@ -1,7 +1,10 @@
 // Mixed step in one launch: the chunked-prefill tiles and the decode rows of
 // a varlen batch run in one persistent grid (vLLM book, ch. 6 "Structure des
 // métadonnées": one forward over a batch that mixes prefill chunks and
-// decode rows).
+// decode rows).  The same grid runs a cascade whose rows are all decode
+// rows: the prefix pass on the matrix cores beside the suffix pass's decode
+// rows streaming each request's own keys (ch. 6 "forward()", the cascade
+// branch).
 //
 // The prefill tiles keep the matrix cores and vector ALUs busy while the
 // decode rows stream the cache from HBM, so the two kinds of work should
@@ -22,7 +25,10 @@ constexpr int kXcds = 8;
 constexpr int kLdsBytes = pf::kLdsBytes > dec::kLdsBytes ? pf::kLdsBytes : dec::kLdsBytes;
 static_assert(pf::kThreads == dec::kThreads, "one block shape");
 
-template <int BS>
+// CASCADE: the first kind of work is the cascade prefix pass (items = query
+// tile x head group x prefix partition, a fixed count) instead of the
+// listed prefill chunks.
+template <int BS, bool CASCADE>
 __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const AttnArgs pre,
                                                                        const AttnArgs dcd,
                                                                        const MixedGrid g) {
@@ -33,13 +39,15 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
 
   // prefill items of the listed multi-row sequences; decode items as in the
   // decode kernel's grid (kv-head chunk fastest, then row item, then range)
-  const int64_t n_pre = (int64_t)load_uniform_i32(g.pre_count, 0) * g.pre_x * g.pre_y;
+  const int64_t n_pre = CASCADE ? (int64_t)g.pre_x * g.pre_y * g.pre_z
+                               : (int64_t)load_uniform_i32(g.pre_count, 0) * g.pre_x * g.pre_y;
   const int64_t n_dec = g.n_dec;
-  // three workgroups in four start on the prefill queue, the fourth on the
-  // decode queue (of the splits tried, 1:1 and 1:3 were slower, and all on
-  // prefill first gave no overlap); a workgroup whose queue is empty moves
-  // to the other one, and stops when both are
-  int role = (blockIdx.x & 3) == 3 ? 1 : 0;
+  // pre_share workgroups in four start on the first queue, the others on
+  // the decode queue (for chunked prefill 3 of 4: of the splits tried, 1:1
+  // and 1:3 were slower, and all on prefill first gave no overlap); a
+  // workgroup whose queue is empty moves to the other one, and stops when
+  // both are
+  int role = (int)(blockIdx.x & 3) < g.pre_share ? 0 : 1;
   bool switched = false;
   while (true) {
     __syncthreads();                       // the previous item's LDS use is over
@@ -52,7 +60,13 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
       role ^= 1;
       continue;
     }
-    if (role == 0) {
+    if (role == 0 && CASCADE) {
+      const int bx = (int)(item % g.pre_x);
+      const int64_t t = item / g.pre_x;
+      const int by = (int)(t % g.pre_y);
+      const int part = (int)(t / g.pre_y);
+      pf::prefill_block<BS, true>(pre, bx, by, part, s_lds);
+    } else if (role == 0) {
       // the last query tiles of a chunk see the most keys: they go first
       const int bx = g.pre_x - 1 - (int)(item % g.pre_x);
       const int64_t t = item / g.pre_x;
@@ -69,19 +83,30 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   }
 }
 
+template <bool CASCADE>
+hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, int block_size,
+                  hipStream_t stream) {
+  if (g.workgroups <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)g.workgroups);
+  switch (block_size) {
+    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                              int block_size, hipStream_t stream) {
-  if (g.workgroups <= 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)g.workgroups);
-  switch (block_size) {
-    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
-    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
-    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch<false>(pre, dcd, g, block_size, stream);
+}
+
+hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
+                               int block_size, hipStream_t stream) {
+  return launch<true>(pre, dcd, g, block_size, stream);
 }
 
 }  // namespace pkv

@@ -120,6 +120,8 @@ hipError_t launch_seq_order(const int32_t* seq_lens, int32_t num_seqs, int32_t m
 struct MixedGrid {
   int64_t n_dec;                   // decode items: dec_x * dec_y * dec_z
   int32_t pre_x, pre_y;            // prefill items per listed sequence: query tiles x head groups
+  int32_t pre_z;                   // cascade: prefix partitions (items = pre_x * pre_y * pre_z)
+  int32_t pre_share;               // workgroups in four that start on the first queue
   int32_t dec_x, dec_y, dec_z;     // kv-head chunks, row items, key ranges
   int32_t workgroups;              // persistent grid size
   const int32_t* pre_list;         // [num_seqs] multi-row sequences (planner)
@@ -128,6 +130,10 @@ struct MixedGrid {
 };
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                              int block_size, hipStream_t stream);
+// The same persistent grid for a cascade of decode rows: prefix-pass items
+// (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`).
+hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
+                               int block_size, hipStream_t stream);
 
 // Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16, head
 // size 128): grid = (query tiles of 128 / head_chunks_gc rows over all

@@ -460,10 +460,12 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
 # Algorithmic byte and flop counts (what the method must move / compute).
 # --------------------------------------------------------------------------
 
-def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
+def algorithmic_bytes(w: Workload, include_write: bool = True, shared_prefix: bool = True) -> int:
     """KV bytes of every valid token read once, plus q, out, block-table
     entries and seq_lens; for a mixed step also the new K/V read and written
-    and the slot_mapping read."""
+    and the slot_mapping read.  A shared prefix (common_prefix_len > 0) is
+    counted once, as the cascade form reads it; shared_prefix=False counts it
+    once per sequence, as the plain form does."""
     e = w.elem_bytes
     L = w.seq_lens.astype(np.int64)
     if w.window_left >= 0 and w.cu_seqlens_q is None:
@@ -475,6 +477,12 @@ def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
     else:
         keys = L
         blocks = np.array([blocks_needed(x, w.block_size) for x in L], dtype=np.int64)
+    if shared_prefix and w.common_prefix_len > 0:
+        cpl = w.common_prefix_len
+        holders = int((L > 0).sum())
+        keys = np.append(keys - np.where(L > 0, cpl, 0), cpl if holders else 0)
+        blocks = np.append(blocks - np.where(L > 0, cpl // w.block_size, 0),
+                           cpl // w.block_size if holders else 0)
     kv = int(keys.sum()) * 2 * w.num_kv_heads * w.head_size * e
     qo = 2 * w.num_q_rows * w.num_heads * w.head_size * w.io_bytes
     meta = 4 * int(blocks.sum()) + 4 * w.num_seqs
@@ -487,6 +495,12 @@ def algorithmic_bytes(w: Workload, include_write: bool = True) -> int:
         T = int(w.slot_mapping.shape[0])
         total += 2 * T * w.num_kv_heads * w.head_size * (w.io_bytes + e) + 8 * T
     return total
+
+
+def prefix_flops(w: Workload) -> int:
+    """Flops of the cascade prefix pass: every query row against the shared
+    prefix (2 flops per multiply-add over QK^T and PV)."""
+    return 4 * w.num_q_rows * w.num_heads * w.head_size * int(w.common_prefix_len)
 
 
 def attention_flops(w: Workload) -> int:

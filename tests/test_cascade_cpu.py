@@ -61,7 +61,8 @@ def test_cascade_workspace_formula(L, S, T, Hq, Hkv, max_len, cpl, ps):
     a16 = lambda n: (n + 15) // 16 * 16
     rows = parts * Hq * T
     suf = a16(rows * D * 4 + rows * 4)
-    varlen = a16(suf + T * Hq * 4)
+    plan = a16(suf + T * Hq * 4)                     # sequence order + 2 queue counters
+    varlen = a16(plan + (S + 2) * 4)
     span = max_len - (cpl & ~31)
     vw = pagedkv.workspace_bytes(S, Hq, Hkv, D, span, ps)
     got = pagedkv.cascade_workspace_bytes(S, T, Hq, Hkv, D, max_len, cpl, ps)
