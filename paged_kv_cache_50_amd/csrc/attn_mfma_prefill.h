@@ -21,10 +21,13 @@
 // lane l's 16 bytes at offset 16*l, so the swizzled LDS layouts (16-byte slot
 // c ^ f(row)) are produced by choosing which chunk each lane fetches.  Tokens
 // past the key range load the last valid token (finite data; their
-// probabilities are exactly 0).  Per wave and tile:
+// probabilities are exactly 0).  Per wave and tile, every LDS read issued
+// first:
 //   S^T[32 tok x 16 rows] = K . Q^T        (8 A reads from LDS, 8 MFMAs per column tile)
 //   online softmax per column (= query row), causal mask by select
 //   O^T[128 x 16] += V^T . P^T             (V^T via ds_read_b64_tr_b16, shared by both tiles)
+// with the second column tile's exponentials interleaved between the first
+// tile's PV products (fenced, so that the VALU and matrix work overlap).
 // Tiles lying wholly above a wave's rows on the causal diagonal are skipped,
 // and masks are applied only to tiles that cross a diagonal or the range end.
 // The running max used as the exponent reference is raised only when a
@@ -47,6 +50,10 @@ namespace pf {
 constexpr int kWaves = 4;
 constexpr int kColTiles = 2 * kWaves;          // column tiles per workgroup
 constexpr float kRescaleSlack = 8.f;            // log2 of the largest unscaled probability
+// Initial exponent reference: a finite stand-in for -inf, far below any
+// logit, so that no step needs an infinity test (the first visible key
+// raises it; a column that sees no key keeps it and has sum 0)
+constexpr float kMinRef = -3.0e38f;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
 constexpr int kTile = 32;
@@ -55,6 +62,9 @@ constexpr int kVBytes = kTile * kD * 2;
 constexpr int kStageBytes = kKBytes + kVBytes;   // 16 KiB
 constexpr int kStages = 4;                       // LDS ring depth
 constexpr int kLdsBytes = kStages * kStageBytes;
+// A scheduling fence: the compiler moves no instruction across it, so code
+// written interleaved stays interleaved.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
@@ -67,6 +77,31 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_ca
 __device__ __forceinline__ int kslot(int t, int c) { return c ^ (t & 15); }
 __device__ __forceinline__ int vslot(int t, int c) { return c ^ ((t & 7) << 1); }
 __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (kslot(t, c) << 4); }
+
+// Transposed LDS read (ds_read_b64_tr_b16) written as inline asm.  Before
+// the intrinsic form the compiler waits for every outstanding direct-to-LDS
+// load, since it cannot tell which LDS bytes they write; here that would
+// drain the tile ring on every tile.  The reads of a tile are ordered after
+// its loads by each thread's own wait for them plus the barrier; their
+// results are waited for with lds_results_ready.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
+  return r;
+}
+// Waits for every outstanding LDS read, then marks the registers written so
+// that no use of them is scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_results_ready(u32x2 (&r)[N][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    asm volatile("" : "+v"(r[i][0]));
+    asm volatile("" : "+v"(r[i][1]));
+  }
+}
 
 // NaN-propagating max (v_maximum3_f32): unlike fmaxf it needs no
 // canonicalisation of its operands.
@@ -182,7 +217,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) o[c][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[c] = -INFINITY;
+    m[c] = kMinRef;
     lsum[c] = 0.f;
   }
 
@@ -200,33 +235,67 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int64_t max_blk = a.num_blocks - 1;
   const int last_tok = max(0, kv_end - 1);
 
-  // block offsets of tile t's two 16-token halves for this wave (scalar
-  // loads, fetched one iteration before they are used)
-  auto fetch_ids = [&](int t, int64_t* ids) {
+  // block ids of tile t's two 16-token halves for this wave (scalar loads,
+  // fetched one iteration before they are used; the arithmetic on them waits
+  // until then, so the load's latency hides behind a tile of work)
+  auto fetch_ids = [&](int t, int32_t* raw) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tw = min(t * kTile + 16 * u + 4 * wave, last_tok);       // wave's first token
       const int bi = __builtin_amdgcn_readfirstlane(tw / BS);
-      ids[u] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * a.block_stride;
+      raw[u] = load_uniform_i32(bt, bi);
     }
   };
+  // lane part (bytes) of the loads of a tile inside the key range: token
+  // t * 32 + r sits at offset r % BS of its block (32 is a multiple of BS)
+  uint32_t klane[2], vlane[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * u + lrow;
+    const uint32_t lo = (uint32_t)(r % BS) * tok_stride + head_off;
+    klane[u] = (lo + kslot(r, lslot) * 8) * 2;   // slot s holds chunk s ^ f(r): involution
+    vlane[u] = (lo + vslot(r, lslot) * 8) * 2;
+  }
   // issue the direct-to-LDS loads of tile t into stage buf (4 per thread);
-  // tokens clamped to the last valid one stay in the block of the wave's
-  // first token
-  auto issue = [&](int t, const int64_t* ids, char* buf) {
+  // in the last, partial tile tokens past the range are clamped to the last
+  // valid one, which stays in the block of the wave's first token
+  auto issue = [&](int t, const int32_t* raw, char* buf) {
+    const bool full = (t + 1) * kTile <= kv_end;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int r = 16 * u + lrow;
-      const int tok = min(t * kTile + r, last_tok);
-      const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off;
-      const int kch = kslot(r, lslot);   // slot s holds chunk s ^ f(r): involution
-      const int vch = vslot(r, lslot);
+      const int64_t boff = min((int64_t)max(raw[u], 0), max_blk) * a.block_stride * 2;
+      const char* kb = reinterpret_cast<const char*>(kc) + boff;
+      const char* vb = reinterpret_cast<const char*>(vc) + boff;
       char* kdst = buf + u * 4096 + wave * 1024;
       char* vdst = buf + kKBytes + u * 4096 + wave * 1024;
-      __builtin_amdgcn_global_load_lds(kc + ids[u] + lo + kch * 8, (lds_void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vc + ids[u] + lo + vch * 8, (lds_void*)vdst, 16, 0, 0);
+      if (full) {
+        __builtin_amdgcn_global_load_lds(kb + klane[u], (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + vlane[u], (lds_void*)vdst, 16, 0, 0);
+      } else {
+        const int r = 16 * u + lrow;
+        const int tok = min(t * kTile + r, last_tok);
+        const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off;
+        __builtin_amdgcn_global_load_lds(kb + (lo + kslot(r, lslot) * 8) * 2, (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + (lo + vslot(r, lslot) * 8) * 2, (lds_void*)vdst, 16, 0, 0);
+      }
     }
   };
+
+  // LDS read offsets of this lane inside a stage: K chunk 4j + kg of row n
+  // (row n + 16 adds 4096 B); V rows t0 = 4kg + n/4 (and t0 + 16, + 4096 B)
+  // for dims 16jd + 4(n%4) .. +3, i.e. half (n%4)&1 of chunk 2jd + (n%4)/2
+  uint32_t koff[4], voff[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = ktile_off(n, 4 * j + kg);
+  {
+    const int jj = n >> 2, q4 = n & 3;
+    const int t0 = 4 * kg + jj;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const int ch = 2 * jd + (q4 >> 1);
+      voff[jd] = kKBytes + t0 * (kD * 2) + (vslot(t0, ch) << 4) + (q4 & 1) * 8;
+    }
+  }
 
   // MASKED: the tile may hold keys past a row's causal limit or the range
   // end, or lie wholly above this wave's rows (skipped).
@@ -235,77 +304,104 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     const int j0 = t * kTile;
     // wholly above this wave's diagonal, or below its window
     if (MASKED && (j0 > wave_last_pos || j0 + kTile - 1 < wave_first_key)) return;
-    const char* kl = buf;
-    const char* vl = buf + kKBytes;
+    // every LDS read of the tile issued up front: K chunks for the A
+    // operands, then the transposed V rows (waited for before the first PV
+    // product)
+    bf16x8_t ka[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ka[tt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + koff[j] + tt * 4096));
+    const uint32_t vbase = (uint32_t)(uintptr_t)(lds_void*)buf;
+    u32x2 vr[8][2];
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      vr[jd][0] = ds_read_tr16_b64<0>(vbase + voff[jd]);
+      vr[jd][1] = ds_read_tr16_b64<16 * kD * 2>(vbase + voff[jd]);
+    }
+    // S^T = K Q^T for both column tiles
     f32x4 sacc[2][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) sacc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < 2; ++tt) {
+        sacc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + ktile_off(tt * 16 + n, 4 * j + kg)));
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[c][j], sacc[c][tt], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][j], qb[c][j], sacc[c][tt], 0, 0, 0);
       }
-    bf16x8_t pb[2];
+    // masked raw logits (the scale is applied inside the exponent), row
+    // maxima and the reference decisions of both column tiles
+    float s[2][8], mn[2];
+    bool raise[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qpos = rowb[c] + n + off;            // this lane's column = query row
       const int lim = causal ? min(qpos, kv_end - 1)
                               : (win >= 0 ? min(qpos + win, kv_end - 1) : kv_end - 1);
       const int lo = max(win >= 0 ? qpos - win : 0, key_lo);
-      // raw logits; the scale is applied inside the exponent (one FMA)
-      float s[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = j0 + tt * 16 + 4 * kg + i;
-          s[tt * 4 + i] = (!MASKED || (j <= lim && j >= lo)) ? sacc[c][tt][i] : -INFINITY;
+          s[c][tt * 4 + i] = (!MASKED || (j <= lim && j >= lo)) ? sacc[c][tt][i] : -INFINITY;
         }
-      float mx = vmax(vmax(vmax(s[0], s[1]), vmax(s[2], s[3])), vmax(vmax(s[4], s[5]), vmax(s[6], s[7])));
+      float mx = vmax(vmax(vmax(s[c][0], s[c][1]), vmax(s[c][2], s[c][3])),
+                      vmax(vmax(s[c][4], s[c][5]), vmax(s[c][6], s[c][7])));
       mx = xmax16_32(mx) * a.scale_log2;             // scale > 0 preserves the max
-      // raise the reference only when the max outgrows it by the slack; the
-      // accumulators are then rescaled (alpha = 1 for columns that keep it)
-      const bool raise = mx > m[c] + kRescaleSlack;
-      const float mn = raise ? mx : m[c];
-      const float alpha = (m[c] == -INFINITY) ? 0.f : fast_exp2(m[c] - mn);
-      m[c] = mn;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      // raise the reference only when the max outgrows it by the slack
+      raise[c] = mx > m[c] + kRescaleSlack;
+      mn[c] = raise[c] ? mx : m[c];
+    }
+    // rescale the accumulators of the columns whose reference rose (alpha
+    // = 2^0 = 1 for the others; the reference starts at kMinRef, so a first
+    // raise gives alpha = 0)
+    if (__builtin_amdgcn_ballot_w64(raise[0] || raise[1])) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float alpha = fast_exp2(m[c] - mn[c]);
         lsum[c] *= alpha;
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
       }
-      const float mref = (m[c] == -INFINITY) ? 0.f : m[c];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(fmaf(s[e], a.scale_log2, -mref));
-        psum += p;
-        pb[c][e] = (__bf16)p;
-      }
-      lsum[c] += psum;
     }
-    // lane (kg, n) reads 8 bytes of row 4kg + n/4 (and row + 16): dims
-    // 16jd + 4(n%4) .. +3, i.e. half (n%4)&1 of chunk 2jd + (n%4)/2
-    const int jj = n >> 2, q4 = n & 3;
-    const int t0 = 4 * kg + jj, t1 = t0 + 16;
+    m[0] = mn[0];
+    m[1] = mn[1];
+    // probabilities and O^T += V^T P^T: the first column tile's
+    // exponentials, then its eight products, each followed (in program
+    // order, fenced so that the compiler keeps it) by one exponential of the
+    // second column tile, whose products come last
+    bf16x8_t pb0, pb1;
+    float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(fmaf(s[0][e], a.scale_log2, -m[0]));
+      psum0 += p;
+      pb0[e] = (__bf16)p;
+    }
+    lsum[0] += psum0;
+    lds_results_ready(vr);
+    bf16x8_t va[8];
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
-      const int ch = 2 * jd + (q4 >> 1);
-      const char* p0 = vl + t0 * (kD * 2) + (vslot(t0, ch) << 4) + (q4 & 1) * 8;
-      const char* p1 = vl + t1 * (kD * 2) + (vslot(t1, ch) << 4) + (q4 & 1) * 8;
-      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
-      bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        o[c][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[c], o[c][jd], 0, 0, 0);
+      const u32x4 w = {vr[jd][0][0], vr[jd][0][1], vr[jd][1][0], vr[jd][1][1]};
+      va[jd] = as_bf16x8(w);
     }
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      sched_fence();
+      o[0][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb0, o[0][jd], 0, 0, 0);
+      const float p = fast_exp2(fmaf(s[1][jd], a.scale_log2, -m[1]));
+      psum1 += p;
+      pb1[jd] = (__bf16)p;
+    }
+    sched_fence();
+    lsum[1] += psum1;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd)
+      o[1][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb1, o[1][jd], 0, 0, 0);
   };
 
   // LDS ring: tile t lives in stage t % kStages.  Before computing tile t a
@@ -313,7 +409,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // tiles may stay in flight), then the barrier makes t visible to all and
   // guarantees every wave has finished tile t - 1, whose stage is refilled.
   constexpr int kLoadsPerTile = 4;
-  int64_t ids[2];
+  int32_t ids[2];
 #pragma unroll
   for (int t = t_begin; t < t_begin + kStages - 1; ++t)
     if (t < ntiles) {
@@ -333,11 +429,11 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     const int tn = t + kStages - 1;
-    if (tn < ntiles) {
-      issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
-      if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
-    }
+    if (tn < ntiles) issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
     compute(t, s_lds + (t % kStages) * kStageBytes, masked_tag);
+    // the next tile's block ids: loaded after this tile's LDS reads, so that
+    // their waits do not include the scalar loads
+    if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
   };
   // Tiles wholly at or below the workgroup's first row position and inside
   // the key range need no mask for any wave; the rest (the diagonal band and
