@@ -228,6 +228,10 @@ int32_t device_cus() {
   return cus[dev];
 }
 
+// XCDs in four (by workgroup index) that start the mixed launch on prefill
+// tiles: 2 (of 1-3 tried, with roles per XCD or inside each XCD).
+constexpr int32_t kMixedShare = 2;
+
 // Mixed batches (prefill chunks and decode rows) run as one interleaved
 // launch when both kinds use the matrix-core kernels and a split workspace
 // holds the planner's lists.  PKV_MIXED=0 keeps two launches (A/B runs).
@@ -319,8 +323,8 @@ bool use_cascade_launch(const pkv_kv_cache* cache, int group) {
   return use_mfma_decode(cache, group) && device_cus() > 0;
 }
 
-// Workgroups in four of the one-launch cascade that start on prefix items
-// (of 1, 2 and 3 tried, 1 was fastest).
+// XCDs in four (by workgroup index) that start the one-launch cascade on
+// prefix items (of 1 and 2 tried, 1 was faster).
 constexpr int32_t kCascadeShare = 1;
 
 struct PrefixGeometry {
@@ -441,7 +445,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
     g.pre_y = cache->num_kv_heads * (group / gc);
     g.pre_z = 1;
-    g.pre_share = 3;
+    g.pre_share = kMixedShare;
     g.dec_x = (int32_t)gx_d;
     g.dec_y = num_seqs;
     g.dec_z = (int32_t)gparts;

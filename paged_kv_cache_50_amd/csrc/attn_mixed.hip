@@ -42,11 +42,13 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   const int64_t n_pre = CASCADE ? (int64_t)g.pre_x * g.pre_y * g.pre_z
                                : (int64_t)load_uniform_i32(g.pre_count, 0) * g.pre_x * g.pre_y;
   const int64_t n_dec = g.n_dec;
-  // pre_share workgroups in four start on the first queue, the others on
-  // the decode queue (for chunked prefill 3 of 4: of the splits tried, 1:1
-  // and 1:3 were slower, and all on prefill first gave no overlap); a
-  // workgroup whose queue is empty moves to the other one, and stops when
-  // both are
+  // Workgroup i runs on XCD i % 8, so its start role follows its XCD: the
+  // XCDs with i % 4 < pre_share start on the first queue, the others on the
+  // decode queue.  Whole XCDs per role keep each kind's data in its own L2s,
+  // and i % 4 spreads both kinds over the two halves of the chip (XCDs 0-3
+  // and 4-7); an uneven spread, or roles mixed inside each XCD, measured
+  // slower.  A workgroup whose queue is empty moves to the other one, and
+  // stops when both are.
   int role = (int)(blockIdx.x & 3) < g.pre_share ? 0 : 1;
   bool switched = false;
   while (true) {
