@@ -233,8 +233,9 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
  *                  block_tables will do)
  *   other arguments as for pkv_paged_attention_varlen
  *   workspace      >= pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned
- * Needs a bfloat16 cache with head_size 128 (PKV_ERR_UNSUPPORTED otherwise);
- * common_prefix_len 0 is the plain varlen call.  Asynchronous on `stream`.
+ * Needs a bfloat16 or fp8 (e4m3) cache with head_size 128
+ * (PKV_ERR_UNSUPPORTED otherwise); common_prefix_len 0 is the plain varlen
+ * call.  Asynchronous on `stream`.
  * The suffix result is rounded to bfloat16 before the merge, as the output of
  * the pages' suffix call is; the prefix partials stay fp32.
  */

@@ -84,10 +84,13 @@ bool use_mfma_decode(const pkv_kv_cache* c, int group) {
   return group >= kMfmaMinGroup;
 }
 
-// Prefill kernel choice: the matrix-core kernel for bfloat16 / head 128;
-// PKV_PREFILL_KERNEL=valu forces the generic row kernel (A/B measurements).
+// Prefill kernel choice: the matrix-core kernel for bfloat16 or e4m3 caches
+// with head 128 (the only prefill kernel for e4m3); PKV_PREFILL_KERNEL=valu
+// forces the generic row kernel for bfloat16 (A/B measurements).
 bool use_mfma_prefill(const pkv_kv_cache* c) {
-  if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
+  if (c->head_size != 128) return false;
+  if (c->dtype == PKV_FP8_E4M3) return true;
+  if (c->dtype != PKV_BF16) return false;
   static const char* force = std::getenv("PKV_PREFILL_KERNEL");
   return !(force && std::strcmp(force, "valu") == 0);
 }
@@ -320,7 +323,7 @@ constexpr int64_t kPrefixTargetWgsFused = 128;
 bool use_cascade_launch(const pkv_kv_cache* cache, int group) {
   static const char* env = std::getenv("PKV_CASCADE_FUSED");
   if (env && std::strcmp(env, "0") == 0) return false;
-  return use_mfma_decode(cache, group) && device_cus() > 0;
+  return !is_fp8(cache) && use_mfma_decode(cache, group) && device_cus() > 0;
 }
 
 // XCDs in four (by workgroup index) that start the one-launch cascade on
@@ -396,8 +399,6 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
-  // fp8 caches have the one-row (decode) kernel only
-  if (is_fp8(cache) && max_query_len > 1) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
@@ -485,7 +486,8 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
       for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
         r.z_base = (int32_t)z0;
         const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, num_seqs - z0);
-        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, dim3(qtiles, gy, gz), s) != hipSuccess)
+        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, is_fp8(cache), dim3(qtiles, gy, gz),
+                                          s) != hipSuccess)
           st = PKV_ERR_HIP;
       }
     } else {
@@ -666,8 +668,8 @@ size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t
 const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int32_t num_tokens,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                int32_t dtype, int32_t window_left) {
-  if (dtype != PKV_BF16 || head_size != 128)
-    return "cascade attention needs bfloat16 caches with head_size 128";
+  if ((dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) || head_size != 128)
+    return "cascade attention needs bfloat16 or fp8 caches with head_size 128";
   if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
     return "num_heads must be a positive multiple of num_kv_heads";
   if (window_left >= 0) return "sliding-window attention does not use the cascade";
@@ -680,7 +682,7 @@ const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int3
   // max(requests x prefix bytes / HBM, flops / MFMA).  The cascade streams it
   // once, does the same flops on the matrix cores, and writes and reads the
   // fp32 partials: max(prefix bytes / HBM, flops / MFMA) + partials / HBM.
-  const double kv_bytes = 2.0 * common_prefix_len * num_kv_heads * head_size * 2;
+  const double kv_bytes = 2.0 * common_prefix_len * num_kv_heads * head_size * elem_bytes(dtype);
   const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, num_kv_heads, common_prefix_len);
   const double partial_bytes = 2.0 * g.parts * num_heads * (double)num_tokens * (head_size + 1) * 4;
   const double flops = 4.0 * num_tokens * num_heads * (double)head_size * common_prefix_len;
@@ -707,7 +709,8 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
-  if (cache->dtype != PKV_BF16 || cache->head_size != 128) return PKV_ERR_UNSUPPORTED;
+  if ((cache->dtype != PKV_BF16 && cache->dtype != PKV_FP8_E4M3) || cache->head_size != 128)
+    return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   const int32_t cpl = common_prefix_len;
   if (cpl < 0 || cpl % cache->block_size != 0 || cpl > max_seq_len ||
@@ -791,7 +794,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     if (ns > 1) st = launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
     if (st != PKV_OK) return st;
   } else {
-    if (pkv::launch_attn_mfma_prefix(p, cache->block_size,
+    if (pkv::launch_attn_mfma_prefix(p, cache->block_size, is_fp8(cache),
                                      dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
       return PKV_ERR_HIP;
     // 2. suffix pass: each row against its own keys (from the prefix end on)

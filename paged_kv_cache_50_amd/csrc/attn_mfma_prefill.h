@@ -62,6 +62,12 @@ constexpr int kVBytes = kTile * kD * 2;
 constexpr int kStageBytes = kKBytes + kVBytes;   // 16 KiB
 constexpr int kStages = 4;                       // LDS ring depth
 constexpr int kLdsBytes = kStages * kStageBytes;
+// fp8 caches: a ring of kStages stages of codes (K rows of 128 B, then V
+// rows), then two bfloat16 tiles laid out as the stages above
+constexpr int kKBytes8 = kTile * kD;             // 4 KiB
+constexpr int kStageBytes8 = 2 * kKBytes8;       // 8 KiB
+constexpr int kRingBytes8 = kStages * kStageBytes8;
+static_assert(kRingBytes8 + 2 * kStageBytes <= kLdsBytes, "fp8 layout fits the LDS of a workgroup");
 // A scheduling fence: the compiler moves no instruction across it, so code
 // written interleaved stays interleaved.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -126,7 +132,13 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // the batch, the keys are partition `seq` (partition_size tokens) of the
 // shared prefix read through block_tables row 0, no mask applies, and the
 // result is a normalised fp32 partial with its log2-domain log-sum-exp.
-template <int BS, bool PREFIX = false>
+// FP8: e4m3 caches.  The tile loads bring the codes into a ring of 8 KiB
+// stages (K rows of 128 B, then V rows); each step the workgroup converts
+// the next tile exactly to bfloat16 into one of two 16 KiB tiles laid out
+// as the bfloat16 stages are (each thread converts the 16 + 16 codes it
+// loaded itself), and the products read those.  The per-kv-head k_scale is
+// folded into the logit scale and v_scale into the output.
+template <int BS, bool PREFIX = false, bool FP8 = false>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
   int qs, q_len, L, off;
@@ -153,6 +165,10 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int chunks = group / GC;
   const int kvh = by / chunks;
   const int hbase = kvh * group + (by % chunks) * GC;
+  // logit scale (log2 domain) and output scale: the fp8 cache's per-head
+  // scales fold into them
+  const float sl2 = FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float oscale = FP8 ? a.v_scale[kvh] : 1.f;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,49 +244,68 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int lrow = tid >> 4;
   const int lslot = tid & 15;
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
-  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v_cache);
+  const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
+  const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
+  // token row and head offsets in elements (bfloat16) or bytes (fp8)
   const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
   const uint32_t head_off = (uint32_t)kvh * kD;
   const int64_t max_blk = a.num_blocks - 1;
   const int last_tok = max(0, kv_end - 1);
 
-  // block ids of tile t's two 16-token halves for this wave (scalar loads,
-  // fetched one iteration before they are used; the arithmetic on them waits
-  // until then, so the load's latency hides behind a tile of work)
+  // block ids of tile t's token groups for this wave (two 16-token halves;
+  // fp8: one group of 8 tokens), as scalar loads fetched one iteration
+  // before they are used; the arithmetic on them waits until then, so the
+  // load's latency hides behind a tile of work
   auto fetch_ids = [&](int t, int32_t* raw) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tw = min(t * kTile + 16 * u + 4 * wave, last_tok);       // wave's first token
+    for (int u = 0; u < (FP8 ? 1 : 2); ++u) {
+      const int tw = min(t * kTile + (FP8 ? 8 * wave : 16 * u + 4 * wave), last_tok);
       const int bi = __builtin_amdgcn_readfirstlane(tw / BS);
       raw[u] = load_uniform_i32(bt, bi);
     }
   };
-  // lane part (bytes) of the loads of a tile inside the key range: token
-  // t * 32 + r sits at offset r % BS of its block (32 is a multiple of BS)
+  // bfloat16: load u (0, 1) of thread tid fills LDS row r = 16u + tid/16,
+  // slot tid%16, with the chunk of token r that belongs there (each wave
+  // covers 4 consecutive tokens per load, inside one block).  fp8: thread
+  // tid loads codes 16 (tid%8) .. +15 of token r = tid/8 (each wave covers 8
+  // consecutive tokens, inside one block), into the stage row r.
+  // Lane part (bytes) of the loads of a tile inside the key range: token
+  // t * 32 + r sits at offset r % BS of its block (32 is a multiple of BS).
+  constexpr int kEB = FP8 ? 1 : 2;                   // cache element bytes
   uint32_t klane[2], vlane[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int r = 16 * u + lrow;
-    const uint32_t lo = (uint32_t)(r % BS) * tok_stride + head_off;
-    klane[u] = (lo + kslot(r, lslot) * 8) * 2;   // slot s holds chunk s ^ f(r): involution
-    vlane[u] = (lo + vslot(r, lslot) * 8) * 2;
+    if constexpr (FP8) {
+      const int r = tid >> 3;
+      klane[u] = vlane[u] = ((uint32_t)(r % BS) * tok_stride + head_off) + (tid & 7) * 16;
+    } else {
+      const int r = 16 * u + lrow;
+      const uint32_t lo = (uint32_t)(r % BS) * tok_stride + head_off;
+      klane[u] = (lo + kslot(r, lslot) * 8) * 2;   // slot s holds chunk s ^ f(r): involution
+      vlane[u] = (lo + vslot(r, lslot) * 8) * 2;
+    }
   }
-  // issue the direct-to-LDS loads of tile t into stage buf (4 per thread);
-  // in the last, partial tile tokens past the range are clamped to the last
-  // valid one, which stays in the block of the wave's first token
+  // issue the direct-to-LDS loads of tile t into stage buf (4 per thread;
+  // fp8: 2); in the last, partial tile tokens past the range are clamped to
+  // the last valid one, which stays in the block of the wave's first token
   auto issue = [&](int t, const int32_t* raw, char* buf) {
     const bool full = (t + 1) * kTile <= kv_end;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t boff = min((int64_t)max(raw[u], 0), max_blk) * a.block_stride * 2;
+    for (int u = 0; u < (FP8 ? 1 : 2); ++u) {
+      const int64_t boff = min((int64_t)max(raw[u], 0), max_blk) * a.block_stride * kEB;
       const char* kb = reinterpret_cast<const char*>(kc) + boff;
       const char* vb = reinterpret_cast<const char*>(vc) + boff;
-      char* kdst = buf + u * 4096 + wave * 1024;
-      char* vdst = buf + kKBytes + u * 4096 + wave * 1024;
+      char* kdst = buf + (FP8 ? 0 : u * 4096) + wave * 1024;
+      char* vdst = buf + (FP8 ? kKBytes8 : kKBytes + u * 4096) + wave * 1024;
       if (full) {
         __builtin_amdgcn_global_load_lds(kb + klane[u], (lds_void*)kdst, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vb + vlane[u], (lds_void*)vdst, 16, 0, 0);
+      } else if constexpr (FP8) {
+        const int r = tid >> 3;
+        const int tok = min(t * kTile + r, last_tok);
+        const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off + (tid & 7) * 16;
+        __builtin_amdgcn_global_load_lds(kb + lo, (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + lo, (lds_void*)vdst, 16, 0, 0);
       } else {
         const int r = 16 * u + lrow;
         const int tok = min(t * kTile + r, last_tok);
@@ -278,6 +313,23 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
         __builtin_amdgcn_global_load_lds(kb + (lo + kslot(r, lslot) * 8) * 2, (lds_void*)kdst, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vb + (lo + vslot(r, lslot) * 8) * 2, (lds_void*)vdst, 16, 0, 0);
       }
+    }
+  };
+  // fp8: convert this thread's codes of the stage (K chunk pair and V chunk
+  // pair of token r = tid/8, dims 16 (tid%8) .. +15) into the bfloat16 tile
+  // dst, at the slots the bfloat16 layouts give them
+  auto convert = [&](const char* stage, char* dst) {
+    if constexpr (FP8) {
+      const int r = tid >> 3, c8 = tid & 7;
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(stage + tid * 16);
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(stage + kKBytes8 + tid * 16);
+      u32x4 k0, k1, v0, v1;
+      e4m3x16_to_bf16x16(kw, k0, k1);
+      e4m3x16_to_bf16x16(vw, v0, v1);
+      *reinterpret_cast<u32x4*>(dst + ktile_off(r, 2 * c8)) = k0;
+      *reinterpret_cast<u32x4*>(dst + ktile_off(r, 2 * c8 + 1)) = k1;
+      *reinterpret_cast<u32x4*>(dst + kKBytes + r * (kD * 2) + (vslot(r, 2 * c8) << 4)) = v0;
+      *reinterpret_cast<u32x4*>(dst + kKBytes + r * (kD * 2) + (vslot(r, 2 * c8 + 1) << 4)) = v1;
     }
   };
 
@@ -350,7 +402,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
         }
       float mx = vmax(vmax(vmax(s[c][0], s[c][1]), vmax(s[c][2], s[c][3])),
                       vmax(vmax(s[c][4], s[c][5]), vmax(s[c][6], s[c][7])));
-      mx = xmax16_32(mx) * a.scale_log2;             // scale > 0 preserves the max
+      mx = xmax16_32(mx) * sl2;             // scale > 0 preserves the max
       // raise the reference only when the max outgrows it by the slack
       raise[c] = mx > m[c] + kRescaleSlack;
       mn[c] = raise[c] ? mx : m[c];
@@ -377,7 +429,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(fmaf(s[0][e], a.scale_log2, -m[0]));
+      const float p = fast_exp2(fmaf(s[0][e], sl2, -m[0]));
       psum0 += p;
       pb0[e] = (__bf16)p;
     }
@@ -393,7 +445,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     for (int jd = 0; jd < 8; ++jd) {
       sched_fence();
       o[0][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb0, o[0][jd], 0, 0, 0);
-      const float p = fast_exp2(fmaf(s[1][jd], a.scale_log2, -m[1]));
+      const float p = fast_exp2(fmaf(s[1][jd], sl2, -m[1]));
       psum1 += p;
       pb1[jd] = (__bf16)p;
     }
@@ -404,33 +456,57 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
       o[1][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb1, o[1][jd], 0, 0, 0);
   };
 
-  // LDS ring: tile t lives in stage t % kStages.  Before computing tile t a
-  // thread waits for its own loads of t (the loads of up to kStages - 2 later
-  // tiles may stay in flight), then the barrier makes t visible to all and
-  // guarantees every wave has finished tile t - 1, whose stage is refilled.
-  constexpr int kLoadsPerTile = 4;
+  // LDS ring: tile t lives in stage t % kStages.  bfloat16: before
+  // computing tile t a thread waits for its own loads of t (the loads of up
+  // to kStages - 2 later tiles may stay in flight), then the barrier makes t
+  // visible to all and guarantees every wave has finished tile t - 1, whose
+  // stage is refilled.  fp8: at step t a thread waits for its own loads of
+  // tile t + 1 and for its conversion writes of tile t, the barrier makes
+  // the bfloat16 tile t visible and frees the bfloat16 tile of t - 1, into
+  // which the thread then converts its codes of t + 1.
+  constexpr int kLoadsPerTile = FP8 ? 2 : 4;
+  auto stage = [&](int t) { return s_lds + (t % kStages) * (FP8 ? kStageBytes8 : kStageBytes); };
+  auto tile = [&](int t) { return FP8 ? s_lds + kRingBytes8 + (t & 1) * kStageBytes : stage(t); };
   int32_t ids[2];
 #pragma unroll
   for (int t = t_begin; t < t_begin + kStages - 1; ++t)
     if (t < ntiles) {
       fetch_ids(t, ids);
-      issue(t, ids, s_lds + (t % kStages) * kStageBytes);
+      issue(t, ids, stage(t));
     }
   if (t_begin + kStages - 1 < ntiles) fetch_ids(t_begin + kStages - 1, ids);
+  if constexpr (FP8) {
+    if (t_begin < ntiles) {
+      const int ahead = min(kStages - 2, ntiles - 1 - t_begin);   // tiles issued after t_begin
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+      convert(stage(t_begin), tile(t_begin));
+    }
+  }
   auto step = [&](int t, auto masked_tag) {
-    const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    if constexpr (FP8) {
+      const int ahead = min(1, ntiles - 2 - t);           // tiles issued after t + 1
+      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this thread's conversion writes
+    } else {
+      const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
+    }
     // a bare barrier: __syncthreads() would add a fence that drains the
     // loads of the tiles still in flight.  Each thread has waited for its own
     // loads of tile t above; LDS reads of tile t - 1 were consumed before.
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    if constexpr (FP8)
+      if (t + 1 < ntiles) convert(stage(t + 1), tile(t + 1));
     const int tn = t + kStages - 1;
-    if (tn < ntiles) issue(tn, ids, s_lds + (tn % kStages) * kStageBytes);
-    compute(t, s_lds + (t % kStages) * kStageBytes, masked_tag);
+    if (tn < ntiles) issue(tn, ids, stage(tn));
+    compute(t, tile(t), masked_tag);
     // the next tile's block ids: loaded after this tile's LDS reads, so that
     // their waits do not include the scalar loads
     if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
@@ -455,7 +531,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     const float ls = xsum16_32(lsum[c]);
     const int row = rowb[c] + n;
     if (!live[c] || row >= q_len) continue;
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    const float inv = ls > 0.f ? oscale / ls : 0.f;
     if constexpr (PREFIX) {
       const int64_t e = ((int64_t)part * a.num_heads + head[c]) * a.num_tokens + row;
       float* op = a.ws_o + e * kD;

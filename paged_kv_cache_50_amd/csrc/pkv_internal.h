@@ -101,9 +101,10 @@ hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, bool fp8, 
                                    hipStream_t stream);
 
 // Chunked prefill on the matrix cores (rows of sequences with > 1 query
-// rows): bfloat16, head size 128.  grid = (query tiles of 128 / head_chunks_gc
-// rows, num_kv_heads * group / head_chunks_gc, sequences).
-hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, dim3 grid,
+// rows): bfloat16 (or e4m3 with fp8 = true) caches, head size 128.
+// grid = (query tiles of 128 / head_chunks_gc rows, num_kv_heads * group /
+// head_chunks_gc, sequences).
+hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
                                     hipStream_t stream);
 
 // Permutation of 0..num_seqs-1 ordering sequences longest first (one
@@ -135,12 +136,12 @@ hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const Mix
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                                int block_size, hipStream_t stream);
 
-// Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16, head
-// size 128): grid = (query tiles of 128 / head_chunks_gc rows over all
+// Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16 or
+// e4m3 caches, head size 128): grid = (query tiles of 128 / head_chunks_gc rows over all
 // num_tokens rows, num_kv_heads * group / head_chunks_gc, key partitions).
 // Writes normalised fp32 partials to ws_o [part][head][row][D] and their
 // log2-domain log-sum-exps to ws_lse [part][head][row].
-hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, dim3 grid,
+hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
                                    hipStream_t stream);
 
 // Cascade merge: out (the suffix result, in place) and its natural-log lse

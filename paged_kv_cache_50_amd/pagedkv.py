@@ -304,18 +304,19 @@ def cascade_reason(common_prefix_len, num_seqs, num_tokens, num_heads, num_kv_he
 def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
                       prefix_blocks, common_prefix_len: int, scale: float, max_query_len: int,
                       max_seq_len: int, causal: bool = True, partition_size: int = 0,
-                      workspace=None, lse_out=None):
+                      workspace=None, lse_out=None, k_scale=None, v_scale=None):
     """Cascade (shared-prefix) attention over a flattened batch (q/out
     [T, Hq, D]): the result of paged_attention_varlen on the same arguments,
     with the prefix blocks (int32 [common_prefix_len / block_size], shared
-    by every sequence's table) read once for the whole batch."""
+    by every sequence's table) read once for the whole batch.  fp8 caches
+    take k_scale / v_scale as in paged_attention_varlen."""
     _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, prefix_blocks, workspace, lse_out)
-    desc = cache_descriptor(k_cache, v_cache)
+    desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"),
                  (block_tables, "block_tables"), (prefix_blocks, "prefix_blocks")):
         _meta(t, n)
-    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != k_cache.dtype or out.dtype != q.dtype:
-        raise ValueError("q/out must be contiguous and in the cache dtype")
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dtype != _io_dtype(k_cache) or out.dtype != q.dtype:
+        raise ValueError("q/out must be contiguous and in the cache's input dtype")
     T, Hq, D = q.shape
     S = seq_lens.shape[0]
     if out.shape != q.shape or cu_seqlens_q.shape[0] != S + 1 or block_tables.shape[0] != S:

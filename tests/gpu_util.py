@@ -102,12 +102,14 @@ def run_cascade(dw: DevWorkload, partition_size=None, lse=True, write=True,
     ps = w.partition_size if partition_size is None else partition_size
     cpl = w.common_prefix_len if common_prefix_len is None else common_prefix_len
     if write and dw.slot_mapping is not None:
-        pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new, dw.slot_mapping)
+        pagedkv.kv_cache_write(dw.k_cache, dw.v_cache, dw.key_new, dw.value_new, dw.slot_mapping,
+                               k_scale=dw.k_scale, v_scale=dw.v_scale)
     pre = dw.prefix_blocks if dw.prefix_blocks is not None else dw.block_tables[0]
     pagedkv.cascade_attention(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q, dw.seq_lens,
                               dw.block_tables, pre, cpl, w.scale, w.max_query_len, w.max_seq_len,
                               causal=w.causal, partition_size=ps,
-                              lse_out=dw.lse if lse else None)
+                              lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
+                              v_scale=dw.v_scale)
     return dw.out
 
 

@@ -151,10 +151,93 @@ def test_fp8_varlen_decode_rows_with_write():
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "fp8 varlen rows")
 
 
-def test_fp8_prefill_rows_are_rejected():
-    from paged_kv_cache_50_amd import pagedkv
-    w = W.make_varlen("fp8_chunk", [10, 5], [3, 1], 8, 2, 128, 16, "fp8", seed=23)
+def _fp8_mixed(hq, hkv, bs, causal, seed, cpl=0):
+    rng = np.random.default_rng(seed)
+    ql = np.array([1] * 6 + [37, 150, 64, 3])
+    ctx = cpl + rng.integers(0, 400, size=len(ql))
+    return W.make_varlen("fp8_mixed", ctx, ql, hq, hkv, 128, bs, "fp8", seed, causal=causal,
+                         common_prefix_len=cpl)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8)])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_chunks(hq, hkv, bs, causal):
+    """Chunked prefill rows and decode rows over an fp8 cache, with the
+    quantising write of the new tokens first."""
+    w = _fp8_mixed(hq, hkv, bs, causal, 90 + hq + bs)
+    _announce(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} causal={causal}")
     dw = G.DevWorkload(w)
-    with pytest.raises(pagedkv.PagedKVError) as e:
-        G.run(dw, write=False)
-    assert e.value.status == 3
+    G.run(dw, partition_size=256)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 prefill {hq}/{hkv} bs={bs}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 prefill {hq}/{hkv} bs={bs}")
+
+
+def test_fp8_prefill_needle_bit_exact():
+    """q = 64 e0 and key 0 = 64 e0 (code 0x68, scale 1), every other key
+    orthogonal to e0: every prefill row sees key 0, whose probability is 1
+    while every other one underflows to 0, so each output row is that key's
+    value row times a power-of-two scale, exactly."""
+    w = W.make_varlen("fp8_pf_needle", [100, 260], [70, 130], 32, 8, 128, 16, "fp8", seed=33)
+    kc, vc = G.oracle_inputs(w)
+    import dataclasses
+    w = dataclasses.replace(w, k_cache=kc, v_cache=vc, slot_mapping=None, key_new=None,
+                            value_new=None)
+    w.k_scale = np.ones(8, dtype=np.float32)
+    w.v_scale = np.full(8, 2.0 ** -5, dtype=np.float32)
+    valid = w.valid_slot_mask()
+    w.k_cache[valid, :, 0] = 0
+    w.q[:] = 0
+    w.q[:, :, 0] = W.f32_to_bf16_bits(np.float32(64.0))
+    for s in range(2):
+        w.k_cache[w.block_tables[s, 0], 0, :, 0] = 0x68
+    _announce("fp8 prefill needle")
+    dw = G.DevWorkload(w)
+    G.run(dw, write=False)
+    out = G.dev_to_bits(dw.out)
+    for s in range(2):
+        blk = w.block_tables[s, 0]
+        for r in range(w.cu_seqlens_q[s], w.cu_seqlens_q[s + 1]):
+            for h in range(32):
+                v = oracle.e4m3_decode(w.v_cache[blk, 0, h // 4]) * 2.0 ** -5
+                assert np.array_equal(out[r, h], W.f32_to_bf16_bits(v.astype(np.float32))), (s, r, h)
+
+
+def test_fp8_prefill_equals_bf16_path_with_power_of_two_scales():
+    """Prefill chunks over the same values held as e4m3 codes with
+    power-of-two scales or as bfloat16: bit-identical outputs."""
+    import dataclasses
+    torch = G.torch()
+    w8 = _fp8_mixed(32, 8, 16, True, 95)
+    kc, vc = G.oracle_inputs(w8)
+    w8 = dataclasses.replace(w8, k_cache=kc, v_cache=vc, slot_mapping=None, key_new=None,
+                             value_new=None)
+    w8.k_scale = np.full(8, 2.0 ** -6, dtype=np.float32)
+    w8.v_scale = np.full(8, 2.0 ** -4, dtype=np.float32)
+    kb = W.f32_to_bf16_bits((oracle.e4m3_decode(w8.k_cache) * 2.0 ** -6).astype(np.float32))
+    vb = W.f32_to_bf16_bits((oracle.e4m3_decode(w8.v_cache) * 2.0 ** -4).astype(np.float32))
+    kb[w8.k_cache == 0x7F] = W.BF16_QNAN
+    vb[w8.v_cache == 0x7F] = W.BF16_QNAN
+    wb = dataclasses.replace(w8, dtype="bf16", k_cache=kb, v_cache=vb, k_scale=None, v_scale=None)
+    _announce("fp8 prefill vs bf16 identity")
+    d8, db = G.DevWorkload(w8), G.DevWorkload(wb)
+    G.run(d8, partition_size=256, write=False)
+    G.run(db, partition_size=256, write=False)
+    torch.cuda.synchronize()
+    # the decode rows take the grouped decode kernel in both cases; the
+    # prefill rows the matrix-core prefill kernel (fp8 and bf16 forms)
+    assert np.array_equal(G.dev_to_bits(d8.out), G.dev_to_bits(db.out))
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 8)])
+def test_fp8_cascade(hq, hkv):
+    """Cascade attention over an fp8 cache (prefix pass on the fp8 form of
+    the prefill body, suffix pass on the fp8 kernels) against the oracle."""
+    w = _fp8_mixed(hq, hkv, 16, True, 97, cpl=256)
+    _announce(f"fp8 cascade hq={hq} hkv={hkv}")
+    dw = G.DevWorkload(w)
+    G.run_cascade(dw)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 cascade {hq}/{hkv}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 cascade {hq}/{hkv}")
