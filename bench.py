@@ -13,7 +13,7 @@ rate against the MI355X peak, from per-launch HIP events recorded by the
 library inside the timed region; `cpu_baseline` times the fp64 CPU oracle on
 the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..9]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..10]
 """
 from __future__ import annotations
 
@@ -43,6 +43,7 @@ WORKLOAD_DESC = {
     7: "workload 3 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
     8: "workload 4 (same lengths and pool) with a 4096-key sliding window (window_left 4095)",
     9: "slot write + cascade attention: 256 decode requests sharing a 4096-token prefix, own context U[0,1023] + 1 new token, 32/8 heads, head 128, block 16, bf16, seed 5",
+    10: "workload 5 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
 }
 
 
@@ -208,7 +209,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)

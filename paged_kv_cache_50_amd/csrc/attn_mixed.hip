@@ -27,8 +27,9 @@ static_assert(pf::kThreads == dec::kThreads, "one block shape");
 
 // CASCADE: the first kind of work is the cascade prefix pass (items = query
 // tile x head group x prefix partition, a fixed count) instead of the
-// listed prefill chunks.
-template <int BS, bool CASCADE>
+// listed prefill chunks.  FP8: e4m3 caches (both kinds of work; used for
+// the cascade).
+template <int BS, bool CASCADE, bool FP8>
 __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const AttnArgs pre,
                                                                        const AttnArgs dcd,
                                                                        const MixedGrid g) {
@@ -67,33 +68,33 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int part = (int)(t / g.pre_y);
-      pf::prefill_block<BS, true>(pre, bx, by, part, s_lds);
+      pf::prefill_block<BS, true, FP8>(pre, bx, by, part, s_lds);
     } else if (role == 0) {
       // the last query tiles of a chunk see the most keys: they go first
       const int bx = g.pre_x - 1 - (int)(item % g.pre_x);
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int li = (int)(t / g.pre_y);
-      pf::prefill_block<BS>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
+      pf::prefill_block<BS, false, FP8>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
     } else {
       const int bx = (int)(item % g.dec_x);
       const int64_t t = item / g.dec_x;
       const int zi = (int)(t % g.dec_y);
       const int bz = (int)(t / g.dec_y);
-      dec::decode_block<BS, false>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
+      dec::decode_block<BS, FP8>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
     }
   }
 }
 
-template <bool CASCADE>
+template <bool CASCADE, bool FP8>
 hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, int block_size,
                   hipStream_t stream) {
   if (g.workgroups <= 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)g.workgroups);
+  const dim3 grid((unsigned)g.workgroups), block(dec::kThreads);
   switch (block_size) {
-    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
-    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
-    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE>), grid, dim3(dec::kThreads), 0, stream, pre, dcd, g); break;
+    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
+    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
+    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -103,12 +104,13 @@ hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, 
 
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                              int block_size, hipStream_t stream) {
-  return launch<false>(pre, dcd, g, block_size, stream);
+  return launch<false, false>(pre, dcd, g, block_size, stream);
 }
 
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                               int block_size, hipStream_t stream) {
-  return launch<true>(pre, dcd, g, block_size, stream);
+                               int block_size, bool fp8, hipStream_t stream) {
+  return fp8 ? launch<true, true>(pre, dcd, g, block_size, stream)
+             : launch<true, false>(pre, dcd, g, block_size, stream);
 }
 
 }  // namespace pkv

@@ -132,9 +132,10 @@ struct MixedGrid {
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
                              int block_size, hipStream_t stream);
 // The same persistent grid for a cascade of decode rows: prefix-pass items
-// (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`).
+// (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`);
+// bfloat16 or (fp8 = true) e4m3 caches.
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                               int block_size, hipStream_t stream);
+                               int block_size, bool fp8, hipStream_t stream);
 
 // Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16 or
 // e4m3 caches, head size 128): grid = (query tiles of 128 / head_chunks_gc rows over all

@@ -368,9 +368,10 @@ CONFIG_NAMES = {
     7: "gqa_decode_fp8",
     8: "long_context_sliding_window_decode_bf16",
     9: "shared_prefix_cascade_decode_bf16",
+    10: "mixed_chunked_prefill_decode_fp8",
 }
 
-DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3, 9: 5}   # 6, 7: the lengths and pools of 2, 3
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3, 9: 5, 10: 4}   # 6, 7: the lengths and pools of 2, 3
 
 
 def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
@@ -397,7 +398,7 @@ def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=No
 def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
                 max_len: Optional[int] = None, num_chunks: Optional[int] = None,
                 chunk_len: Optional[int] = None) -> Workload:
-    """Build workload `cfg` (1..9).  num_seqs / max_len / num_chunks /
+    """Build workload `cfg` (1..10).  num_seqs / max_len / num_chunks /
     chunk_len shrink it for quick parity runs; None keeps the full size."""
     if seed is None:
         seed = DEFAULT_SEEDS[cfg]
@@ -418,7 +419,8 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         L = config_lengths(4, meta, num_seqs, max_len)
         return make_decode(name, L, 64, 8, 128, 16, "bf16", seed, sigma=0.5,
                            partition_size=512, meta_rng=meta, root=root)
-    if cfg == 5:
+    if cfg in (5, 10):
+        # 10: the same step over an fp8 cache (same lengths and pool)
         nc = 4 if num_chunks is None else num_chunks
         cl = 512 if chunk_len is None else chunk_len
         nd = 128 if num_seqs is None else num_seqs
@@ -428,8 +430,8 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         dec_L = meta.integers(min(64, dec_hi), dec_hi, size=nd, endpoint=True)
         context = np.concatenate([ctx, dec_L - 1]).astype(np.int64)
         qlens = np.concatenate([np.full(nc, cl), np.ones(nd)]).astype(np.int64)
-        return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16", seed, causal=True,
-                           meta_rng=meta, root=root)
+        return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16" if cfg == 5 else "fp8",
+                           seed, causal=True, meta_rng=meta, root=root)
     if cfg == 8:
         # the shapes, lengths and pool of workload 4 with a 4096-key window
         L = config_lengths(4, meta, num_seqs, max_len)

@@ -72,14 +72,16 @@ def test_fp8_decode_small(cfg, ps):
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 config{cfg} ps={ps}")
 
 
-@pytest.mark.parametrize("cfg", [6, 7])
+@pytest.mark.parametrize("cfg", [6, 7, 10])
 def test_fp8_full_size_sampled(cfg):
     """Full-size fp8 workloads in the launch configuration the benchmark
     times; the oracle checks sampled (sequence, kv head) pairs."""
     w = W.make_config(cfg)
     rng = np.random.default_rng(cfg)
-    pairs = [(int(s), int(rng.integers(w.num_kv_heads))) for s in
-             rng.choice(w.num_seqs, size=min(12, w.num_seqs), replace=False)]
+    seqs = list(rng.choice(w.num_seqs, size=min(12, w.num_seqs), replace=False))
+    if cfg == 10:
+        seqs = [0, 1, 2, 3] + [s for s in seqs if s > 3][:8]     # every prefill chunk
+    pairs = [(int(s), int(rng.integers(w.num_kv_heads))) for s in seqs]
     _announce(f"fp8 config{cfg} full, {len(pairs)} sampled pairs")
     dw = G.DevWorkload(w)
     G.run(dw)
@@ -241,3 +243,19 @@ def test_fp8_cascade(hq, hkv):
     ref, ref_lse = G.reference(w)
     G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 cascade {hq}/{hkv}")
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 cascade {hq}/{hkv}")
+
+
+def test_fp8_cascade_decode_rows_one_launch():
+    """Decode rows only: the prefix pass and the suffix's decode rows share
+    one persistent launch over the fp8 cache."""
+    rng = np.random.default_rng(98)
+    n = 24
+    ctx = 512 + rng.integers(0, 300, size=n)
+    w = W.make_varlen("fp8_casc_dec", ctx, np.ones(n, dtype=np.int64), 32, 8, 128, 16, "fp8", 98,
+                      causal=True, common_prefix_len=512)
+    _announce("fp8 cascade decode rows")
+    dw = G.DevWorkload(w)
+    G.run_cascade(dw, partition_size=128)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", "fp8 cascade decode rows")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "fp8 cascade decode rows")
