@@ -26,11 +26,14 @@
 // consecutive key partitions); the grid puts ranges on its slowest axis so
 // that the workgroups of ranges a short sequence does not have are dispatched
 // last.  Either wave w owns partition w of a full 4-partition range, or the
-// waves take the range's 32-token tiles round-robin.  A wave copies its tile
-// from registers into its LDS area, issues the next tile's loads into the
-// same registers (block ids run one tile further ahead) and computes from LDS
-// while they are in flight; the 4 waves merge their softmax states through
-// LDS at the end and write the row, or the range's partial result.
+// waves take the range's 32-token tiles round-robin.  A wave copies its
+// tile's K rows from registers into its LDS area, issues the next tile's K
+// loads into the same registers, computes the logits; then does the same
+// with the V rows (in the same LDS area) and the PV product, so the next
+// tile's loads are in flight while it computes and the LDS of a workgroup
+// stays at 34 KiB (block ids run one tile further ahead).  The 4 waves merge
+// their softmax states through LDS at the end and write the row, or the
+// range's partial result.
 // Tokens past the partition end are loaded from an in-bounds slot of the last
 // valid block; their logits are replaced by -inf and their V rows by zeros
 // (select, never multiply), so stale NaNs in unused cache slots cannot reach
@@ -52,8 +55,11 @@ constexpr int kTile = 32;                 // tokens per wave step
 constexpr int kKTileBytes = kTile * kD * 2;
 constexpr int kVPitch = kD * 2 + 16;      // LDS bytes per V token row (padded)
 constexpr int kVTileBytes = kTile * kVPitch;
-constexpr int kWaveLds = kKTileBytes + kVTileBytes;
+// a wave stages a tile's K rows, computes the logits, then stages the V rows
+// in the same area: 8.5 KiB per wave, 34 KiB per workgroup
+constexpr int kWaveLds = kKTileBytes > kVTileBytes ? kKTileBytes : kVTileBytes;
 constexpr int kLdsBytes = kWaves * kWaveLds;
+static_assert(kWaveLds >= 16 * kD * 4, "the final merge stages [16 heads][D] floats per wave");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
@@ -158,7 +164,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int last_bi = (pend - 1) / BS;
 
   char* klds = s_lds + wave * kWaveLds;
-  char* vlds = klds + kKTileBytes;
+  char* vlds = klds;                                 // V rows replace the K rows
 
   // Block ids of one tile (wave uniform, scalar loads), fetched a step early.
   auto fetch_ids = [&](int tile, int64_t* ids) {
@@ -170,22 +176,40 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     }
   };
 
-  // K and V loads of one tile: kLoads + kLoads natural loads, each
-  // kRowsPerLoad whole token rows (row kRowsPerLoad * i + lrow, 16 bytes at
-  // lbyte).  Each such group of rows lies in one block.
-  auto issue = [&](const int64_t* ids, u32x4* K, u32x4* V) {
+  // K (or V) loads of one tile: kLoads natural loads, each kRowsPerLoad
+  // whole token rows (row kRowsPerLoad * i + lrow, 16 bytes at lbyte).  Each
+  // such group of rows lies in one block.
+  auto issue = [&](const char* cache, const int64_t* ids, u32x4* R) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int tok = kRowsPerLoad * i + lrow;
       const int64_t boff = ids[(kRowsPerLoad * i) / BS];
       const uint32_t lo = (uint32_t)(tok % BS) * tok_stride + head_off + lbyte;
-      K[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kc + boff + lo));
-      V[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vc + boff + lo));
+      R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cache + boff + lo));
     }
   };
 
-  // Stage a tile in LDS (V rows of tokens past the end become zeros).
-  auto stage = [&](int tile, const u32x4* K, const u32x4* V) {
+  // Stage a tile's K rows, or its V rows (those of tokens past the end
+  // become zeros), in the wave's LDS area.
+  auto stage_k = [&](const u32x4* K) {
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int tok = kRowsPerLoad * i + lrow;
+      if constexpr (FP8) {
+        // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
+        const int c = lane & 7;
+        u32x4 k0, k1;
+        e4m3x16_to_bf16x16(K[i], k0, k1);
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
+      } else {
+        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
+      }
+    }
+    __asm__ volatile("" ::: "memory");
+  };
+  auto stage_v = [&](int tile, const u32x4* V) {
     const int tbase = pstart + tile * kTile;
     const bool full = tbase + kTile <= pend && tbase >= pbegin;
     __asm__ volatile("" ::: "memory");
@@ -194,18 +218,13 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       const int tok = kRowsPerLoad * i + lrow;
       const bool dead = !full && (tbase + tok >= pend || tbase + tok < pbegin);
       if constexpr (FP8) {
-        // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
         const int c = lane & 7;
-        u32x4 k0, k1, v0, v1;
-        e4m3x16_to_bf16x16(K[i], k0, k1);
+        u32x4 v0, v1;
         e4m3x16_to_bf16x16(V[i], v0, v1);
         if (dead) v0 = v1 = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
         *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32) = v0;
         *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + c * 32 + 16) = v1;
       } else {
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
         u32x4 v = V[i];
         if (dead) v = u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + n * 16) = v;
@@ -214,8 +233,9 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     __asm__ volatile("" ::: "memory");
   };
 
-  // One staged tile of the online softmax: logits, running max/sum, PV.
-  auto compute = [&](int tile) {
+  // Logits of a tile whose K rows are staged, and the online softmax update:
+  // returns the probabilities (the B operand of the PV product).
+  auto logits = [&](int tile) {
     const int tbase = pstart + tile * kTile;
     const bool full = tbase + kTile <= pend && tbase >= pbegin;
 
@@ -258,9 +278,14 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     lsum = lsum * alpha + psum;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) o[jd] *= alpha;
+    __asm__ volatile("" ::: "memory");
+    return pb;
+  };
 
-    // O^T += V^T P^T, one 16-dim tile at a time; the transposed reads give
-    // lane (kg, n) V[4kg + jj][16jd + n] and V[16 + 4kg + jj][16jd + n].
+  // O^T += V^T P^T for a tile whose V rows are staged, one 16-dim tile at a
+  // time; the transposed reads give lane (kg, n) V[4kg + jj][16jd + n] and
+  // V[16 + 4kg + jj][16jd + n].
+  auto pv = [&](const bf16x8_t pb) {
     {
       const int jj = n >> 2, q4 = n & 3;
       const char* r0 = vlds + (4 * kg + jj) * kVPitch + q4 * 8;
@@ -276,10 +301,11 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     __asm__ volatile("" ::: "memory");
   };
 
-  // The tile stream of this wave.  Tile t is waited for and copied into LDS;
-  // the loads of the wave's next tile are then issued into the same
-  // registers and stay in flight while t is computed from LDS.  Block ids run
-  // one tile further ahead.  Either wave w owns partition w of the range
+  // The tile stream of this wave.  Tile t's K rows are waited for and
+  // copied into LDS, the next tile's K loads are issued into the same
+  // registers, the logits are computed; then the same for the V rows and the
+  // PV product.  Loads stay in flight while the wave computes, and block ids
+  // run one tile further ahead.  Either wave w owns partition w of the range
   // (long rows: waves never wait for each other), or the waves take the
   // range's tiles round-robin (short rows: every wave gets work).
   const int tpp = it.P / kTile;                      // tiles per partition (split rows)
@@ -297,17 +323,21 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   int64_t ids[kBlkPerTile];
   if (tile < tend) {
     fetch_ids(tile, ids);
-    issue(ids, kr, vr);
+    issue(kc, ids, kr);
+    issue(vc, ids, vr);
     if (tile + tstep < tend) fetch_ids(tile + tstep, ids);
   }
   while (tile < tend) {
-    stage(tile, kr, vr);
     const int nt = tile + tstep;
+    stage_k(kr);
+    if (nt < tend) issue(kc, ids, kr);
+    const bf16x8_t pb = logits(tile);
+    stage_v(tile, vr);
     if (nt < tend) {
-      issue(ids, kr, vr);
+      issue(vc, ids, vr);
       if (nt + tstep < tend) fetch_ids(nt + tstep, ids);
     }
-    compute(tile);
+    pv(pb);
     tile = nt;
   }
 

@@ -5,8 +5,11 @@
 namespace pkv {
 namespace {
 
+// Three workgroups per CU for fp8 caches (more loads in flight per CU for a
+// kernel that moves half the bytes per token; four measured slower), two for
+// bfloat16 (three would spill: measured slower).
 template <int BS, bool FP8>
-__global__ void __launch_bounds__(dec::kThreads, 2) attn_mfma_decode_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(dec::kThreads, FP8 ? 3 : 2) attn_mfma_decode_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char s_lds[dec::kLdsBytes];
   __shared__ float s_m[dec::kWaves][16];
   __shared__ float s_l[dec::kWaves][16];
