@@ -72,6 +72,7 @@ int64_t block_stride_elems(const pkv_kv_cache* c) {
 // head per kv head the work is a matrix-vector product and stays on the VALU.
 // PKV_DECODE_KERNEL=valu|mfma forces one variant (for A/B measurements).
 constexpr int kMfmaMinGroup = 4;
+constexpr int32_t kPlanMinSeqs = 64;
 constexpr int kMfmaTokensPerWg = 2048;
 constexpr int64_t kMfmaTargetWgs = 2048;   // about four rounds of 512 workgroup slots
 
@@ -147,6 +148,7 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // With the sequences ordered longest first, the last key ranges (which
     // only long sequences have) are dispatched first and the first ranges of
     // the shortest sequences last: close to longest-processing-time first.
+    // (Without the order, ranges last first measured slower.)
     a.range_desc = a.seq_order ? 1 : 0;
     const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
     const unsigned gparts = (gy + a.parts_per_wg - 1) / a.parts_per_wg;
@@ -200,13 +202,17 @@ int32_t* order_area(const AttnArgs& a, const pkv_kv_cache* cache, void* workspac
                                     order_offset(rows, cache->head_size));
 }
 
-// One-row decode launches with a split workspace order their sequences
-// longest first (the planner writes the order into the workspace).  With
+// One-row decode launches with a split workspace and at least
+// kPlanMinSeqs sequences order their sequences longest first (the planner
+// writes the order into the workspace).  With
 // `multi`, the planner also lists the multi-row sequences (mixed launch).
 pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspace,
                           hipStream_t st, bool multi = false) {
   if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads))
     return PKV_OK;
+  // with few sequences the planner's launch costs more than the order saves
+  // (C4's 8 sequences: the same step time; with a 4096-key window: 47 -> 42 us)
+  if (!multi && a.num_seqs < kPlanMinSeqs) return PKV_OK;
   int32_t* order = order_area(a, cache, workspace);
   if (pkv::launch_seq_order(a.seq_lens, a.num_seqs, a.max_seq_len, order,
                             multi ? a.cu_seqlens_q : nullptr, a.num_tokens,
