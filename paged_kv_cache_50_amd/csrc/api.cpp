@@ -75,6 +75,7 @@ constexpr int kMfmaMinGroup = 4;
 constexpr int32_t kPlanMinSeqs = 64;
 constexpr int kMfmaTokensPerWg = 2048;
 constexpr int64_t kMfmaTargetWgs = 2048;   // about four rounds of 512 workgroup slots
+constexpr int64_t kWgFixedTokens = 128;    // a workgroup's fixed cost in streamed tokens
 
 bool use_mfma_decode(const pkv_kv_cache* c, int group) {
   if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
@@ -121,20 +122,48 @@ pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_
 // in `a` for the split merge that follows), launches over all z.
 // Matrix-core decode launch geometry for gy partitions: sets head chunks,
 // partitions per workgroup and the range order in `a`; returns (gx, ranges).
+int32_t device_cus();
 std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cache* cache,
                                                    unsigned gy) {
   const int group = a.num_heads / cache->num_kv_heads;
   {
     a.head_chunks = (group + 15) / 16;
-    // Tokens one workgroup streams: about kMfmaTokensPerWg for large batches,
-    // fewer (down to 256) when the whole launch has too little work to give
-    // the 512 workgroup slots several rounds (few rows, or a short window).
+    // Tokens one workgroup streams.  The floor: the largest of 2048 .. 256
+    // that still gives the launch about kMfmaTargetWgs workgroups (several
+    // rounds of the workgroup slots; large batches keep 2048).  Above the
+    // floor, the candidate with the least estimated makespan wins: rounds of
+    // workgroup slots times (tokens per workgroup + a fixed cost of about
+    // four tiles), with every row at its longest visible range (the host
+    // does not read seq_lens).  It matters for small launches whose floor
+    // leaves a short last round: sliding-window decode of 8 sequences gets
+    // 320 workgroups of 1024 tokens instead of 576 of 512 (1.1 rounds of
+    // 512 slots): 42 -> 29 us.  (Searching below the floor as well measured
+    // slower on the large batches.)
     int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
                                          : a.max_seq_len;
     eff_len = std::max<int64_t>(1, std::min<int64_t>(eff_len, a.max_seq_len - a.kv_start));
-    const int64_t work = (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks * eff_len;
+    const int64_t streams = (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks;
     int tpw = kMfmaTokensPerWg;
-    while (tpw > 256 && work / tpw < kMfmaTargetWgs) tpw >>= 1;
+    while (tpw > 256 && streams * eff_len / tpw < kMfmaTargetWgs) tpw >>= 1;
+    if (a.partition_size > 0) {
+      const int P = a.partition_size;
+      const int64_t span = eff_len + 31;             // the range starts at a multiple of 32
+      const int64_t nparts = (span + P - 1) / P;
+      const int cus = device_cus() > 0 ? device_cus() : 256;
+      const int64_t slots = (int64_t)cus * (is_fp8(cache) ? 3 : 2);
+      int64_t best = -1;
+      const int floor_tpw = tpw;
+      for (int cand = kMfmaTokensPerWg; cand >= floor_tpw; cand >>= 1) {
+        const int ppw = (P <= cand / 4) ? 4 : std::max(1, cand / P);
+        const int64_t wgs = streams * ((nparts + ppw - 1) / ppw);
+        const int64_t tok = std::min<int64_t>((int64_t)ppw * P, span);
+        const int64_t est = (wgs + slots - 1) / slots * (tok + kWgFixedTokens);
+        if (best < 0 || est < best) {
+          best = est;
+          tpw = cand;
+        }
+      }
+    }
     // a workgroup streams about kMfmaTokensPerWg tokens: consecutive
     // partitions share its queries and block-table row, and its fixed cost
     // (queries, first loads, merge) is paid once per stream
