@@ -124,10 +124,22 @@ pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_
 // partitions per workgroup and the range order in `a`; returns (gx, ranges).
 int32_t device_cus();
 std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cache* cache,
-                                                   unsigned gy) {
+                                                   unsigned gy, bool two_heads_ok = false) {
   const int group = a.num_heads / cache->num_kv_heads;
   {
     a.head_chunks = (group + 15) / 16;
+    // e4m3 caches: a kv head's token row is 128 bytes, and whole 256-byte
+    // rows gather faster (a microbenchmark of the two patterns: +7-9 %), so
+    // each wave reads the rows of two adjacent kv heads when there is an
+    // even number of them and a single head chunk.  Measured: MHA decode at
+    // C2 shapes 200 -> 190 us; GQA decode at C3 shapes unchanged (twice the
+    // LDS per workgroup: two workgroups per CU instead of three).  Only for
+    // the decode kernel's own launch (the one-launch forms keep one head).
+    // PKV_FP8_PAIRS=0 keeps one head per wave (A/B runs).
+    static const char* pe = std::getenv("PKV_FP8_PAIRS");
+    const bool pairs_on = !(pe && std::strcmp(pe, "0") == 0);
+    a.heads_per_wave = (two_heads_ok && pairs_on && is_fp8(cache) && a.head_chunks == 1 &&
+                        cache->num_kv_heads % 2 == 0) ? 2 : 1;
     // Tokens one workgroup streams.  The floor: the largest of 2048 .. 256
     // that still gives the launch about kMfmaTargetWgs workgroups (several
     // rounds of the workgroup slots; large batches keep 2048).  Above the
@@ -142,18 +154,20 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
                                          : a.max_seq_len;
     eff_len = std::max<int64_t>(1, std::min<int64_t>(eff_len, a.max_seq_len - a.kv_start));
-    const int64_t streams = (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks;
-    int tpw = kMfmaTokensPerWg;
+    const int64_t streams =
+        (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks / a.heads_per_wave;
+    const int tpw_max = kMfmaTokensPerWg;
+    int tpw = tpw_max;
     while (tpw > 256 && streams * eff_len / tpw < kMfmaTargetWgs) tpw >>= 1;
     if (a.partition_size > 0) {
       const int P = a.partition_size;
       const int64_t span = eff_len + 31;             // the range starts at a multiple of 32
       const int64_t nparts = (span + P - 1) / P;
       const int cus = device_cus() > 0 ? device_cus() : 256;
-      const int64_t slots = (int64_t)cus * (is_fp8(cache) ? 3 : 2);
+      const int64_t slots = (int64_t)cus * (is_fp8(cache) && a.heads_per_wave == 1 ? 3 : 2);
       int64_t best = -1;
       const int floor_tpw = tpw;
-      for (int cand = kMfmaTokensPerWg; cand >= floor_tpw; cand >>= 1) {
+      for (int cand = tpw_max; cand >= floor_tpw; cand >>= 1) {
         const int ppw = (P <= cand / 4) ? 4 : std::max(1, cand / P);
         const int64_t wgs = streams * ((nparts + ppw - 1) / ppw);
         const int64_t tok = std::min<int64_t>((int64_t)ppw * P, span);
@@ -179,7 +193,7 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // the shortest sequences last: close to longest-processing-time first.
     // (Without the order, ranges last first measured slower.)
     a.range_desc = a.seq_order ? 1 : 0;
-    const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
+    const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks / a.heads_per_wave);
     const unsigned gparts = (gy + a.parts_per_wg - 1) / a.parts_per_wg;
     return {gx, gparts};
   }
@@ -189,7 +203,7 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
                           hipStream_t st) {
   const int group = a.num_heads / cache->num_kv_heads;
   if (use_mfma_decode(cache, group)) {
-    const auto [gx, gparts] = mfma_decode_geometry(a, cache, gy);
+    const auto [gx, gparts] = mfma_decode_geometry(a, cache, gy, true);
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);

@@ -59,6 +59,9 @@ constexpr int kVTileBytes = kTile * kVPitch;
 // in the same area: 8.5 KiB per wave, 34 KiB per workgroup
 constexpr int kWaveLds = kKTileBytes > kVTileBytes ? kKTileBytes : kVTileBytes;
 constexpr int kLdsBytes = kWaves * kWaveLds;
+// LDS of a workgroup whose waves cover HP kv heads each
+template <int HP>
+constexpr int kLdsBytesHp = HP * kLdsBytes;
 static_assert(kWaveLds >= 16 * kD * 4, "the final merge stages [16 heads][D] floats per wave");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -89,18 +92,27 @@ __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (
 // FP8: the caches hold e4m3 codes with per-kv-head scales; a token row is
 // then 128 bytes, read by 8 lanes, and converted (exactly) to bfloat16 while
 // it is staged in LDS, so the matrix-core part is the same.  The K scale is
-// folded into the logit scale and the V scale into the output.
-// One workgroup's work: kv-head chunk bx, row item zi (before the dispatch
-// order is applied), key range bz of nz.  The caller provides the LDS areas
-// (kLdsBytes, 16-byte aligned, and the two [kWaves][16] merge arrays).
-template <int BS, bool FP8>
+// folded into the logit scale and the V scale into the output.  With HP = 2
+// a wave serves two adjacent kv heads: one load covers 4 tokens' 256-byte
+// rows of both heads (16 lanes a row, the gather pattern of bfloat16 rows),
+// each lane converts into the K or V tile of its head, and the products and
+// softmax states run per head.
+// One workgroup's work: kv-head chunk bx (kv-head pair with HP = 2), row
+// item zi (before the dispatch order is applied), key range bz of nz.  The
+// caller provides the LDS areas (kLdsBytesHp<HP>, 16-byte aligned, and the
+// two [kWaves][32] merge arrays).
+template <int BS, bool FP8, int HP>
 __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, int bz, int nz,
-                                             char* __restrict__ s_lds, float (*s_m)[16],
-                                             float (*s_l)[16]) {
+                                             char* __restrict__ s_lds, float (*s_m)[32],
+                                             float (*s_l)[32]) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(HP == 1 || (HP == 2 && FP8), "two heads per wave: e4m3 caches");
   constexpr int kBlkPerTile = kTile / BS;
   constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
-  constexpr int kRowsPerLoad = FP8 ? 8 : 4;          // token rows per wave load
+  // bytes of one token's row as a wave reads it: HP adjacent kv heads
+  constexpr int kRowBytes = HP * kD * kEB;
+  constexpr int kLanesPerRow = kRowBytes / 16;
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;    // token rows per wave load
   constexpr int kLoads = kTile / kRowsPerLoad;       // loads per tile (K and V each)
 
   Item it;
@@ -118,9 +130,10 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int n = lane & 15;     // MFMA column (query head) / A row (token or dim)
   const int kg = lane >> 4;    // k group / token row of a natural load
   const int group = a.num_heads / a.num_kv_heads;
-  const int kvh = bx / a.head_chunks;
-  const int chunk = bx % a.head_chunks;
-  const int h0 = kvh * group + chunk * 16;
+  // HP == 2: bx is a pair of kv heads (head_chunks is 1), 2 bx and 2 bx + 1
+  const int kvh = HP == 2 ? 2 * bx : bx / a.head_chunks;
+  const int chunk = HP == 2 ? 0 : bx % a.head_chunks;
+  const int h0 = kvh * group + chunk * 16;           // first query head of head hp: h0 + hp * group
   const int G = min(16, group - chunk * 16);
 
   const int pstart = it.base + part_first * it.P;
@@ -128,22 +141,30 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int pbegin = it.L_begin;                 // first visible key (sliding window)
 
   // Q^T B operands: lane (kg, n) holds q[h0+n][(4j+kg)*8 .. +8] for k-step j.
-  bf16x8_t qb[4];
-  {
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((int64_t)it.row * a.num_heads + h0 + n) * kD;
+  bf16x8_t qb[HP][4];
+#pragma unroll
+  for (int hp = 0; hp < HP; ++hp) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)it.row * a.num_heads + h0 + hp * group + n) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (n < G) v = *reinterpret_cast<const u32x4*>(qrow + (4 * j + kg) * 8);
-      qb[j] = as_bf16x8(v);
+      qb[hp][j] = as_bf16x8(v);
     }
   }
 
-  f32x4 o[8];
+  f32x4 o[HP][8];
+  float m[HP], lsum[HP], logit_scale[HP];
 #pragma unroll
-  for (int jd = 0; jd < 8; ++jd) o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int hp = 0; hp < HP; ++hp) {
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) o[hp][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[hp] = -INFINITY;
+    lsum[hp] = 0.f;
+    logit_scale[hp] = a.scale_log2;
+    if constexpr (FP8) logit_scale[hp] *= a.k_scale[kvh + hp];
+  }
 
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
@@ -151,20 +172,17 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD * kEB;   // bytes
   const uint32_t head_off = (uint32_t)kvh * kD * kEB;
   const int64_t blk_stride = a.block_stride * kEB;
-  float logit_scale = a.scale_log2, out_scale = 1.f;
-  if constexpr (FP8) {
-    logit_scale *= a.k_scale[kvh];
-    out_scale = a.v_scale[kvh];
-  }
   // lane's place in a natural load: token row within the load, byte offset
-  const int lrow = FP8 ? (lane >> 3) : kg;
-  const int lbyte = FP8 ? (lane & 7) * 16 : n * 16;
+  // in the row, and (fp8) which head's 128 bytes it holds
+  const int lrow = lane / kLanesPerRow;
+  const int lbyte = (lane % kLanesPerRow) * 16;
+  const int lhead = FP8 ? (lane % kLanesPerRow) / 8 : 0;
   const int64_t max_blk = a.num_blocks - 1;
   const int ntiles = (pend > pstart) ? (pend - pstart + kTile - 1) / kTile : 0;
   const int last_bi = (pend - 1) / BS;
 
-  char* klds = s_lds + wave * kWaveLds;
-  char* vlds = klds;                                 // V rows replace the K rows
+  // the wave's LDS: HP areas of kWaveLds bytes, one per head
+  char* wlds = s_lds + wave * HP * kWaveLds;
 
   // Block ids of one tile (wave uniform, scalar loads), fetched a step early.
   auto fetch_ids = [&](int tile, int64_t* ids) {
@@ -190,7 +208,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   };
 
   // Stage a tile's K rows, or its V rows (those of tokens past the end
-  // become zeros), in the wave's LDS area.
+  // become zeros), in the wave's LDS area (of the lane's head).
   auto stage_k = [&](const u32x4* K) {
     __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -199,12 +217,13 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       if constexpr (FP8) {
         // 16 codes = dims 16c .. 16c + 15 -> bfloat16 chunks 2c and 2c + 1
         const int c = lane & 7;
+        char* klds = wlds + lhead * kWaveLds;
         u32x4 k0, k1;
         e4m3x16_to_bf16x16(K[i], k0, k1);
         *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
         *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
       } else {
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, n)) = K[i];
+        *reinterpret_cast<u32x4*>(wlds + ktile_off(tok, n)) = K[i];
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -219,6 +238,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       const bool dead = !full && (tbase + tok >= pend || tbase + tok < pbegin);
       if constexpr (FP8) {
         const int c = lane & 7;
+        char* vlds = wlds + lhead * kWaveLds;
         u32x4 v0, v1;
         e4m3x16_to_bf16x16(V[i], v0, v1);
         if (dead) v0 = v1 = u32x4{0u, 0u, 0u, 0u};
@@ -227,17 +247,19 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       } else {
         u32x4 v = V[i];
         if (dead) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(vlds + tok * kVPitch + n * 16) = v;
+        *reinterpret_cast<u32x4*>(wlds + tok * kVPitch + n * 16) = v;
       }
     }
     __asm__ volatile("" ::: "memory");
   };
 
-  // Logits of a tile whose K rows are staged, and the online softmax update:
-  // returns the probabilities (the B operand of the PV product).
-  auto logits = [&](int tile) {
+  // Logits of head hp for a tile whose K rows are staged, and its online
+  // softmax update: returns the probabilities (the B operand of the PV
+  // product).
+  auto logits = [&](int tile, int hp) {
     const int tbase = pstart + tile * kTile;
     const bool full = tbase + kTile <= pend && tbase >= pbegin;
+    const char* klds = wlds + hp * kWaveLds;
 
     // logits S^T: A operand = K rows (token tt*16 + n, chunk 4j + kg)
     f32x4 sacc[2];
@@ -247,7 +269,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 ka = *reinterpret_cast<const u32x4*>(klds + ktile_off(tt * 16 + n, 4 * j + kg));
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], sacc[tt], 0, 0, 0);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[hp][j], sacc[tt], 0, 0, 0);
       }
     }
     // lane holds tokens tt*16 + 4kg + i of head column n
@@ -257,16 +279,17 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tbase + tt * 16 + 4 * kg + i;
-        s[tt * 4 + i] = (full || (tok < pend && tok >= pbegin)) ? sacc[tt][i] * logit_scale : -INFINITY;
+        s[tt * 4 + i] = (full || (tok < pend && tok >= pbegin)) ? sacc[tt][i] * logit_scale[hp]
+                                                                : -INFINITY;
       }
     float mx = s[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
     mx = xmax16_32(mx);
-    const float mn = fmaxf(m, mx);
+    const float mn = fmaxf(m[hp], mx);
     const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    m = mn;
+    const float alpha = fast_exp2(m[hp] - mref);
+    m[hp] = mn;
     bf16x8_t pb;
     float psum = 0.f;
 #pragma unroll
@@ -275,27 +298,27 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       psum += p;
       pb[e] = (__bf16)p;
     }
-    lsum = lsum * alpha + psum;
+    lsum[hp] = lsum[hp] * alpha + psum;
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) o[jd] *= alpha;
+    for (int jd = 0; jd < 8; ++jd) o[hp][jd] *= alpha;
     __asm__ volatile("" ::: "memory");
     return pb;
   };
 
-  // O^T += V^T P^T for a tile whose V rows are staged, one 16-dim tile at a
-  // time; the transposed reads give lane (kg, n) V[4kg + jj][16jd + n] and
-  // V[16 + 4kg + jj][16jd + n].
-  auto pv = [&](const bf16x8_t pb) {
+  // O^T += V^T P^T for head hp of a tile whose V rows are staged, one 16-dim
+  // tile at a time; the transposed reads give lane (kg, n) V[4kg + jj][16jd + n]
+  // and V[16 + 4kg + jj][16jd + n].
+  auto pv = [&](const bf16x8_t pb, int hp) {
     {
       const int jj = n >> 2, q4 = n & 3;
-      const char* r0 = vlds + (4 * kg + jj) * kVPitch + q4 * 8;
+      const char* r0 = wlds + hp * kWaveLds + (4 * kg + jj) * kVPitch + q4 * 8;
       const char* r1 = r0 + 16 * kVPitch;
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) {
         bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r0 + jd * 32));
         bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r1 + jd * 32));
         bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[jd], 0, 0, 0);
+        o[hp][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[hp][jd], 0, 0, 0);
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -331,44 +354,54 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     const int nt = tile + tstep;
     stage_k(kr);
     if (nt < tend) issue(kc, ids, kr);
-    const bf16x8_t pb = logits(tile);
+    bf16x8_t pb[HP];
+#pragma unroll
+    for (int hp = 0; hp < HP; ++hp) pb[hp] = logits(tile, hp);
     stage_v(tile, vr);
     if (nt < tend) {
       issue(vc, ids, vr);
       if (nt + tstep < tend) fetch_ids(nt + tstep, ids);
     }
-    pv(pb);
+#pragma unroll
+    for (int hp = 0; hp < HP; ++hp) pv(pb[hp], hp);
     tile = nt;
   }
 
-  // Merge the 4 waves (log-sum-exp rule) and write the row, or this range's
-  // partial result.  Each wave stages its state inside its own LDS area.
-  lsum = xsum16_32(lsum);
-  float* so = reinterpret_cast<float*>(klds);       // [16 heads][128]
+  // Merge the 4 waves (log-sum-exp rule) per head and write the row, or this
+  // range's partial result.  Each wave stages its state inside its own LDS
+  // areas.
 #pragma unroll
-  for (int jd = 0; jd < 8; ++jd)
-    *reinterpret_cast<f32x4*>(so + n * kD + 16 * jd + 4 * kg) = o[jd];
-  if (kg == 0) {
-    s_m[wave][n] = m;
-    s_l[wave][n] = lsum;
+  for (int hp = 0; hp < HP; ++hp) {
+    lsum[hp] = xsum16_32(lsum[hp]);
+    float* so = reinterpret_cast<float*>(wlds + hp * kWaveLds);   // [16 heads][128]
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd)
+      *reinterpret_cast<f32x4*>(so + n * kD + 16 * jd + 4 * kg) = o[hp][jd];
+    if (kg == 0) {
+      s_m[wave][hp * 16 + n] = m[hp];
+      s_l[wave][hp * 16 + n] = lsum[hp];
+    }
   }
   __syncthreads();
   const int range = rz;
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int h = idx / kD;
+  for (int idx = threadIdx.x; idx < HP * G * kD; idx += kThreads) {
+    const int hp = idx / (G * kD);
+    const int h = (idx / kD) % G;
     const int d = idx % kD;
-    float M = s_m[0][h];
+    float M = s_m[0][hp * 16 + h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hp * 16 + h]);
     const float Mref = (M == -INFINITY) ? 0.f : M;
     float O = 0.f, Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][h] - Mref);
-      O = fmaf(reinterpret_cast<const float*>(s_lds + w * kWaveLds)[h * kD + d], f, O);
-      Ls = fmaf(s_l[w][h], f, Ls);
+      const float f = fast_exp2(s_m[w][hp * 16 + h] - Mref);
+      O = fmaf(reinterpret_cast<const float*>(s_lds + (w * HP + hp) * kWaveLds)[h * kD + d], f, O);
+      Ls = fmaf(s_l[w][hp * 16 + h], f, Ls);
     }
-    const int head = h0 + h;
+    const int head = h0 + hp * group + h;
+    float out_scale = 1.f;
+    if constexpr (FP8) out_scale = a.v_scale[kvh + hp];
     if (it.nranges == 1) {
       const float v = Ls > 0.f ? O / Ls * out_scale : 0.f;
       static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * kD + d] =

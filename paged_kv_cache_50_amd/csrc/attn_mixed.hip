@@ -34,8 +34,8 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
                                                                        const AttnArgs dcd,
                                                                        const MixedGrid g) {
   __shared__ __attribute__((aligned(16))) char s_lds[kLdsBytes];
-  __shared__ float s_m[dec::kWaves][16];
-  __shared__ float s_l[dec::kWaves][16];
+  __shared__ float s_m[dec::kWaves][32];
+  __shared__ float s_l[dec::kWaves][32];
   __shared__ int s_item;
 
   // prefill items of the listed multi-row sequences; decode items as in the
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
       const int64_t t = item / g.dec_x;
       const int zi = (int)(t % g.dec_y);
       const int bz = (int)(t / g.dec_y);
-      dec::decode_block<BS, FP8>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
+      dec::decode_block<BS, FP8, 1>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
     }
   }
 }

@@ -46,6 +46,8 @@ struct AttnArgs {
   int32_t parts_per_wg;            // consecutive partitions one workgroup covers (>= 1);
                                    // the workspace holds one partial per workgroup range
   int32_t wave_per_part;           // 1: wave w of a workgroup owns partition w of its range
+  int32_t heads_per_wave;          // grouped decode over e4m3 caches: 2 = each wave reads two
+                                   // adjacent kv heads (grid.x = kv-head pairs); else 1
   int32_t head_chunks_gc;          // prefill: query heads per column group (power of 2, <= 8)
   int32_t z_base;                  // offset added to blockIdx.z
   int32_t range_desc;              // 1: grid.z runs over key ranges from the last one down
