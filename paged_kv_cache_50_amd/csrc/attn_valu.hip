@@ -9,8 +9,10 @@
 // varlen path.
 //
 // Work decomposition
-//   grid.x = kv head * head chunks, grid.y = key partition, grid.z = sequence
-//   (or query row in kModeVarlenRows).  A workgroup is 4 waves of 64 lanes.
+//   grid.x = kv head * head chunks, grid.y = sequence (or query row in
+//   kModeVarlenRows; plus z_base for launches split along this axis),
+//   grid.z = key partition (slowest, so that the empty partitions of short
+//   sequences dispatch last).  A workgroup is 4 waves of 64 lanes.
 //   One token row of one kv head (head_size elements) is read by LPR lanes
 //   with one 16-byte load each: 16 lanes for bf16 x 128, so a wave load
 //   covers RPW = 64 / LPR consecutive tokens of one block, fully coalesced.
