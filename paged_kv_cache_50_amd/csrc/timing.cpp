@@ -23,23 +23,32 @@ struct Timing {
   int64_t tail = 0;  // next record
 };
 Timing g_timing;
+constexpr int kEagerSlots = 64;
 
 }  // namespace
+
+// Creates the events of record slot i if needed.  Timing-only events:
+// without the system-scope fence a record costs no L2 writeback/invalidate
+// (which would otherwise add a few microseconds around every timed launch
+// and cool the caches of the next kernel).
+bool ensure_events(int i) {
+  if (g_timing.start[i]) return true;
+  if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess)
+    return false;
+  if (hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess) {
+    (void)hipEventDestroy(g_timing.start[i]);
+    g_timing.start[i] = nullptr;
+    return false;
+  }
+  return true;
+}
 
 bool timing_begin(hipStream_t st, int* slot) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   if (!g_timing.enabled) return false;
   if (g_timing.calls++ % g_timing.every != 0) return false;
   const int i = (int)(g_timing.tail % Timing::kCap);
-  if (!g_timing.start[i]) {
-    // timing-only events: without the system-scope fence a record costs no
-    // L2 writeback/invalidate (which would otherwise add a few microseconds
-    // around every timed launch and cool the caches of the next kernel)
-    if (hipEventCreateWithFlags(&g_timing.start[i], hipEventDisableSystemFence) != hipSuccess)
-      return false;
-    if (hipEventCreateWithFlags(&g_timing.stop[i], hipEventDisableSystemFence) != hipSuccess)
-      return false;
-  }
+  if (!ensure_events(i)) return false;
   if (g_timing.tail - g_timing.head >= Timing::kCap) g_timing.head++;  // overwrite oldest
   if (hipEventRecord(g_timing.start[i], st) != hipSuccess) return false;
   *slot = i;
@@ -53,7 +62,9 @@ void timing_end(hipStream_t st, int slot) {
 
 }  // namespace pkv
 
+using pkv::ensure_events;
 using pkv::g_timing;
+using pkv::kEagerSlots;
 using pkv::Timing;
 
 extern "C" {
@@ -65,6 +76,11 @@ pkv_status pkv_timing_enable(int32_t every_n) {
   g_timing.every = every_n > 0 ? every_n : 1;
   g_timing.calls = 0;
   g_timing.head = g_timing.tail = 0;
+  // the first records' events are created here, not between the launches
+  // being timed (a creation costs host time that a short step can notice)
+  if (g_timing.enabled)
+    for (int i = 0; i < kEagerSlots; ++i)
+      if (!ensure_events(i)) return PKV_ERR_HIP;
   return PKV_OK;
 }
 
