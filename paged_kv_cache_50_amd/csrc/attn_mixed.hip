@@ -21,7 +21,6 @@
 namespace pkv {
 namespace {
 
-constexpr int kXcds = 8;
 constexpr int kLdsBytes = pf::kLdsBytes > dec::kLdsBytes ? pf::kLdsBytes : dec::kLdsBytes;
 static_assert(pf::kThreads == dec::kThreads, "one block shape");
 
