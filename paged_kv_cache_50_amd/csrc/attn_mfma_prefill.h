@@ -50,6 +50,7 @@ namespace pf {
 constexpr int kWaves = 4;
 constexpr int kColTiles = 2 * kWaves;          // column tiles per workgroup
 constexpr float kRescaleSlack = 8.f;            // log2 of the largest unscaled probability
+constexpr float kSlackSum = 256.f;              // 2^kRescaleSlack
 // Initial exponent reference: a finite stand-in for -inf, far below any
 // logit, so that no step needs an infinity test (the first visible key
 // raises it; a column that sees no key keeps it and has sum 0)
@@ -387,6 +388,71 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     // maxima and the reference decisions of both column tiles
     float s[2][8], mn[2];
     bool raise[2];
+    if constexpr (!MASKED) {
+      // Unmasked tiles: the probabilities are formed against the current
+      // reference without the tile's maxima first.  If a column's max
+      // outgrew the reference by more than the slack, some probability
+      // exceeds 2^slack and so does its lane's sum; then (and only then) that
+      // column tile takes the full step: maxima, raised reference, rescale,
+      // probabilities again.  The result is the same as always taking it.
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[c][tt * 4 + i] = sacc[c][tt][i];
+      auto full_step = [&](int c, bf16x8_t& pb, float& psum) {
+        float mx = vmax(vmax(vmax(s[c][0], s[c][1]), vmax(s[c][2], s[c][3])),
+                        vmax(vmax(s[c][4], s[c][5]), vmax(s[c][6], s[c][7])));
+        mx = xmax16_32(mx) * sl2;
+        if (mx > m[c] + kRescaleSlack) {
+          const float alpha = fast_exp2(m[c] - mx);
+          lsum[c] *= alpha;
+#pragma unroll
+          for (int jd = 0; jd < 8; ++jd) o[c][jd] *= alpha;
+          m[c] = mx;
+        }
+        psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(s[c][e], sl2, -m[c]));
+          psum += p;
+          pb[e] = (__bf16)p;
+        }
+      };
+      bf16x8_t pb0, pb1;
+      float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(s[0][e], sl2, -m[0]));
+        psum0 += p;
+        pb0[e] = (__bf16)p;
+      }
+      if (__builtin_amdgcn_ballot_w64(!(psum0 <= kSlackSum))) full_step(0, pb0, psum0);
+      lsum[0] += psum0;
+      lds_results_ready(vr);
+      bf16x8_t va[8];
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        const u32x4 w = {vr[jd][0][0], vr[jd][0][1], vr[jd][1][0], vr[jd][1][1]};
+        va[jd] = as_bf16x8(w);
+      }
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        sched_fence();
+        o[0][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb0, o[0][jd], 0, 0, 0);
+        const float p = fast_exp2(fmaf(s[1][jd], sl2, -m[1]));
+        psum1 += p;
+        pb1[jd] = (__bf16)p;
+      }
+      sched_fence();
+      if (__builtin_amdgcn_ballot_w64(!(psum1 <= kSlackSum))) full_step(1, pb1, psum1);
+      lsum[1] += psum1;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        o[1][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb1, o[1][jd], 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int qpos = rowb[c] + n + off;            // this lane's column = query row
