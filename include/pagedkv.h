@@ -105,7 +105,8 @@ typedef struct pkv_kv_cache {
   int32_t head_size;     /* 64 or 128                                               */
   int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value, which
                             are bfloat16 for PKV_FP8_E4M3)                          */
-  int64_t block_stride;  /* elements between consecutive blocks; 0 = dense         */
+  int64_t block_stride;  /* elements between consecutive blocks; 0 = dense; the
+                            stride in bytes must be below 2 GiB (PKV_ERR_SHAPE)    */
   const float* k_scale;  /* PKV_FP8_E4M3: device float32 [num_kv_heads]; cached code
                             c of kv head h stands for e4m3(c) * k_scale[h].  The
                             pages' (num_sequences, num_kv_heads) descale (vLLM book,

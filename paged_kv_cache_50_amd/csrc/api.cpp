@@ -58,6 +58,8 @@ pkv_status check_cache(const pkv_kv_cache* c, int32_t num_heads) {
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache)) return PKV_ERR_ALIGN;
   if (c->dtype == PKV_FP8_E4M3 && (!c->k_scale || !c->v_scale)) return PKV_ERR_NULL;
   const int64_t stride = c->block_stride ? c->block_stride : dense;
+  // the kernels form block offsets as 32-bit block id x 32-bit block bytes
+  if (stride > (int64_t)INT32_MAX / elem_bytes(c->dtype)) return PKV_ERR_SHAPE;
   if ((stride * elem_bytes(c->dtype)) % 16 != 0) return PKV_ERR_ALIGN;
   return PKV_OK;
 }

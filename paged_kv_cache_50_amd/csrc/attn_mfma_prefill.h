@@ -250,7 +250,10 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // token row and head offsets in elements (bfloat16) or bytes (fp8)
   const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD;
   const uint32_t head_off = (uint32_t)kvh * kD;
-  const int64_t max_blk = a.num_blocks - 1;
+  // block ids are clamped into the pool: num_blocks < 2^31, and a block is
+  // far below 4 GiB, so the byte offset is one 32 x 32 -> 64-bit product
+  const uint32_t max_blk = (uint32_t)min<int64_t>(a.num_blocks - 1, INT32_MAX);
+  const uint32_t blk_bytes = (uint32_t)(a.block_stride * (FP8 ? 1 : 2));
   const int last_tok = max(0, kv_end - 1);
 
   // block ids of tile t's token groups for this wave (two 16-token halves;
@@ -260,8 +263,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   auto fetch_ids = [&](int t, int32_t* raw) {
 #pragma unroll
     for (int u = 0; u < (FP8 ? 1 : 2); ++u) {
-      const int tw = min(t * kTile + (FP8 ? 8 * wave : 16 * u + 4 * wave), last_tok);
-      const int bi = __builtin_amdgcn_readfirstlane(tw / BS);
+      const uint32_t tw = min((uint32_t)t * kTile + (FP8 ? 8 * wave : 16 * u + 4 * wave),
+                              (uint32_t)last_tok);
+      const uint32_t bi = __builtin_amdgcn_readfirstlane(tw / BS);
       raw[u] = load_uniform_i32(bt, bi);
     }
   };
@@ -289,11 +293,11 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // issue the direct-to-LDS loads of tile t into stage buf (4 per thread;
   // fp8: 2); in the last, partial tile tokens past the range are clamped to
   // the last valid one, which stays in the block of the wave's first token
-  auto issue = [&](int t, const int32_t* raw, char* buf) {
-    const bool full = (t + 1) * kTile <= kv_end;
+  auto issue = [&](int t, const int32_t* raw, char* buf, auto full_tag) {
+    const bool full = decltype(full_tag)::value || (t + 1) * kTile <= kv_end;
 #pragma unroll
     for (int u = 0; u < (FP8 ? 1 : 2); ++u) {
-      const int64_t boff = min((int64_t)max(raw[u], 0), max_blk) * a.block_stride * kEB;
+      const uint64_t boff = (uint64_t)min((uint32_t)max(raw[u], 0), max_blk) * blk_bytes;
       const char* kb = reinterpret_cast<const char*>(kc) + boff;
       const char* vb = reinterpret_cast<const char*>(vc) + boff;
       char* kdst = buf + (FP8 ? 0 : u * 4096) + wave * 1024;
@@ -531,14 +535,16 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // the bfloat16 tile t visible and frees the bfloat16 tile of t - 1, into
   // which the thread then converts its codes of t + 1.
   constexpr int kLoadsPerTile = FP8 ? 2 : 4;
-  auto stage = [&](int t) { return s_lds + (t % kStages) * (FP8 ? kStageBytes8 : kStageBytes); };
+  auto stage = [&](int t) {
+    return s_lds + ((uint32_t)t % kStages) * (FP8 ? kStageBytes8 : kStageBytes);
+  };
   auto tile = [&](int t) { return FP8 ? s_lds + kRingBytes8 + (t & 1) * kStageBytes : stage(t); };
   int32_t ids[2];
 #pragma unroll
   for (int t = t_begin; t < t_begin + kStages - 1; ++t)
     if (t < ntiles) {
       fetch_ids(t, ids);
-      issue(t, ids, stage(t));
+      issue(t, ids, stage(t), std::false_type{});
     }
   if (t_begin + kStages - 1 < ntiles) fetch_ids(t_begin + kStages - 1, ids);
   if constexpr (FP8) {
@@ -550,14 +556,18 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
       convert(stage(t_begin), tile(t_begin));
     }
   }
-  auto step = [&](int t, auto masked_tag) {
+  // STEADY: t + kStages < ntiles, so the tiles issued after t are in flight
+  // (kStages - 2 of them), and the tile issued now (t + kStages - 1) is whole
+  // and has a successor whose block ids are fetched.
+  auto step = [&](int t, auto masked_tag, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
     if constexpr (FP8) {
-      const int ahead = min(1, ntiles - 2 - t);           // tiles issued after t + 1
+      const int ahead = STEADY ? 1 : min(1, ntiles - 2 - t);   // tiles issued after t + 1
       if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
       else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this thread's conversion writes
     } else {
-      const int ahead = min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
+      const int ahead = STEADY ? kStages - 2 : min(kStages - 2, ntiles - 1 - t);   // tiles issued after t
       if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_enc(2 * kLoadsPerTile));
       else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_enc(kLoadsPerTile));
       else __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));
@@ -569,13 +579,13 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     if constexpr (FP8)
-      if (t + 1 < ntiles) convert(stage(t + 1), tile(t + 1));
+      if (STEADY || t + 1 < ntiles) convert(stage(t + 1), tile(t + 1));
     const int tn = t + kStages - 1;
-    if (tn < ntiles) issue(tn, ids, stage(tn));
+    if (STEADY || tn < ntiles) issue(tn, ids, stage(tn), steady_tag);
     compute(t, tile(t), masked_tag);
     // the next tile's block ids: loaded after this tile's LDS reads, so that
     // their waits do not include the scalar loads
-    if (tn + 1 < ntiles) fetch_ids(tn + 1, ids);
+    if (STEADY || tn + 1 < ntiles) fetch_ids(tn + 1, ids);
   };
   // Tiles wholly at or below the workgroup's first row position and inside
   // the key range need no mask for any wave; the rest (the diagonal band and
@@ -587,9 +597,11 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int unmasked_begin = max(win >= 0 ? max(0, q_last + off - win) : 0, key_lo);
   const int tu = min(ntiles, max(t_begin, (unmasked_begin + kTile - 1) / kTile));
   const int tm = min(ntiles, max(tu, (unmasked_end + 1) / kTile));
-  for (int t = t_begin; t < tu; ++t) step(t, std::true_type{});
-  for (int t = tu; t < tm; ++t) step(t, std::false_type{});
-  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{});
+  const int ts = max(tu, min(tm, ntiles - kStages));   // steady unmasked tiles: [tu, ts)
+  for (int t = t_begin; t < tu; ++t) step(t, std::true_type{}, std::false_type{});
+  for (int t = tu; t < ts; ++t) step(t, std::false_type{}, std::true_type{});
+  for (int t = ts; t < tm; ++t) step(t, std::false_type{}, std::false_type{});
+  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{}, std::false_type{});
 
   // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]
 #pragma unroll

@@ -110,6 +110,8 @@ def test_decode_error_codes(L):
     assert decode(L, cache(), S=-1) == 2
     assert decode(L, cache(), mb=0) == 2
     assert decode(L, cache(stride=100)) == 2                     # stride smaller than a block
+    assert decode(L, cache(stride=1 << 30)) == 2                 # a block stride of 2 GiB (bf16)
+    assert decode(L, cache(dtype=0, stride=1 << 29)) == 2        # 2 GiB of fp32
     assert decode(L, cache(), ps=100) == 2                       # partition not a multiple of 32
     assert decode(L, cache(), win=-2) == 2                       # window below -1
     need = pagedkv.workspace_bytes(4, 32, 8, 128, 1000, 0)
