@@ -139,7 +139,9 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // as the bfloat16 stages are (each thread converts the 16 + 16 codes it
 // loaded itself), and the products read those.  The per-kv-head k_scale is
 // folded into the logit scale and v_scale into the output.
-template <int BS, bool PREFIX = false, bool FP8 = false>
+// UNROLL: the steady tiles run four at a time with every LDS stage known at
+// compile time (more registers: kept out of the one-launch forms).
+template <int BS, bool PREFIX = false, bool FP8 = false, bool UNROLL = true>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
   int qs, q_len, L, off;
@@ -539,6 +541,22 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     return s_lds + ((uint32_t)t % kStages) * (FP8 ? kStageBytes8 : kStageBytes);
   };
   auto tile = [&](int t) { return FP8 ? s_lds + kRingBytes8 + (t & 1) * kStageBytes : stage(t); };
+  // the same with the stage known at compile time: PH = t % kStages (>= 0),
+  // so that the LDS addresses become immediate offsets
+  auto stage_ph = [&](int t, auto ph, int k) {
+    constexpr int PH = decltype(ph)::value;
+    if constexpr (PH >= 0)
+      return s_lds + ((PH + k) % kStages) * (FP8 ? kStageBytes8 : kStageBytes);
+    else
+      return stage(t + k);
+  };
+  auto tile_ph = [&](int t, auto ph, int k) {
+    constexpr int PH = decltype(ph)::value;
+    if constexpr (PH >= 0)
+      return FP8 ? s_lds + kRingBytes8 + ((PH + k) & 1) * kStageBytes : stage_ph(t, ph, k);
+    else
+      return tile(t + k);
+  };
   int32_t ids[2];
 #pragma unroll
   for (int t = t_begin; t < t_begin + kStages - 1; ++t)
@@ -559,7 +577,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // STEADY: t + kStages < ntiles, so the tiles issued after t are in flight
   // (kStages - 2 of them), and the tile issued now (t + kStages - 1) is whole
   // and has a successor whose block ids are fetched.
-  auto step = [&](int t, auto masked_tag, auto steady_tag) {
+  // PH: t % kStages when known at compile time, else -1
+  constexpr std::integral_constant<int, -1> kNoPhase{};
+  auto step = [&](int t, auto masked_tag, auto steady_tag, auto ph) {
     constexpr bool STEADY = decltype(steady_tag)::value;
     if constexpr (FP8) {
       const int ahead = STEADY ? 1 : min(1, ntiles - 2 - t);   // tiles issued after t + 1
@@ -579,10 +599,10 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     if constexpr (FP8)
-      if (STEADY || t + 1 < ntiles) convert(stage(t + 1), tile(t + 1));
+      if (STEADY || t + 1 < ntiles) convert(stage_ph(t, ph, 1), tile_ph(t, ph, 1));
     const int tn = t + kStages - 1;
-    if (STEADY || tn < ntiles) issue(tn, ids, stage(tn), steady_tag);
-    compute(t, tile(t), masked_tag);
+    if (STEADY || tn < ntiles) issue(tn, ids, stage_ph(t, ph, kStages - 1), steady_tag);
+    compute(t, tile_ph(t, ph, 0), masked_tag);
     // the next tile's block ids: loaded after this tile's LDS reads, so that
     // their waits do not include the scalar loads
     if (STEADY || tn + 1 < ntiles) fetch_ids(tn + 1, ids);
@@ -598,10 +618,21 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int tu = min(ntiles, max(t_begin, (unmasked_begin + kTile - 1) / kTile));
   const int tm = min(ntiles, max(tu, (unmasked_end + 1) / kTile));
   const int ts = max(tu, min(tm, ntiles - kStages));   // steady unmasked tiles: [tu, ts)
-  for (int t = t_begin; t < tu; ++t) step(t, std::true_type{}, std::false_type{});
-  for (int t = tu; t < ts; ++t) step(t, std::false_type{}, std::true_type{});
-  for (int t = ts; t < tm; ++t) step(t, std::false_type{}, std::false_type{});
-  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{}, std::false_type{});
+  for (int t = t_begin; t < tu; ++t) step(t, std::true_type{}, std::false_type{}, kNoPhase);
+  // steady tiles: up to a multiple of kStages one by one, then kStages at a
+  // time with every stage known at compile time
+  int t = tu;
+  for (; t < ts && ((uint32_t)t % kStages) != 0; ++t) step(t, std::false_type{}, std::true_type{}, kNoPhase);
+  static_assert(kStages == 4, "the unrolled steady loop covers four stages");
+  for (; UNROLL && t + kStages <= ts; t += kStages) {
+    step(t, std::false_type{}, std::true_type{}, std::integral_constant<int, 0>{});
+    step(t + 1, std::false_type{}, std::true_type{}, std::integral_constant<int, 1>{});
+    step(t + 2, std::false_type{}, std::true_type{}, std::integral_constant<int, 2>{});
+    step(t + 3, std::false_type{}, std::true_type{}, std::integral_constant<int, 3>{});
+  }
+  for (; t < ts; ++t) step(t, std::false_type{}, std::true_type{}, kNoPhase);
+  for (int t = ts; t < tm; ++t) step(t, std::false_type{}, std::false_type{}, kNoPhase);
+  for (int t = tm; t < ntiles; ++t) step(t, std::true_type{}, std::false_type{}, kNoPhase);
 
   // normalise and write the rows this lane holds: O^T[16jd + 4kg + r][n]
 #pragma unroll
