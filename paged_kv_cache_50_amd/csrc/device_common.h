@@ -39,24 +39,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // round to nearest even and handle subnormals (out-of-range inputs must be
 // clamped first: they would become NaN).
 
-// Four e4m3 codes (bytes of w, low first) -> four bfloat16 (exact: every
-// e4m3 value is a bfloat16), as two words of two.
-__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);    // bytes 0, 1
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);     // bytes 2, 3
-  // the float32 results have zero low halves: keep the high 16 bits of each
-  uint2 r;
-  r.x = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-  return r;
+// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with hi) -> two bfloat16 (low
+// half first) in one instruction: the gfx950 scaled converter with scale 1.
+// Exact, since every e4m3 value is a bfloat16; on the device it gives the
+// same bits as converting to float32 (v_cvt_pk_f32_fp8) and keeping the high
+// halves, for all 2^16 code pairs, NaNs included.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi));
 }
 
 // Sixteen e4m3 codes -> two 16-byte chunks of eight bfloat16.
 __device__ __forceinline__ void e4m3x16_to_bf16x16(const u32x4 w, u32x4& c0, u32x4& c1) {
-  const uint2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-  const uint2 c = e4m3x4_to_bf16x4(w[2]), d = e4m3x4_to_bf16x4(w[3]);
-  c0 = u32x4{a.x, a.y, b.x, b.y};
-  c1 = u32x4{c.x, c.y, d.x, d.y};
+  c0 = u32x4{e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
+             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
+  c1 = u32x4{e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
+             e4m3x2_to_bf16x2(w[3], false), e4m3x2_to_bf16x2(w[3], true)};
 }
 
 // Saturate to the finite e4m3 range; NaN passes through.

@@ -120,12 +120,18 @@ def test_fp8_needle_bit_exact(ps):
     w.q[:] = 0
     w.q[:, :, 0] = W.f32_to_bf16_bits(np.float32(64.0))
     needles = [257, 16, 512]
+    # the needles' V rows hold every finite code (2 kv heads x 128 dims), so
+    # the kernels' e4m3 -> bfloat16 conversion is checked code by code; -0
+    # (0x80) is left out: an output summed from a +0 start reads +0
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0x80, 0xFF]] = 0
     for s, L in enumerate(w.seq_lens):
         blk = w.block_tables[s, np.arange(L) // 16]
         off = np.arange(L) % 16
         w.k_cache[blk, off, :, 0] = 0                          # every key orthogonal to e0
         j = needles[s]
         w.k_cache[w.block_tables[s, j // 16], j % 16, :, 0] = 0x68   # 64.0
+        w.v_cache[w.block_tables[s, j // 16], j % 16] = np.roll(codes, 37 * s).reshape(2, 128)
     _announce(f"fp8 needle ps={ps}")
     dw = G.DevWorkload(w)
     G.run(dw, partition_size=ps)
@@ -216,8 +222,13 @@ def test_fp8_prefill_needle_bit_exact():
     w.k_cache[valid, :, 0] = 0
     w.q[:] = 0
     w.q[:, :, 0] = W.f32_to_bf16_bits(np.float32(64.0))
+    # key 0's V rows hold every finite code except -0 (each 4 times over 8
+    # kv heads)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0x80, 0xFF]] = 0
     for s in range(2):
         w.k_cache[w.block_tables[s, 0], 0, :, 0] = 0x68
+        w.v_cache[w.block_tables[s, 0], 0] = np.resize(np.roll(codes, 11 * s), (8, 128))
     _announce("fp8 prefill needle")
     dw = G.DevWorkload(w)
     G.run(dw, write=False)
