@@ -21,9 +21,10 @@ namespace {
 constexpr int kMaxPrefixParts = 16;
 
 // grid = (rows, head groups of 256 / (D/4) heads); a group of D/4 lanes owns
-// one query head and issues all of its loads at once (partials past
-// num_parts are clamped in bounds and weighted 0).
-template <int D>
+// one query head and issues all of its loads at once.  NP (a power of two,
+// at least num_parts) fixes how many partial slots are loaded; slots past
+// num_parts are clamped in bounds and weighted 0.
+template <int D, int NP>
 __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
                                                             const float* __restrict__ lse_suffix,
                                                             int num_parts) {
@@ -45,13 +46,13 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
   const int qe = clamp_i(a.cu_seqlens_q[lo + 1], 0, a.num_tokens);
   if (row < qs || row >= qe || row - qs >= a.max_query_len) return;
   const bool with_prefix = a.seq_lens[lo] > 0;
-  const int np = max(1, min(num_parts, kMaxPrefixParts));
+  const int np = max(1, min(num_parts, NP));
   const int64_t stride = (int64_t)a.num_heads * a.num_tokens;     // between partitions
   const int64_t base = (int64_t)head * a.num_tokens + row;
-  float l[kMaxPrefixParts];
-  f32x4 v[kMaxPrefixParts];
+  float l[NP];
+  f32x4 v[NP];
 #pragma unroll
-  for (int p = 0; p < kMaxPrefixParts; ++p) {
+  for (int p = 0; p < NP; ++p) {
     const int64_t e = base + (int64_t)min(p, np - 1) * stride;
     l[p] = a.ws_lse[e];
     v[p] = *reinterpret_cast<const f32x4*>(a.ws_o + e * D + 4 * c);
@@ -64,14 +65,14 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
   const float ls = lse_suffix[oi] * kLog2e;
   float M = ls;
 #pragma unroll
-  for (int p = 0; p < kMaxPrefixParts; ++p)
+  for (int p = 0; p < NP; ++p)
     M = fmaxf(M, with_prefix && p < np ? l[p] : -INFINITY);
   const float Mref = (M == -INFINITY) ? 0.f : M;
   const float ws = ls == -INFINITY ? 0.f : fast_exp2(ls - Mref);
   f32x4 acc = ws * vs;
   float wsum = ws;
 #pragma unroll
-  for (int p = 0; p < kMaxPrefixParts; ++p) {
+  for (int p = 0; p < NP; ++p) {
     const float w = with_prefix && p < np ? fast_exp2(l[p] - Mref) : 0.f;
     acc += w * v[p];
     wsum += w;
@@ -90,8 +91,16 @@ hipError_t launch_cascade_merge(const AttnArgs& a, const float* lse_suffix, int 
   if (num_parts < 1 || num_parts > kMaxPrefixParts) return hipErrorInvalidValue;
   constexpr int D = 128;
   constexpr int NG = 256 / (D / 4);
-  hipLaunchKernelGGL((cascade_merge_kernel<D>), dim3(a.num_tokens, (a.num_heads + NG - 1) / NG),
-                     dim3(256), 0, stream, a, lse_suffix, num_parts);
+  const dim3 grid(a.num_tokens, (a.num_heads + NG - 1) / NG), block(256);
+  if (num_parts <= 2)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 2>), grid, block, 0, stream, a, lse_suffix, num_parts);
+  else if (num_parts <= 4)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 4>), grid, block, 0, stream, a, lse_suffix, num_parts);
+  else if (num_parts <= 8)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 8>), grid, block, 0, stream, a, lse_suffix, num_parts);
+  else
+    hipLaunchKernelGGL((cascade_merge_kernel<D, kMaxPrefixParts>), grid, block, 0, stream, a,
+                       lse_suffix, num_parts);
   return hipGetLastError();
 }
 

@@ -39,21 +39,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // round to nearest even and handle subnormals (out-of-range inputs must be
 // clamped first: they would become NaN).
 
-// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with hi) -> two bfloat16 (low
+// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with HI) -> two bfloat16 (low
 // half first) in one instruction: the gfx950 scaled converter with scale 1.
 // Exact, since every e4m3 value is a bfloat16; on the device it gives the
 // same bits as converting to float32 (v_cvt_pk_f32_fp8) and keeping the high
 // halves, for all 2^16 code pairs, NaNs included.
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi));
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // Sixteen e4m3 codes -> two 16-byte chunks of eight bfloat16.
 __device__ __forceinline__ void e4m3x16_to_bf16x16(const u32x4 w, u32x4& c0, u32x4& c1) {
-  c0 = u32x4{e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true),
-             e4m3x2_to_bf16x2(w[1], false), e4m3x2_to_bf16x2(w[1], true)};
-  c1 = u32x4{e4m3x2_to_bf16x2(w[2], false), e4m3x2_to_bf16x2(w[2], true),
-             e4m3x2_to_bf16x2(w[3], false), e4m3x2_to_bf16x2(w[3], true)};
+  c0 = u32x4{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
+             e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
+  c1 = u32x4{e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
+             e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
 }
 
 // Saturate to the finite e4m3 range; NaN passes through.

@@ -64,6 +64,23 @@ def test_cascade_mixed_batch(hq, hkv, bs, causal):
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"cascade mixed {hq}/{hkv} bs={bs}")
 
 
+@pytest.mark.parametrize("cpl", [1024, 2048, 4096])
+def test_cascade_many_prefix_partitions(cpl):
+    """Long shared prefixes split into 4, 8 and 16 key partitions (a mixed
+    batch: the prefix pass and the merge run as their own launches)."""
+    rng = np.random.default_rng(cpl)
+    ql = np.array([1] * 6 + [40, 9])
+    own = rng.integers(0, 200, size=len(ql))
+    w = W.make_varlen("cascade_long_prefix", cpl + own, ql, 32, 8, 128, 16, "bf16", 90 + cpl // 1024,
+                      causal=True, common_prefix_len=cpl)
+    _announce(f"cascade with a {cpl}-token prefix")
+    dw = G.DevWorkload(w)
+    G.run_cascade(dw)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"cascade cpl={cpl}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"cascade cpl={cpl}")
+
+
 def test_cascade_close_to_plain_call():
     torch = G.torch()
     w = _mixed(32, 8, 16, True, 71)
