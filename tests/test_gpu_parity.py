@@ -376,6 +376,27 @@ def test_parity_prefill_shapes(hq, hkv, bs, causal):
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "prefill")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("ps", [0, -1])
+def test_parity_prefill_long_context(causal, bs, ps):
+    """Chunks over long cached contexts, so that most key tiles take the
+    steady step; the contexts start the steady tiles at every tile phase and
+    end on ragged tails.  ps = 0: one launch with the decode rows (split
+    workspace); ps = -1: the prefill launch of its own, whose steady tiles go
+    four at a time."""
+    ctx = [1000, 1031, 2050, 777, 0]
+    ql = [64, 100, 40, 1, 130]
+    w = W.make_varlen("prefill_long", ctx, ql, 32, 8, 128, bs, "bf16", seed=17 + bs + causal,
+                      causal=causal)
+    _announce(f"prefill long context bs={bs} causal={causal} ps={ps}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=ps)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"prefill long bs={bs} causal={causal}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "prefill long")
+
+
 def test_prefill_needle_bit_exact():
     """Causal chunk whose rows each see a needle key placed at a row-dependent
     position at or before the row's own position: exact block indexing and
