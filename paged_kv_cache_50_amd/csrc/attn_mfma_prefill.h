@@ -34,7 +34,12 @@
 // column's max grows by more than 2^8 (then the accumulators are rescaled);
 // otherwise probabilities up to 2^8 are accumulated against the old
 // reference.  The result is unchanged: output and log-sum-exp are formed
-// from the same reference.
+// from the same reference.  Unmasked tiles form their probabilities against
+// the current reference first and compute the maxima only when some lane's
+// sum exceeds 2^8 (the only case in which the reference can need raising).
+// Tiles inside the key range whose successor tiles are all in flight run a
+// steady step without end-of-range tests; in the prefill launch of its own
+// they run four at a time, each with its LDS stage fixed at compile time.
 #pragma once
 
 #include <type_traits>
