@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 COPY_BYTES = 1 << 30
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof/trace_w{n} "
-             "-o t -- python3 $REPO/bench.py --workload {n} --steps 50 --warmup 5 --no-cpu-baseline")
+             "-o t -- python3 $REPO/bench.py --workload {n} --steps 50 --warmup 200 --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/prof/{tag}_w{n} -o {o} "
            "-- python3 $REPO/bench.py --workload {n} --steps 3 --warmup 1 --no-cpu-baseline")
 COPY_CMD = ("rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/prof/{tag}_copy -o {o} "
