@@ -363,8 +363,12 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 
   // MASKED: the tile may hold keys past a row's causal limit or the range
   // end, or lie wholly above this wave's rows (skipped).
-  auto compute = [&](int t, const char* buf, auto masked_tag) {
+  // SO: the tile's byte offset from s_lds when known at compile time (>= 0),
+  // else -1; the transposed reads then take it as their immediate offset, so
+  // their address registers do not depend on the stage
+  auto compute = [&](int t, const char* buf, auto masked_tag, auto so_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int SO = decltype(so_tag)::value;
     const int j0 = t * kTile;
     // wholly above this wave's diagonal, or below its window
     if (MASKED && (j0 > wave_last_pos || j0 + kTile - 1 < wave_first_key)) return;
@@ -377,12 +381,21 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         ka[tt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + koff[j] + tt * 4096));
-    const uint32_t vbase = (uint32_t)(uintptr_t)(lds_void*)buf;
     u32x2 vr[8][2];
+    if constexpr (SO >= 0) {
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)s_lds;
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      vr[jd][0] = ds_read_tr16_b64<0>(vbase + voff[jd]);
-      vr[jd][1] = ds_read_tr16_b64<16 * kD * 2>(vbase + voff[jd]);
+      for (int jd = 0; jd < 8; ++jd) {
+        vr[jd][0] = ds_read_tr16_b64<SO>(lds0 + voff[jd]);
+        vr[jd][1] = ds_read_tr16_b64<SO + 16 * kD * 2>(lds0 + voff[jd]);
+      }
+    } else {
+      const uint32_t vbase = (uint32_t)(uintptr_t)(lds_void*)buf;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        vr[jd][0] = ds_read_tr16_b64<0>(vbase + voff[jd]);
+        vr[jd][1] = ds_read_tr16_b64<16 * kD * 2>(vbase + voff[jd]);
+      }
     }
     // S^T = K Q^T for both column tiles
     f32x4 sacc[2][2];
@@ -607,7 +620,13 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
       if (STEADY || t + 1 < ntiles) convert(stage_ph(t, ph, 1), tile_ph(t, ph, 1));
     const int tn = t + kStages - 1;
     if (STEADY || tn < ntiles) issue(tn, ids, stage_ph(t, ph, kStages - 1), steady_tag);
-    compute(t, tile_ph(t, ph, 0), masked_tag);
+    {
+      constexpr int PH = decltype(ph)::value;
+      constexpr int SO = PH < 0 ? -1
+                         : FP8 ? kRingBytes8 + (PH & 1) * kStageBytes
+                               : (PH % kStages) * kStageBytes;
+      compute(t, tile_ph(t, ph, 0), masked_tag, std::integral_constant<int, SO>{});
+    }
     // the next tile's block ids: loaded after this tile's LDS reads, so that
     // their waits do not include the scalar loads
     if (STEADY || tn + 1 < ntiles) fetch_ids(tn + 1, ids);
