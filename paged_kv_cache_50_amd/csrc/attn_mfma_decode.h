@@ -125,8 +125,14 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   if (rz >= it.nranges) return;
   const int part_end = min(part_first + a.parts_per_wg, it.nparts);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The thread index passes through an empty asm: in a persistent grid that
+  // runs this body and another per item, the lane-derived offsets are then
+  // formed inside each body, not hoisted above the item loop and held in
+  // registers across both bodies.
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;     // MFMA column (query head) / A row (token or dim)
   const int kg = lane >> 4;    // k group / token row of a natural load
   const int group = a.num_heads / a.num_kv_heads;
@@ -384,7 +390,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   }
   __syncthreads();
   const int range = rz;
-  for (int idx = threadIdx.x; idx < HP * G * kD; idx += kThreads) {
+  for (int idx = tid; idx < HP * G * kD; idx += kThreads) {
     const int hp = idx / (G * kD);
     const int h = (idx / kD) % G;
     const int d = idx % kD;

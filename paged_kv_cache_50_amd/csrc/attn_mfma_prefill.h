@@ -38,8 +38,8 @@
 // the current reference first and compute the maxima only when some lane's
 // sum exceeds 2^8 (the only case in which the reference can need raising).
 // Tiles inside the key range whose successor tiles are all in flight run a
-// steady step without end-of-range tests; in the prefill launch of its own
-// they run four at a time, each with its LDS stage fixed at compile time.
+// steady step without end-of-range tests, four at a time, each with its LDS
+// stage fixed at compile time.
 #pragma once
 
 #include <type_traits>
@@ -144,9 +144,7 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // as the bfloat16 stages are (each thread converts the 16 + 16 codes it
 // loaded itself), and the products read those.  The per-kv-head k_scale is
 // folded into the logit scale and v_scale into the output.
-// UNROLL: the steady tiles run four at a time with every LDS stage known at
-// compile time (more registers: kept out of the one-launch forms).
-template <int BS, bool PREFIX = false, bool FP8 = false, bool UNROLL = true>
+template <int BS, bool PREFIX = false, bool FP8 = false>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
   int qs, q_len, L, off;
@@ -178,7 +176,12 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const float sl2 = FP8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
   const float oscale = FP8 ? a.v_scale[kvh] : 1.f;
 
-  const int tid = threadIdx.x;
+  // The thread index passes through an empty asm: in a persistent grid that
+  // runs this body and another per item, the lane-derived offsets are then
+  // formed inside each body, not hoisted above the item loop and held in
+  // registers across both bodies.
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
@@ -648,7 +651,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   int t = tu;
   for (; t < ts && ((uint32_t)t % kStages) != 0; ++t) step(t, std::false_type{}, std::true_type{}, kNoPhase);
   static_assert(kStages == 4, "the unrolled steady loop covers four stages");
-  for (; UNROLL && t + kStages <= ts; t += kStages) {
+  for (; t + kStages <= ts; t += kStages) {
     step(t, std::false_type{}, std::true_type{}, std::integral_constant<int, 0>{});
     step(t + 1, std::false_type{}, std::true_type{}, std::integral_constant<int, 1>{});
     step(t + 2, std::false_type{}, std::true_type{}, std::integral_constant<int, 2>{});

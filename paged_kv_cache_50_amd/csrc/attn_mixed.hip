@@ -67,15 +67,14 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int part = (int)(t / g.pre_y);
-      pf::prefill_block<BS, true, FP8, false>(pre, bx, by, part, s_lds);
+      pf::prefill_block<BS, true, FP8>(pre, bx, by, part, s_lds);
     } else if (role == 0) {
       // the last query tiles of a chunk see the most keys: they go first
       const int bx = g.pre_x - 1 - (int)(item % g.pre_x);
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int li = (int)(t / g.pre_y);
-      pf::prefill_block<BS, false, FP8, false>(pre, bx, by, load_uniform_i32(g.pre_list, li),
-                                             s_lds);
+      pf::prefill_block<BS, false, FP8>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
     } else {
       const int bx = (int)(item % g.dec_x);
       const int64_t t = item / g.dec_x;
