@@ -421,7 +421,7 @@ def main() -> int:
         pre_rows = int(sum(int(x) for x in ql if x > 1))
         pre_bytes = (pre_kv * 2 * w.num_kv_heads * w.head_size * e
                      + 2 * pre_rows * w.num_heads * w.head_size * w.io_bytes)
-        mixed = os.environ.get("PKV_MIXED", "1") != "0" and w.dtype == "bf16" and ps != -1
+        mixed = os.environ.get("PKV_MIXED", "1") != "0" and w.dtype in ("bf16", "fp8") and ps != -1
         if mixed:
             # one launch carries the prefill tiles and the decode rows: its
             # ideal time is set by the bytes of all rows (HBM), not by the

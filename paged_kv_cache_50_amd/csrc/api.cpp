@@ -283,19 +283,21 @@ int32_t device_cus() {
 }
 
 // XCDs in four (by workgroup index) that start the mixed launch on prefill
-// tiles: 2 (of 1-3 tried, with roles per XCD or inside each XCD).
+// tiles: 2 over a bfloat16 cache, 3 over an fp8 one (of 1-4 tried, with
+// roles per XCD or inside each XCD).  Over an fp8 cache the prefill tiles
+// also convert their codes and the decode rows move half the bytes, so more
+// of the chip starts on prefill (C5's batch over an fp8 cache: 250 us, against
+// 262 us in two launches and 285 us with 2 XCDs in four).
 constexpr int32_t kMixedShare = 2;
+constexpr int32_t kMixedShareFp8 = 3;
 
 // Mixed batches (prefill chunks and decode rows) run as one interleaved
 // launch when both kinds use the matrix-core kernels and a split workspace
-// holds the planner's lists.  Not for fp8 caches: there the prefill tiles
-// (with their conversion) are heavier and the decode rows lighter, and two
-// launches measured faster (C5's batch over an fp8 cache: 303 against
-// 355 us).  PKV_MIXED=0 keeps two launches (A/B runs).
+// holds the planner's lists.  PKV_MIXED=0 keeps two launches (A/B runs).
 bool use_mixed_launch(const AttnArgs& a, const pkv_kv_cache* cache) {
   static const char* env = std::getenv("PKV_MIXED");
   if (env && std::strcmp(env, "0") == 0) return false;
-  return a.num_splits > 1 && use_mfma_prefill(cache) && !is_fp8(cache) &&
+  return a.num_splits > 1 && use_mfma_prefill(cache) &&
          use_mfma_decode(cache, a.num_heads / cache->num_kv_heads);
 }
 
@@ -500,7 +502,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
     g.pre_y = cache->num_kv_heads * (group / gc);
     g.pre_z = 1;
-    g.pre_share = kMixedShare;
+    g.pre_share = is_fp8(cache) ? kMixedShareFp8 : kMixedShare;
     g.dec_x = (int32_t)gx_d;
     g.dec_y = num_seqs;
     g.dec_z = (int32_t)gparts;
@@ -515,7 +517,8 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
       if (st != PKV_OK) return st;
       int tslot = 0;
       const bool timed = timing_begin(s, &tslot);
-      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, s) != hipSuccess) st = PKV_ERR_HIP;
+      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, is_fp8(cache), s) != hipSuccess)
+        st = PKV_ERR_HIP;
       if (timed) timing_end(s, tslot);
       if (st != PKV_OK) return st;
       return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);

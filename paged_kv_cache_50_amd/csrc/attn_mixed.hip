@@ -26,8 +26,8 @@ static_assert(pf::kThreads == dec::kThreads, "one block shape");
 
 // CASCADE: the first kind of work is the cascade prefix pass (items = query
 // tile x head group x prefix partition, a fixed count) instead of the
-// listed prefill chunks.  FP8: e4m3 caches (both kinds of work; used for
-// the cascade).
+// listed prefill chunks.  FP8: e4m3 caches (both kinds of work; the decode
+// rows with one kv head per wave).
 template <int BS, bool CASCADE, bool FP8>
 __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const AttnArgs pre,
                                                                        const AttnArgs dcd,
@@ -102,8 +102,9 @@ hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, 
 }  // namespace
 
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                             int block_size, hipStream_t stream) {
-  return launch<false, false>(pre, dcd, g, block_size, stream);
+                             int block_size, bool fp8, hipStream_t stream) {
+  return fp8 ? launch<false, true>(pre, dcd, g, block_size, stream)
+             : launch<false, false>(pre, dcd, g, block_size, stream);
 }
 
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,

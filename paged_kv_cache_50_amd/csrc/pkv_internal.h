@@ -119,7 +119,7 @@ hipError_t launch_seq_order(const int32_t* seq_lens, int32_t num_seqs, int32_t m
 
 // One launch for a mixed varlen batch: prefill tiles (args `pre`, mode
 // kModeVarlenRows) over the listed multi-row sequences, and decode rows
-// (args `dcd`, mode kModeVarlenOne, grouped bfloat16 decode), interleaved.
+// (args `dcd`, mode kModeVarlenOne, grouped matrix-core decode), interleaved.
 struct MixedGrid {
   int64_t n_dec;                   // decode items: dec_x * dec_y * dec_z
   int32_t pre_x, pre_y;            // prefill items per listed sequence: query tiles x head groups
@@ -131,8 +131,9 @@ struct MixedGrid {
   const int32_t* pre_count;        // [1] how many
   int32_t* queues;                 // [2] item counters (prefill, decode), zeroed by the planner
 };
+// bfloat16 or (fp8 = true) e4m3 caches.
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                             int block_size, hipStream_t stream);
+                             int block_size, bool fp8, hipStream_t stream);
 // The same persistent grid for a cascade of decode rows: prefix-pass items
 // (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`);
 // bfloat16 or (fp8 = true) e4m3 caches.

@@ -194,13 +194,15 @@ def _fp8_mixed(hq, hkv, bs, causal, seed, cpl=0):
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 8)])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_prefill_chunks(hq, hkv, bs, causal):
+@pytest.mark.parametrize("ps", [256, -1])
+def test_fp8_prefill_chunks(hq, hkv, bs, causal, ps):
     """Chunked prefill rows and decode rows over an fp8 cache, with the
-    quantising write of the new tokens first."""
+    quantising write of the new tokens first.  With split rows (ps 256) both
+    kinds run in one persistent launch; unsplit (ps -1), in two launches."""
     w = _fp8_mixed(hq, hkv, bs, causal, 90 + hq + bs)
-    _announce(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} causal={causal}")
+    _announce(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} causal={causal} ps={ps}")
     dw = G.DevWorkload(w)
-    G.run(dw, partition_size=256)
+    G.run(dw, partition_size=ps)
     ref, ref_lse = G.reference(w)
     G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"fp8 prefill {hq}/{hkv} bs={bs}")
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, f"fp8 prefill {hq}/{hkv} bs={bs}")
