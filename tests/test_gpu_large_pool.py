@@ -1,0 +1,97 @@
+"""GPU parity with every block placed past the first 4 GiB of a large pool.
+
+A pool on a 288 GB device spans tens of gigabytes, so the byte offset of a
+block (block id x block bytes) exceeds 2^32 and every kernel must form it in
+64-bit arithmetic.  Each case copies a small workload's blocks to block ids
+whose offsets lie beyond 4 GiB in pools of a little over 4 GiB per cache
+(uninitialised below: only the blocks the tables name are read), shifts the
+block tables, the slot mapping and the prefix blocks to match, and compares
+the outputs with the oracle on the compact workload, and the slot write
+(bit for bit) with the oracle's write.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_50_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_50_amd import pagedkv
+    pagedkv.lib()      # raises if the library was not built
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+# name -> workload (the comment names the kernel it reaches)
+CASES = {
+    "f32_decode": lambda: W.make_config(1),                                   # VALU, fp32
+    "mha_decode": lambda: W.make_config(2, num_seqs=6, max_len=1500),         # VALU, bf16
+    "gqa_decode": lambda: W.make_config(3, num_seqs=6, max_len=1500),         # matrix-core decode
+    "mixed": lambda: W.make_config(5, num_seqs=9, max_len=700, num_chunks=2, chunk_len=70),
+    "fp8_decode": lambda: W.make_config(6, num_seqs=6, max_len=1500),         # fp8, 2 heads/wave
+    "fp8_mixed": lambda: W.make_config(10, num_seqs=9, max_len=700, num_chunks=2, chunk_len=70),
+    "cascade": lambda: W.make_config(9, num_seqs=8, max_len=600),             # prefix pass + merge
+}
+
+
+def _relocate(dw, base: int, block_size: int):
+    """Move the device caches to block ids base.. of pools base + n blocks
+    long, and shift every block reference by base."""
+    t = G.torch()
+
+    def big(c):
+        pool = t.empty((base + c.shape[0],) + tuple(c.shape[1:]), dtype=c.dtype, device=c.device)
+        pool[base:].copy_(c)
+        return pool
+
+    dw.k_cache = big(dw.k_cache)
+    dw.v_cache = big(dw.v_cache)
+    dw.block_tables = dw.block_tables + base
+    if dw.slot_mapping is not None:
+        sm = dw.slot_mapping
+        dw.slot_mapping = t.where(sm >= 0, sm + base * block_size, sm)
+    if dw.prefix_blocks is not None:
+        dw.prefix_blocks = dw.prefix_blocks + base
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    """Cache contents as integers (float32 caches may hold NaN padding)."""
+    return x.view(np.uint32) if x.dtype == np.float32 else x
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_blocks_beyond_4gib(case):
+    w = CASES[case]()
+    dw = G.DevWorkload(w)
+    blk_bytes = dw.k_cache[0].numel() * dw.k_cache.element_size()
+    base = (1 << 32) // blk_bytes + 3                 # first block id used: past 4 GiB
+    assert base * blk_bytes > (1 << 32)
+    _announce(f"{case}: blocks from id {base} ({base * blk_bytes / 2**30:.2f} GiB), "
+              f"{dw.k_cache.shape[0]} blocks moved")
+    _relocate(dw, base, w.block_size)
+    if case == "cascade":
+        G.run_cascade(dw)
+    else:
+        G.run(dw)
+    ref, ref_lse = G.reference(w)
+    io = "f32" if w.dtype == "f32" else "bf16"
+    G.assert_close(G.dev_to_f64(dw.out), ref, io, case)
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, case)
+    if w.slot_mapping is not None:
+        kc, vc = G.oracle_inputs(w)
+        assert np.array_equal(_bits(G.dev_to_bits(dw.k_cache[base:])), _bits(kc)), case
+        assert np.array_equal(_bits(G.dev_to_bits(dw.v_cache[base:])), _bits(vc)), case
+    del dw
+    G.torch().cuda.empty_cache()
