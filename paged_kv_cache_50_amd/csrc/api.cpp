@@ -1,9 +1,10 @@
 // Host side of libpagedkv.so: argument validation, kernel selection, launch
-// geometry, split workspace layout, per-launch timing and the host metadata
-// checker.  The C ABI is declared in include/pagedkv.h.
+// geometry, split workspace layout, per-launch timing and the host-side metadata
+// validation.  The C ABI is declared in include/pagedkv.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -269,17 +270,21 @@ pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspac
   return PKV_OK;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that race
+// on the first call all store the same count).  0 if it cannot be read.
 int32_t device_cus() {
-  static int32_t cus[64] = {0};
+  static std::atomic<int32_t> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+  int32_t n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int attr = 0;
+    if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    n = attr;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // XCDs in four (by workgroup index) that start the mixed launch on prefill

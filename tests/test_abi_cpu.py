@@ -1,7 +1,7 @@
 """Host-side checks of libpagedkv.so that need no GPU: the library loads and
 exports every function include/pagedkv.h declares, capability and workspace
 queries, argument validation (error codes forced from the host; no kernel is
-ever launched here) and the host metadata checker."""
+ever launched here) and the host-side metadata validation."""
 import ctypes
 import os
 import re
@@ -139,7 +139,7 @@ def test_varlen_and_write_error_codes(L):
     assert w(ctypes.byref(c), A16, A16, A16, 0, None) == 0
 
 
-# ------------------------------------------------------------------ metadata checker
+# ------------------------------------------------------------------ metadata validation
 
 def test_validate_metadata_accepts_generated_workloads(L):
     for cfg, kw in ((1, {}), (3, dict(num_seqs=10, max_len=800))):

@@ -1,6 +1,6 @@
 """Host-side checks of the cascade entry points (no GPU, no kernel launch):
 error codes, workspace sizes, the decision helper's thresholds and the
-cascade metadata checker."""
+cascade metadata validation."""
 import ctypes
 import math
 
