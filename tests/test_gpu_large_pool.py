@@ -1,4 +1,5 @@
-"""GPU parity with every block placed past the first 4 GiB of a large pool.
+"""GPU parity over pool layouts: blocks past the first 4 GiB of a large pool,
+and K and V interleaved in one allocation.
 
 A pool on a 288 GB device spans tens of gigabytes, so the byte offset of a
 block (block id x block bytes) exceeds 2^32 and every kernel must form it in
@@ -8,6 +9,11 @@ whose offsets lie beyond 4 GiB in pools of a little over 4 GiB per cache
 block tables, the slot mapping and the prefix blocks to match, and compares
 the outputs with the oracle on the compact workload, and the slot write
 (bit for bit) with the oracle's write.
+
+The interleaved layout is one [num_blocks, 2, block_size, kv heads, head]
+allocation whose K and V halves are views: the block stride is twice a
+block, and every kernel must step blocks by the stride, not by the block's
+own size.
 """
 import numpy as np
 import pytest
@@ -66,6 +72,23 @@ def _relocate(dw, base: int, block_size: int):
         dw.prefix_blocks = dw.prefix_blocks + base
 
 
+def _check(case, w, dw, k_blocks, v_blocks):
+    """Run the step, compare with the oracle; k_blocks / v_blocks: the
+    device blocks that hold the workload's pool, for the write check."""
+    if case == "cascade":
+        G.run_cascade(dw)
+    else:
+        G.run(dw)
+    ref, ref_lse = G.reference(w)
+    io = "f32" if w.dtype == "f32" else "bf16"
+    G.assert_close(G.dev_to_f64(dw.out), ref, io, case)
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, case)
+    if w.slot_mapping is not None:
+        kc, vc = G.oracle_inputs(w)
+        assert np.array_equal(_bits(G.dev_to_bits(k_blocks)), _bits(kc)), case
+        assert np.array_equal(_bits(G.dev_to_bits(v_blocks)), _bits(vc)), case
+
+
 def _bits(x: np.ndarray) -> np.ndarray:
     """Cache contents as integers (float32 caches may hold NaN padding)."""
     return x.view(np.uint32) if x.dtype == np.float32 else x
@@ -81,17 +104,21 @@ def test_blocks_beyond_4gib(case):
     _announce(f"{case}: blocks from id {base} ({base * blk_bytes / 2**30:.2f} GiB), "
               f"{dw.k_cache.shape[0]} blocks moved")
     _relocate(dw, base, w.block_size)
-    if case == "cascade":
-        G.run_cascade(dw)
-    else:
-        G.run(dw)
-    ref, ref_lse = G.reference(w)
-    io = "f32" if w.dtype == "f32" else "bf16"
-    G.assert_close(G.dev_to_f64(dw.out), ref, io, case)
-    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, case)
-    if w.slot_mapping is not None:
-        kc, vc = G.oracle_inputs(w)
-        assert np.array_equal(_bits(G.dev_to_bits(dw.k_cache[base:])), _bits(kc)), case
-        assert np.array_equal(_bits(G.dev_to_bits(dw.v_cache[base:])), _bits(vc)), case
+    _check(case, w, dw, dw.k_cache[base:], dw.v_cache[base:])
     del dw
     G.torch().cuda.empty_cache()
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_interleaved_kv_pool(case):
+    t = G.torch()
+    w = CASES[case]()
+    dw = G.DevWorkload(w)
+    kv = t.empty((dw.k_cache.shape[0], 2) + tuple(dw.k_cache.shape[1:]), dtype=dw.k_cache.dtype,
+                 device=dw.k_cache.device)
+    kv[:, 0].copy_(dw.k_cache)
+    kv[:, 1].copy_(dw.v_cache)
+    dw.k_cache, dw.v_cache = kv[:, 0], kv[:, 1]
+    assert dw.k_cache.stride(0) == 2 * dw.k_cache[0].numel()
+    _announce(f"{case}: K and V interleaved, block stride {dw.k_cache.stride(0)} elements")
+    _check(case, w, dw, dw.k_cache, dw.v_cache)
