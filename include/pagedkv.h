@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -114,6 +114,41 @@ typedef struct pkv_kv_cache {
                             broadcast of these per-layer scales.  NULL otherwise.  */
   const float* v_scale;  /* the same for V                                          */
 } pkv_kv_cache;
+
+/*
+ * Per-call launch choices (in) and a report of what the call enqueued (out),
+ * for measurements and tests.  Optional: the attention calls take a pointer
+ * that may be NULL, which means the library's own choices and no report.
+ * Every choice selects one of the library's kernel variants; all of them
+ * compute the same attention within the stated tolerances.  A choice that
+ * does not apply to a call (a forced VALU decode over an fp8 cache, which has
+ * only the matrix-core kernel) is ignored.  Values other than those listed
+ * return PKV_ERR_SHAPE.  The library keeps nothing of it after the call.
+ */
+typedef struct pkv_call_options {
+  int32_t decode_kernel;   /* 0 library choice; 1 the VALU kernel; 2 the matrix-core
+                              kernel (bfloat16 caches with head_size 128)          */
+  int32_t prefill_kernel;  /* 0 library choice; 1 the VALU row kernel (bfloat16)     */
+  int32_t fp8_head_pairs;  /* 0 library choice; 1 one kv head per wave in fp8 decode  */
+  int32_t mixed_launch;    /* 0 library choice; 1 prefill rows and decode rows of a
+                              varlen batch in separate launches                     */
+  int32_t cascade_launch;  /* 0 library choice; 1 the cascade's prefix and suffix
+                              passes in separate launches                           */
+  uint32_t launched;       /* out: PKV_RAN_* bits of the kernels the call enqueued
+                              (0 when it returned before launching)                 */
+} pkv_call_options;
+
+#define PKV_RAN_PLANNER        0x001u  /* longest-first sequence order / work queues   */
+#define PKV_RAN_DECODE_VALU    0x002u  /* one-row attention on the VALU                */
+#define PKV_RAN_DECODE_MFMA    0x004u  /* one-row attention on the matrix cores        */
+#define PKV_RAN_DECODE_PAIRS   0x008u  /* ... fp8, each wave reading two kv heads      */
+#define PKV_RAN_PREFILL_MFMA   0x010u  /* multi-row (chunked prefill) launch, matrix cores */
+#define PKV_RAN_PREFILL_VALU   0x020u  /* multi-row rows on the VALU row kernel        */
+#define PKV_RAN_MIXED          0x040u  /* prefill tiles and decode rows in one launch  */
+#define PKV_RAN_PREFIX         0x080u  /* cascade prefix pass, a launch of its own     */
+#define PKV_RAN_CASCADE_ONE    0x100u  /* cascade prefix pass and decode rows in one launch */
+#define PKV_RAN_SPLIT_MERGE    0x200u  /* log-sum-exp merge of key-range partials      */
+#define PKV_RAN_CASCADE_MERGE  0x400u  /* merge of the cascade's prefix and suffix results */
 
 /*
  * Scatter new K/V rows into the cache ("reshape_and_cache", ch. 6 "Écriture du
@@ -164,15 +199,18 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs]
  *   max_seq_len   host upper bound of seq_lens (sizes the launch and the split)
- *   scale         logit scale (usually 1/sqrt(head_size))
+ *   scale         logit scale (usually 1/sqrt(head_size)), finite; any sign
  *   window_left   sliding window (vLLM book, ch. 6 "forward()": the window
  *                 symmetrisation): the row at position p = seq_len - 1 sees
- *                 keys p - window_left .. p; -1 = no window.  Blocks wholly
- *                 outside the window are never read.
+ *                 keys p - window_left .. p; -1 = no window.  Key tiles start
+ *                 at a multiple of 32 positions, so at most 31 keys before the
+ *                 window start are read (and masked out); blocks that hold
+ *                 none of those and none of the window are never read.
  *   partition_size see pkv_choose_partition_size
  *   lse_out       optional device float32 [num_seqs, num_heads]
  *   workspace     device, >= pkv_attention_workspace_bytes(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0
+ *   options       optional launch choices and report (pkv_call_options)
  * num_seqs == 0 is a no-op.
  */
 pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cache* cache,
@@ -180,7 +218,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                                       int32_t max_seq_len, float scale, int32_t window_left,
                                       int32_t partition_size, float* lse_out, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      size_t workspace_bytes, pkv_call_options* options,
+                                      void* stream);
 
 /*
  * Variable-length attention over a flattened batch (ch. 6 "Structure des
@@ -195,11 +234,18 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
  *   cu_seqlens_q  device int32 [num_seqs + 1], non-decreasing, from 0
  *   seq_lens      device int32 [num_seqs]
  *   max_query_len host upper bound of the query lengths
+ *   scale         finite; must be positive when max_query_len > 1
+ *                 (PKV_ERR_SHAPE otherwise): the prefill kernels take the
+ *                 row maxima of the unscaled logits
  *   window_left   sliding window, -1 = none: a row at absolute position p sees
  *                 keys p - window_left .. p when causal, and
  *                 p - window_left .. p + window_left when not (the causal
  *                 window (w, 0) made symmetric, ch. 6 "forward()")
  *   lse_out       optional device float32 [num_tokens, num_heads]
+ *   options       optional launch choices and report (pkv_call_options)
+ * Over an fp8 cache the prefill kernels fold k_scale into the logit scale,
+ * so with max_query_len > 1 every k_scale entry must be positive as well
+ * (device values, not checked; results are undefined otherwise).
  */
 pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cache* cache,
                                       const int32_t* cu_seqlens_q, const int32_t* seq_lens,
@@ -208,7 +254,7 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       int32_t max_query_len, int32_t max_seq_len, float scale,
                                       int32_t causal, int32_t window_left, int32_t partition_size,
                                       float* lse_out, void* workspace, size_t workspace_bytes,
-                                      void* stream);
+                                      pkv_call_options* options, void* stream);
 
 /*
  * Cascade (shared-prefix) attention (vLLM book, ch. 6: "Structure des
@@ -235,8 +281,11 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
  *   other arguments as for pkv_paged_attention_varlen
  *   workspace      >= pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned
  * Needs a bfloat16 or fp8 (e4m3) cache with head_size 128
- * (PKV_ERR_UNSUPPORTED otherwise); common_prefix_len 0 is the plain varlen
- * call.  Asynchronous on `stream`.
+ * (PKV_ERR_UNSUPPORTED otherwise) and, when common_prefix_len > 0, a
+ * positive scale (PKV_ERR_SHAPE otherwise) and positive fp8 k_scale entries,
+ * as for the prefill rows of pkv_paged_attention_varlen: the prefix pass is
+ * the prefill kernel.  common_prefix_len 0 is the plain varlen call.
+ * Asynchronous on `stream`.
  * The suffix result is rounded to bfloat16 before the merge, as the output of
  * the pages' suffix call is; the prefix partials stay fp32.
  */
@@ -247,7 +296,8 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
                                  int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
                                  int32_t max_seq_len, int32_t common_prefix_len, float scale,
                                  int32_t causal, int32_t partition_size, float* lse_out,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes,
+                                 pkv_call_options* options, void* stream);
 
 /*
  * Workspace bytes of pkv_cascade_attention: the prefix partials

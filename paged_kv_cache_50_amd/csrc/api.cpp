@@ -1,14 +1,14 @@
 // Host side of libpagedkv.so: argument validation, kernel selection, launch
-// geometry, split workspace layout, per-launch timing and the host-side metadata
-// validation.  The C ABI is declared in include/pagedkv.h.
+// geometry, split workspace layout and the host-side metadata validation.
+// The C ABI is declared in include/pagedkv.h.  Nothing here outlives a call:
+// launch choices arrive with each call (pkv_call_options) and the kernels that
+// ran are reported back through it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <unordered_set>
 
@@ -32,6 +32,43 @@ bool is_fp8(const pkv_kv_cache* c) { return c->dtype == PKV_FP8_E4M3; }
 int32_t io_dtype(int32_t dtype) { return dtype == PKV_FP8_E4M3 ? PKV_BF16 : dtype; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Launch choices of one call (pkv_call_options, 0 = the library's choice)
+// and the PKV_RAN_* bits of what it enqueued.
+struct Choice {
+  int32_t decode_kernel = 0;   // 1 VALU, 2 matrix cores
+  int32_t prefill_kernel = 0;  // 1 VALU rows
+  int32_t fp8_pairs = 0;       // 1 one kv head per wave
+  int32_t mixed = 0;           // 1 separate launches
+  int32_t cascade = 0;         // 1 separate launches
+  uint32_t ran = 0;
+};
+
+pkv_status read_options(const pkv_call_options* o, Choice* c) {
+  *c = Choice{};
+  if (!o) return PKV_OK;
+  if (o->decode_kernel < 0 || o->decode_kernel > 2 || o->prefill_kernel < 0 ||
+      o->prefill_kernel > 1 || o->fp8_head_pairs < 0 || o->fp8_head_pairs > 1 ||
+      o->mixed_launch < 0 || o->mixed_launch > 1 || o->cascade_launch < 0 ||
+      o->cascade_launch > 1)
+    return PKV_ERR_SHAPE;
+  c->decode_kernel = o->decode_kernel;
+  c->prefill_kernel = o->prefill_kernel;
+  c->fp8_pairs = o->fp8_head_pairs;
+  c->mixed = o->mixed_launch;
+  c->cascade = o->cascade_launch;
+  return PKV_OK;
+}
+
+// Writes the report into the caller's options when the call returns, on
+// every path.
+struct Report {
+  pkv_call_options* o;
+  const Choice& c;
+  ~Report() {
+    if (o) o->launched = c.ran;
+  }
+};
 
 const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t num_heads,
                    int32_t num_kv_heads) {
@@ -73,31 +110,29 @@ int64_t block_stride_elems(const pkv_kv_cache* c) {
 // Decode kernel choice.  The matrix-core kernel pays off once a kv head
 // serves several query heads (a dense g x tokens contraction); with one query
 // head per kv head the work is a matrix-vector product and stays on the VALU.
-// PKV_DECODE_KERNEL=valu|mfma forces one variant (for A/B measurements).
+// A call's options may force either variant (A/B measurements).
 constexpr int kMfmaMinGroup = 4;
 constexpr int32_t kPlanMinSeqs = 64;
 constexpr int kMfmaTokensPerWg = 2048;
 constexpr int64_t kMfmaTargetWgs = 2048;   // about four rounds of 512 workgroup slots
 constexpr int64_t kWgFixedTokens = 128;    // a workgroup's fixed cost in streamed tokens
 
-bool use_mfma_decode(const pkv_kv_cache* c, int group) {
+bool use_mfma_decode(const pkv_kv_cache* c, int group, const Choice& ch) {
   if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
   if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
-  static const char* force = std::getenv("PKV_DECODE_KERNEL");
-  if (force && std::strcmp(force, "valu") == 0) return false;
-  if (force && std::strcmp(force, "mfma") == 0) return true;
+  if (ch.decode_kernel == 1) return false;
+  if (ch.decode_kernel == 2) return true;
   return group >= kMfmaMinGroup;
 }
 
 // Prefill kernel choice: the matrix-core kernel for bfloat16 or e4m3 caches
-// with head 128 (the only prefill kernel for e4m3); PKV_PREFILL_KERNEL=valu
-// forces the generic row kernel for bfloat16 (A/B measurements).
-bool use_mfma_prefill(const pkv_kv_cache* c) {
+// with head 128 (the only prefill kernel for e4m3); a call's options may
+// force the generic row kernel for bfloat16 (A/B measurements).
+bool use_mfma_prefill(const pkv_kv_cache* c, const Choice& ch) {
   if (c->head_size != 128) return false;
   if (c->dtype == PKV_FP8_E4M3) return true;
   if (c->dtype != PKV_BF16) return false;
-  static const char* force = std::getenv("PKV_PREFILL_KERNEL");
-  return !(force && std::strcmp(force, "valu") == 0);
+  return ch.prefill_kernel != 1;
 }
 
 // Query heads handled together by one workgroup of the VALU kernel.
@@ -137,11 +172,9 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // even number of them and a single head chunk.  Measured: MHA decode at
     // C2 shapes 200 -> 190 us; GQA decode at C3 shapes unchanged (twice the
     // LDS per workgroup: two workgroups per CU instead of three).  Only for
-    // the decode kernel's own launch (the one-launch forms keep one head).
-    // PKV_FP8_PAIRS=0 keeps one head per wave (A/B runs).
-    static const char* pe = std::getenv("PKV_FP8_PAIRS");
-    const bool pairs_on = !(pe && std::strcmp(pe, "0") == 0);
-    a.heads_per_wave = (two_heads_ok && pairs_on && is_fp8(cache) && a.head_chunks == 1 &&
+    // the decode kernel's own launch (the one-launch forms keep one head),
+    // and a call's options may keep one head per wave (A/B runs).
+    a.heads_per_wave = (two_heads_ok && is_fp8(cache) && a.head_chunks == 1 &&
                         cache->num_kv_heads % 2 == 0) ? 2 : 1;
     // Tokens one workgroup streams.  The floor: the largest of 2048 .. 256
     // that still gives the launch about kMfmaTargetWgs workgroups (several
@@ -203,10 +236,11 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
 }
 
 pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, int64_t z_total,
-                          hipStream_t st) {
+                          hipStream_t st, Choice& ch) {
   const int group = a.num_heads / cache->num_kv_heads;
-  if (use_mfma_decode(cache, group)) {
-    const auto [gx, gparts] = mfma_decode_geometry(a, cache, gy, true);
+  if (use_mfma_decode(cache, group, ch)) {
+    const auto [gx, gparts] = mfma_decode_geometry(a, cache, gy, ch.fp8_pairs == 0);
+    ch.ran |= PKV_RAN_DECODE_MFMA | (a.heads_per_wave == 2 ? PKV_RAN_DECODE_PAIRS : 0u);
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
@@ -219,15 +253,18 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
   }
   const int gt = heads_per_chunk(group);
   a.head_chunks = group / gt;
+  ch.ran |= PKV_RAN_DECODE_VALU;
   return launch_valu_z_chunks(a, cache->dtype, cache->head_size, cache->block_size, gt,
                               (unsigned)(cache->num_kv_heads * a.head_chunks), gy, z_total, st);
 }
 
-pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
+pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st,
+                         Choice& ch) {
   // with a single workgroup range per row (every partition of a row in one
   // workgroup) the attention kernel wrote every row itself
   const int max_ranges = a.partition_size > 0 ? (a.num_splits + a.parts_per_wg - 1) / a.parts_per_wg : 1;
   if (max_ranges <= 1) return PKV_OK;
+  ch.ran |= PKV_RAN_SPLIT_MERGE;
   if (pkv::launch_splitkv_reduce(a, dtype, head_size, st) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
@@ -253,13 +290,14 @@ int32_t* order_area(const AttnArgs& a, const pkv_kv_cache* cache, void* workspac
 // writes the order into the workspace).  With
 // `multi`, the planner also lists the multi-row sequences (mixed launch).
 pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspace,
-                          hipStream_t st, bool multi = false) {
-  if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads))
+                          hipStream_t st, Choice& ch, bool multi = false) {
+  if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads, ch))
     return PKV_OK;
   // with few sequences the planner's launch costs more than the order saves
   // (C4's 8 sequences: the same step time; with a 4096-key window: 47 -> 42 us)
   if (!multi && a.num_seqs < kPlanMinSeqs) return PKV_OK;
   int32_t* order = order_area(a, cache, workspace);
+  ch.ran |= PKV_RAN_PLANNER;
   if (pkv::launch_seq_order(a.seq_lens, a.num_seqs, a.max_seq_len, order,
                             multi ? a.cu_seqlens_q : nullptr, a.num_tokens,
                             multi ? order + a.num_seqs : nullptr,
@@ -270,21 +308,14 @@ pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspac
   return PKV_OK;
 }
 
-// Compute units of the current device (cached per device; threads that race
-// on the first call all store the same count).  0 if it cannot be read.
+// Compute units of the current device, 0 if they cannot be read.  Asked of
+// the runtime on each use (it answers from its own device properties).
 int32_t device_cus() {
-  static std::atomic<int32_t> cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int32_t n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    int attr = 0;
-    if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    n = attr;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
+  int dev = 0, attr = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return attr;
 }
 
 // XCDs in four (by workgroup index) that start the mixed launch on prefill
@@ -298,12 +329,11 @@ constexpr int32_t kMixedShareFp8 = 3;
 
 // Mixed batches (prefill chunks and decode rows) run as one interleaved
 // launch when both kinds use the matrix-core kernels and a split workspace
-// holds the planner's lists.  PKV_MIXED=0 keeps two launches (A/B runs).
-bool use_mixed_launch(const AttnArgs& a, const pkv_kv_cache* cache) {
-  static const char* env = std::getenv("PKV_MIXED");
-  if (env && std::strcmp(env, "0") == 0) return false;
-  return a.num_splits > 1 && use_mfma_prefill(cache) &&
-         use_mfma_decode(cache, a.num_heads / cache->num_kv_heads);
+// holds the planner's lists; a call's options may keep two launches (A/B).
+bool use_mixed_launch(const AttnArgs& a, const pkv_kv_cache* cache, const Choice& ch) {
+  if (ch.mixed == 1) return false;
+  return a.num_splits > 1 && use_mfma_prefill(cache, ch) &&
+         use_mfma_decode(cache, a.num_heads / cache->num_kv_heads, ch);
 }
 
 int32_t num_splits_for(int32_t max_seq_len, int32_t P) {
@@ -380,11 +410,10 @@ constexpr int64_t kPrefixTargetWgsFused = 128;
 
 // A cascade whose rows are all decode rows runs the prefix pass and the
 // suffix pass as one persistent launch when the decode rows use the
-// matrix-core kernel.  PKV_CASCADE_FUSED=0 keeps separate launches (A/B runs).
-bool use_cascade_launch(const pkv_kv_cache* cache, int group) {
-  static const char* env = std::getenv("PKV_CASCADE_FUSED");
-  if (env && std::strcmp(env, "0") == 0) return false;
-  return use_mfma_decode(cache, group) && device_cus() > 0;
+// matrix-core kernel; a call's options may keep separate launches (A/B).
+bool use_cascade_launch(const pkv_kv_cache* cache, int group, const Choice& ch) {
+  if (ch.cascade == 1) return false;
+  return use_mfma_decode(cache, group, ch) && device_cus() > 0;
 }
 
 // XCDs in four (by workgroup index) that start the one-launch cascade on
@@ -450,7 +479,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
                        int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
                        int32_t max_seq_len, float scale, int32_t causal, int32_t window_left,
                        int32_t partition_size, float* lse_out, void* workspace,
-                       size_t workspace_bytes, void* stream, int32_t kv_start) {
+                       size_t workspace_bytes, void* stream, int32_t kv_start, Choice& ch) {
   pkv_status st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
   if (window_left < -1) return PKV_ERR_SHAPE;
@@ -460,6 +489,8 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  // the prefill kernels take row maxima of the unscaled logits
+  if (max_query_len > 1 && !(scale > 0.f)) return PKV_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q) return PKV_ERR_NULL;
   if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
@@ -489,7 +520,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   const unsigned gx = (unsigned)(cache->num_kv_heads * a.head_chunks);
 
   // Prefill chunks and decode rows of one batch: a single interleaved launch.
-  if (max_query_len > 1 && use_mixed_launch(a, cache)) {
+  if (max_query_len > 1 && use_mixed_launch(a, cache, ch)) {
     AttnArgs r = a;
     r.mode = pkv::kModeVarlenRows;
     r.partition_size = 0;
@@ -502,7 +533,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     AttnArgs d = a;
     d.mode = pkv::kModeVarlenOne;
     d.seq_order = order_area(d, cache, workspace);   // written by the planner below
-    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
+    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns, false);
     pkv::MixedGrid g{};
     g.pre_x = (max_query_len + rows_per_wg - 1) / rows_per_wg;
     g.pre_y = cache->num_kv_heads * (group / gc);
@@ -518,15 +549,16 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     g.workgroups = 2 * device_cus();                // two per CU (LDS and registers allow two)
     const int64_t n_pre_max = (int64_t)g.pre_x * g.pre_y * num_seqs;
     if (g.workgroups > 0 && n_pre_max < (int64_t)INT32_MAX && g.n_dec < (int64_t)INT32_MAX) {
-      st = plan_seq_order(d, cache, workspace, s, /*multi=*/true);
+      st = plan_seq_order(d, cache, workspace, s, ch, /*multi=*/true);
       if (st != PKV_OK) return st;
       int tslot = 0;
       const bool timed = timing_begin(s, &tslot);
+      ch.ran |= PKV_RAN_MIXED;
       if (pkv::launch_attn_mixed(r, d, g, cache->block_size, is_fp8(cache), s) != hipSuccess)
         st = PKV_ERR_HIP;
       if (timed) timing_end(s, tslot);
       if (st != PKV_OK) return st;
-      return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+      return launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s, ch);
     }
   }
   // Rows of sequences with several query rows (chunked prefill).
@@ -538,7 +570,8 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
     r.ws_lse = nullptr;
     int tslot = 0;
     const bool timed = timing_begin(s, &tslot);
-    if (use_mfma_prefill(cache)) {
+    if (use_mfma_prefill(cache, ch)) {
+      ch.ran |= PKV_RAN_PREFILL_MFMA;
       int gc = 8;
       while (group % gc) gc >>= 1;
       r.head_chunks_gc = gc;
@@ -553,6 +586,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
           st = PKV_ERR_HIP;
       }
     } else {
+      ch.ran |= PKV_RAN_PREFILL_VALU;
       st = launch_valu_z_chunks(r, cache->dtype, cache->head_size, cache->block_size, gt, gx, 1,
                                 num_tokens, s);
     }
@@ -562,18 +596,48 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   // Sequences with one query row (decode rows), split over the key range;
   // the main launch when the batch has no longer query ranges.
   a.mode = pkv::kModeVarlenOne;
-  st = plan_seq_order(a, cache, workspace, s);
+  st = plan_seq_order(a, cache, workspace, s, ch);
   if (st != PKV_OK) return st;
   int tslot = 0;
   const bool timed = max_query_len <= 1 && timing_begin(s, &tslot);
-  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
+  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s, ch);
   if (timed) timing_end(s, tslot);
   if (st != PKV_OK) return st;
-  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
+  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s, ch);
   return st;
 }
 
 }  // namespace
+
+namespace pkv {
+
+pkv_status decode_host_checks(const void* out, const void* q, const pkv_kv_cache* cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t max_seq_len, float scale, int32_t window_left,
+                              int32_t partition_size, const pkv_call_options* options) {
+  Choice ch;
+  pkv_status st = read_options(options, &ch);
+  if (st != PKV_OK) return st;
+  st = check_cache(cache, num_heads);
+  if (st != PKV_OK) return st;
+  if (window_left < -1) return PKV_ERR_SHAPE;
+  if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_SHAPE;
+  if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
+    return PKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !block_tables || !seq_lens) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
+  const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads,
+                                              max_seq_len, partition_size);
+  if (P < 0) return PKV_ERR_SHAPE;
+  if (num_splits_for(max_seq_len, P) > kMaxGridY) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace pkv
 
 extern "C" {
 
@@ -659,23 +723,20 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
                                       int32_t max_seq_len, float scale, int32_t window_left,
                                       int32_t partition_size, float* lse_out, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
-  pkv_status st = check_cache(cache, num_heads);
+                                      size_t workspace_bytes, pkv_call_options* options,
+                                      void* stream) {
+  Choice ch;
+  const Report report{options, ch};
+  pkv_status st = pkv::decode_host_checks(out, q, cache, block_tables, max_blocks_per_seq,
+                                          seq_lens, num_seqs, num_heads, max_seq_len, scale,
+                                          window_left, partition_size, options);
   if (st != PKV_OK) return st;
-  if (window_left < -1) return PKV_ERR_SHAPE;
-  if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_blocks_per_seq <= 0)
-    return PKV_ERR_SHAPE;
-  if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
-    return PKV_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  st = read_options(options, &ch);
+  if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !block_tables || !seq_lens) return PKV_ERR_NULL;
-  if (!aligned16(out) || !aligned16(q)) return PKV_ERR_ALIGN;
   const int32_t P = pkv_choose_partition_size(num_seqs, num_heads, cache->num_kv_heads,
                                               max_seq_len, partition_size);
-  if (P < 0) return PKV_ERR_SHAPE;
   const int32_t ns = num_splits_for(max_seq_len, P);
-  if (ns > kMaxGridY) return PKV_ERR_UNSUPPORTED;
   if (ns > 1) {
     const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
                                                       cache->head_size, max_seq_len, P);
@@ -687,14 +748,14 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
                          num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
   a.mode = pkv::kModeDecode;
   a.window_left = window_left;
-  st = plan_seq_order(a, cache, workspace, s);
+  st = plan_seq_order(a, cache, workspace, s, ch);
   if (st != PKV_OK) return st;
   int tslot = 0;
   const bool timed = timing_begin(s, &tslot);
-  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s);
+  st = launch_one_row(a, cache, (unsigned)ns, num_seqs, s, ch);
   if (timed) timing_end(s, tslot);
   if (st != PKV_OK) return st;
-  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s);
+  if (ns > 1) st = launch_reduce(a, io_dtype(cache->dtype), cache->head_size, s, ch);
   return st;
 }
 
@@ -705,10 +766,15 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
                                       int32_t max_query_len, int32_t max_seq_len, float scale,
                                       int32_t causal, int32_t window_left, int32_t partition_size,
                                       float* lse_out, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+                                      pkv_call_options* options, void* stream) {
+  Choice ch;
+  const Report report{options, ch};
+  const pkv_status st = read_options(options, &ch);
+  if (st != PKV_OK) return st;
   return varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
                      num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
-                     window_left, partition_size, lse_out, workspace, workspace_bytes, stream, 0);
+                     window_left, partition_size, lse_out, workspace, workspace_bytes, stream, 0,
+                     ch);
 }
 
 size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
@@ -763,8 +829,13 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
                                  int32_t num_tokens, int32_t num_heads, int32_t max_query_len,
                                  int32_t max_seq_len, int32_t common_prefix_len, float scale,
                                  int32_t causal, int32_t partition_size, float* lse_out,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
-  pkv_status st = check_cache(cache, num_heads);
+                                 void* workspace, size_t workspace_bytes,
+                                 pkv_call_options* options, void* stream) {
+  Choice ch;
+  const Report report{options, ch};
+  pkv_status st = read_options(options, &ch);
+  if (st != PKV_OK) return st;
+  st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
       max_query_len < 0 || max_blocks_per_seq <= 0)
@@ -781,7 +852,9 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   if (cpl == 0)
     return varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
                        num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
-                       -1, partition_size, lse_out, workspace, workspace_bytes, stream, 0);
+                       -1, partition_size, lse_out, workspace, workspace_bytes, stream, 0, ch);
+  // the prefix pass is the prefill kernel: row maxima of the unscaled logits
+  if (!(scale > 0.f)) return PKV_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !block_tables || !seq_lens || !cu_seqlens_q || !prefix_blocks)
     return PKV_ERR_NULL;
@@ -811,7 +884,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   p.ws_lse = reinterpret_cast<float*>(ws + lay.pre_lse);
   float* lse_suffix = reinterpret_cast<float*>(ws + lay.suf_lse);
   const int group = num_heads / cache->num_kv_heads;
-  if (max_query_len <= 1 && use_cascade_launch(cache, group)) {
+  if (max_query_len <= 1 && use_cascade_launch(cache, group, ch)) {
     // 1 + 2 in one persistent launch: prefix items on the matrix cores beside
     // the decode rows of the suffix pass
     const PrefixGeometry gf = prefix_geometry(num_tokens, num_heads, cache->num_kv_heads, cpl,
@@ -832,7 +905,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     d.kv_start = cpl;
     int32_t* plan = reinterpret_cast<int32_t*>(ws + lay.plan);
     d.seq_order = plan;
-    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns);
+    const auto [gx_d, gparts] = mfma_decode_geometry(d, cache, (unsigned)ns, false);
     pkv::MixedGrid mg{};
     mg.pre_x = (int32_t)gf.qtiles;
     mg.pre_y = (int32_t)gf.gy;
@@ -845,18 +918,21 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     mg.queues = plan + num_seqs;
     mg.workgroups = 2 * device_cus();
     if (mg.workgroups <= 0 || mg.n_dec >= (int64_t)INT32_MAX) return PKV_ERR_HIP;
+    ch.ran |= PKV_RAN_PLANNER;
     if (pkv::launch_seq_order(seq_lens, num_seqs, max_seq_len, plan, nullptr, num_tokens, nullptr,
                               nullptr, mg.queues, s) != hipSuccess)
       return PKV_ERR_HIP;
     int tslot = 0;
     const bool timed = timing_begin(s, &tslot);
+    ch.ran |= PKV_RAN_CASCADE_ONE;
     if (pkv::launch_attn_cascade(p, d, mg, cache->block_size, is_fp8(cache), s) != hipSuccess)
       st = PKV_ERR_HIP;
     if (timed) timing_end(s, tslot);
     if (st != PKV_OK) return st;
-    if (ns > 1) st = launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s);
+    if (ns > 1) st = launch_reduce(d, io_dtype(cache->dtype), cache->head_size, s, ch);
     if (st != PKV_OK) return st;
   } else {
+    ch.ran |= PKV_RAN_PREFIX;
     if (pkv::launch_attn_mfma_prefix(p, cache->block_size, is_fp8(cache),
                                      dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
       return PKV_ERR_HIP;
@@ -864,13 +940,14 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     st = varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
                      num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
                      -1, partition_size, lse_suffix, vw ? ws + lay.varlen : nullptr, vw, stream,
-                     cpl);
+                     cpl, ch);
     if (st != PKV_OK) return st;
   }
   // 3. merge of the two results, in place in out
   AttnArgs m = p;
   m.cu_seqlens_q = cu_seqlens_q;
   m.lse_out = lse_out;
+  ch.ran |= PKV_RAN_CASCADE_MERGE;
   if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, s) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }

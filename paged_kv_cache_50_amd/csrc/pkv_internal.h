@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pagedkv.h"
+
 namespace pkv {
 
 // How the attention kernels map grid.z to work.
@@ -79,6 +81,15 @@ struct KvWriteArgs {
   const float* k_scale;            // fp8 caches: per-kv-head scales, else nullptr
   const float* v_scale;
 };
+
+// Host checks of pkv_paged_attention_decode's arguments, all but the
+// workspace: PKV_OK when the call would go on to launch (or, for
+// num_seqs == 0, return PKV_OK without launching).
+pkv_status decode_host_checks(const void* out, const void* q, const pkv_kv_cache* cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t max_seq_len, float scale, int32_t window_left,
+                              int32_t partition_size, const pkv_call_options* options);
 
 // Benchmark timing (timing.cpp): timing_begin returns true, with a slot, when
 // this launch is one of the sampled ones and its start event was recorded;

@@ -38,6 +38,50 @@ class PkvKvCache(ctypes.Structure):
     ]
 
 
+# PKV_RAN_* bits of pkv_call_options.launched: the kernels a call enqueued
+RAN_PLANNER = 0x001
+RAN_DECODE_VALU = 0x002
+RAN_DECODE_MFMA = 0x004
+RAN_DECODE_PAIRS = 0x008
+RAN_PREFILL_MFMA = 0x010
+RAN_PREFILL_VALU = 0x020
+RAN_MIXED = 0x040
+RAN_PREFIX = 0x080
+RAN_CASCADE_ONE = 0x100
+RAN_SPLIT_MERGE = 0x200
+RAN_CASCADE_MERGE = 0x400
+RAN_NAMES = {RAN_PLANNER: "planner", RAN_DECODE_VALU: "decode_valu",
+             RAN_DECODE_MFMA: "decode_mfma", RAN_DECODE_PAIRS: "decode_fp8_head_pairs",
+             RAN_PREFILL_MFMA: "prefill_mfma", RAN_PREFILL_VALU: "prefill_valu",
+             RAN_MIXED: "mixed_one_launch", RAN_PREFIX: "cascade_prefix_pass",
+             RAN_CASCADE_ONE: "cascade_one_launch", RAN_SPLIT_MERGE: "split_merge",
+             RAN_CASCADE_MERGE: "cascade_merge"}
+
+
+class CallOptions(ctypes.Structure):
+    """pkv_call_options: per-call launch choices (0 = the library's) and, after
+    the call, `launched`, the RAN_* bits of the kernels it enqueued."""
+    _fields_ = [
+        ("decode_kernel", ctypes.c_int32),    # 1 VALU, 2 matrix cores
+        ("prefill_kernel", ctypes.c_int32),   # 1 VALU rows
+        ("fp8_head_pairs", ctypes.c_int32),   # 1 one kv head per wave
+        ("mixed_launch", ctypes.c_int32),     # 1 separate launches
+        ("cascade_launch", ctypes.c_int32),   # 1 separate launches
+        ("launched", ctypes.c_uint32),
+    ]
+
+    def ran(self):
+        """Names of the kernels the last call with these options enqueued."""
+        return [n for b, n in sorted(RAN_NAMES.items()) if self.launched & b]
+
+
+def _opts(options):
+    """A CallOptions from None, a CallOptions, or a dict of its fields."""
+    if options is None or isinstance(options, CallOptions):
+        return options
+    return CallOptions(**options)
+
+
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -53,13 +97,14 @@ _SIGS = {
     "pkv_choose_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _i32, _vp,
-                                          _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz, _vp]),
+                                          _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz,
+                                          ctypes.POINTER(CallOptions), _vp]),
     "pkv_paged_attention_varlen": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
-                                          _vp, _vp, _sz, _vp]),
+                                          _vp, _vp, _sz, ctypes.POINTER(CallOptions), _vp]),
     "pkv_cascade_attention": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp, _i32,
                                      _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
-                                     _vp, _vp, _sz, _vp]),
+                                     _vp, _vp, _sz, ctypes.POINTER(CallOptions), _vp]),
     "pkv_cascade_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_cascade_reason": (ctypes.c_char_p, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_validate_cascade": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, ctypes.c_char_p,
@@ -227,13 +272,22 @@ def _meta(t, name):
         raise TypeError(f"{name} must be a contiguous int32 tensor")
 
 
-def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-                           max_seq_len: int, partition_size: int = 0, workspace=None,
-                           lse_out=None, k_scale=None, v_scale=None, window_left: int = -1):
-    """Decode attention, one query row per sequence.  out/q: [S, Hq, D].
-    max_seq_len is a host-side upper bound of seq_lens (no device sync).
-    window_left >= 0: sliding window (keys seq_len - 1 - window_left ..)."""
-    _require_gpu(out, q, block_tables, seq_lens, workspace, lse_out)
+def _check_lse(lse_out, rows, heads, what):
+    """lse_out is optional; the kernels write float32 [rows, heads] through it."""
+    torch = _torch()
+    if lse_out is None:
+        return
+    if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (rows, heads)
+            or not lse_out.is_contiguous()):
+        raise ValueError(f"lse_out must be a contiguous float32 [{what}, num_heads]")
+
+
+def _byref(options):
+    return None if options is None else ctypes.byref(options)
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, lse_out, k_scale, v_scale):
+    _require_gpu(out, q, block_tables, seq_lens, lse_out)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     _meta(block_tables, "block_tables")
     _meta(seq_lens, "seq_lens")
@@ -242,14 +296,30 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
     S, Hq, D = q.shape
     if out.shape != q.shape or D != k_cache.shape[3] or block_tables.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("shape mismatch")
-    if lse_out is not None and (tuple(lse_out.shape) != (S, Hq) or not lse_out.is_contiguous()):
-        raise ValueError("lse_out must be a contiguous float32 [num_seqs, num_heads]")
+    _check_lse(lse_out, S, Hq, "num_seqs")
+    return desc, S, Hq, D
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                           max_seq_len: int, partition_size: int = 0, workspace=None,
+                           lse_out=None, k_scale=None, v_scale=None, window_left: int = -1,
+                           options=None):
+    """Decode attention, one query row per sequence.  out/q: [S, Hq, D].
+    max_seq_len is a host-side upper bound of seq_lens (no device sync).
+    window_left >= 0: sliding window (keys seq_len - 1 - window_left ..).
+    options: a CallOptions (or dict of its fields); its `launched` holds the
+    kernels the call enqueued."""
+    _require_gpu(workspace)
+    desc, S, Hq, D = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, lse_out,
+                                  k_scale, v_scale)
+    options = _opts(options)
     need = workspace_bytes(S, Hq, desc.num_kv_heads, D, max_seq_len, partition_size)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     _check(lib().pkv_paged_attention_decode(
         out.data_ptr(), q.data_ptr(), ctypes.byref(desc), block_tables.data_ptr(),
         block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
-        int(window_left), int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
+        int(window_left), int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes,
+        _byref(options), _stream(q)),
         "paged_attention_decode")
     return out
 
@@ -257,9 +327,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
 def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
                            scale: float, max_query_len: int, max_seq_len: int, causal: bool = True,
                            partition_size: int = 0, workspace=None, lse_out=None,
-                           k_scale=None, v_scale=None, window_left: int = -1):
+                           k_scale=None, v_scale=None, window_left: int = -1, options=None):
     """Variable-length attention over a flattened batch (q/out [T, Hq, D]).
-    window_left >= 0: sliding window (symmetric when not causal)."""
+    window_left >= 0: sliding window (symmetric when not causal).  options
+    as for paged_attention_decode."""
     _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
@@ -270,15 +341,16 @@ def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, blo
     S = seq_lens.shape[0]
     if out.shape != q.shape or cu_seqlens_q.shape[0] != S + 1 or block_tables.shape[0] != S:
         raise ValueError("shape mismatch")
-    if lse_out is not None and (tuple(lse_out.shape) != (T, Hq) or not lse_out.is_contiguous()):
-        raise ValueError("lse_out must be a contiguous float32 [num_tokens, num_heads]")
+    _check_lse(lse_out, T, Hq, "num_tokens")
+    options = _opts(options)
     need = workspace_bytes(S, Hq, desc.num_kv_heads, D, max_seq_len, partition_size)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
     _check(lib().pkv_paged_attention_varlen(
         out.data_ptr(), q.data_ptr(), ctypes.byref(desc), cu_seqlens_q.data_ptr(),
         seq_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], S, T, Hq,
         int(max_query_len), int(max_seq_len), float(scale), 1 if causal else 0, int(window_left),
-        int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)),
+        int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes, _byref(options),
+        _stream(q)),
         "paged_attention_varlen")
     return out
 
@@ -304,7 +376,7 @@ def cascade_reason(common_prefix_len, num_seqs, num_tokens, num_heads, num_kv_he
 def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables,
                       prefix_blocks, common_prefix_len: int, scale: float, max_query_len: int,
                       max_seq_len: int, causal: bool = True, partition_size: int = 0,
-                      workspace=None, lse_out=None, k_scale=None, v_scale=None):
+                      workspace=None, lse_out=None, k_scale=None, v_scale=None, options=None):
     """Cascade (shared-prefix) attention over a flattened batch (q/out
     [T, Hq, D]): the result of paged_attention_varlen on the same arguments,
     with the prefix blocks (int32 [common_prefix_len / block_size], shared
@@ -323,8 +395,8 @@ def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_ta
         raise ValueError("shape mismatch")
     if prefix_blocks.shape[0] * k_cache.shape[1] < common_prefix_len:
         raise ValueError("prefix_blocks shorter than the prefix")
-    if lse_out is not None and (tuple(lse_out.shape) != (T, Hq) or not lse_out.is_contiguous()):
-        raise ValueError("lse_out must be a contiguous float32 [num_tokens, num_heads]")
+    _check_lse(lse_out, T, Hq, "num_tokens")
+    options = _opts(options)
     need = cascade_workspace_bytes(S, T, Hq, desc.num_kv_heads, D, max_seq_len, common_prefix_len,
                                    partition_size)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
@@ -333,7 +405,8 @@ def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_ta
         seq_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
         prefix_blocks.data_ptr(), S, T, Hq, int(max_query_len), int(max_seq_len),
         int(common_prefix_len), float(scale), 1 if causal else 0, int(partition_size),
-        _ptr(lse_out), _ptr(workspace), ws_bytes, _stream(q)), "cascade_attention")
+        _ptr(lse_out), _ptr(workspace), ws_bytes, _byref(options), _stream(q)),
+        "cascade_attention")
     return out
 
 

@@ -519,3 +519,42 @@ def attention_flops(w: Workload) -> int:
             keys = int(ql[s] * L[s])
         total += 4 * w.num_heads * w.head_size * keys
     return total
+
+
+# --------------------------------------------------------------------------
+# Device copies of a workload (for the GPU tests, the smoke check and the
+# benchmark): the same arrays, moved as raw bits.
+# --------------------------------------------------------------------------
+
+def np_to_dev(x: np.ndarray, dtype: str, device="cuda"):
+    """A device tensor holding the bits of x: bfloat16 bits (uint16) as
+    torch.bfloat16, e4m3 codes (uint8) as torch.float8_e4m3fn, else as is."""
+    import torch as t
+    if dtype == "bf16":
+        return t.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(t.bfloat16).to(device)
+    if dtype == "fp8":
+        return t.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device).view(t.float8_e4m3fn)
+    return t.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+class DevWorkload:
+    """Device copies of a Workload's tensors."""
+
+    def __init__(self, w: Workload, device="cuda"):
+        import torch as t
+        self.w = w
+        self.q = np_to_dev(w.q, w.io_dtype, device)
+        self.k_cache = np_to_dev(w.k_cache, w.dtype, device)
+        self.v_cache = np_to_dev(w.v_cache, w.dtype, device)
+        self.block_tables = t.from_numpy(w.block_tables).to(device)
+        self.seq_lens = t.from_numpy(w.seq_lens).to(device)
+        self.cu_seqlens_q = None if w.cu_seqlens_q is None else t.from_numpy(w.cu_seqlens_q).to(device)
+        self.key_new = None if w.key_new is None else np_to_dev(w.key_new, w.io_dtype, device)
+        self.value_new = None if w.value_new is None else np_to_dev(w.value_new, w.io_dtype, device)
+        self.k_scale = None if w.k_scale is None else t.from_numpy(w.k_scale).to(device)
+        self.v_scale = None if w.v_scale is None else t.from_numpy(w.v_scale).to(device)
+        self.slot_mapping = None if w.slot_mapping is None else t.from_numpy(w.slot_mapping).to(device)
+        self.prefix_blocks = (t.from_numpy(w.prefix_blocks).to(device)
+                              if w.common_prefix_len > 0 else None)
+        self.out = t.empty_like(self.q)
+        self.lse = t.empty(self.q.shape[0], self.q.shape[1], dtype=t.float32, device=device)

@@ -16,7 +16,7 @@ Writes profiles/<kernel>__<workload>.md for the dominant kernel of every
 workload and updates profiles/traffic.json (keyed by workload name), which
 bench.py reads while the kernel's sources are unchanged.
 
-Usage: python -m paged_kv_cache_50_amd.profsummary PROF_DIR [--workloads 2 3 4 5]
+Usage: python profsummary.py PROF_DIR [--workloads 2 3 4 5]
        [--out profiles]
 """
 from __future__ import annotations
@@ -29,7 +29,7 @@ import os
 import statistics
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
@@ -38,7 +38,7 @@ COPY_BYTES = 1 << 30
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof/trace_w{n} "
              "-o t -- python3 $REPO/bench.py --workload {n} --steps 50 --warmup 200 --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/prof/{tag}_w{n} -o {o} "
-           "-- python3 $REPO/bench.py --workload {n} --steps 3 --warmup 1 --no-cpu-baseline")
+           "-- python3 $REPO/bench.py --workload {n} --steps 3 --warmup 1 --warmup-s 0 --no-cpu-baseline")
 COPY_CMD = ("rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/prof/{tag}_copy -o {o} "
             "-- python3 $REPO/bench.py --copy-calibration 1024")
 

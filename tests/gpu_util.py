@@ -6,12 +6,17 @@ from __future__ import annotations
 import numpy as np
 
 from paged_kv_cache_50_amd import workloads as W
+from paged_kv_cache_50_amd.workloads import DevWorkload, np_to_dev  # noqa: F401
 
 # Tolerances (stated by the benchmark spec for this path):
 #   float32 inputs: max |gpu - ref| <= 1e-5
 #   bfloat16 inputs, fp32 accumulation: |gpu - ref| <= 2e-2 + 1e-2 * |ref| per
 #   element, plus a relative L2 gate ||gpu - ref|| / ||ref|| <= 1e-2 so that a
 #   near-zero output cannot pass on the absolute term alone.
+# (label, pairs, seconds, threads) of every full oracle run, for the summary
+# that tests/conftest.py prints at the end of a session
+ORACLE_TIMES = []
+
 F32_ATOL = 1e-5
 BF16_ATOL = 2e-2
 BF16_RTOL = 1e-2
@@ -21,15 +26,6 @@ BF16_REL_L2 = 1e-2
 def torch():
     import torch as _t
     return _t
-
-
-def np_to_dev(x: np.ndarray, dtype: str, device="cuda"):
-    t = torch()
-    if dtype == "bf16":
-        return t.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(t.bfloat16).to(device)
-    if dtype == "fp8":
-        return t.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device).view(t.float8_e4m3fn)
-    return t.from_numpy(np.ascontiguousarray(x)).to(device)
 
 
 def dev_to_bits(t_):
@@ -47,32 +43,11 @@ def dev_to_f64(t_) -> np.ndarray:
     return t_.detach().float().cpu().numpy().astype(np.float64)
 
 
-class DevWorkload:
-    """Device copies of a Workload's tensors."""
-
-    def __init__(self, w: W.Workload, device="cuda"):
-        t = torch()
-        self.w = w
-        self.q = np_to_dev(w.q, w.io_dtype, device)
-        self.k_cache = np_to_dev(w.k_cache, w.dtype, device)
-        self.v_cache = np_to_dev(w.v_cache, w.dtype, device)
-        self.block_tables = t.from_numpy(w.block_tables).to(device)
-        self.seq_lens = t.from_numpy(w.seq_lens).to(device)
-        self.cu_seqlens_q = None if w.cu_seqlens_q is None else t.from_numpy(w.cu_seqlens_q).to(device)
-        self.key_new = None if w.key_new is None else np_to_dev(w.key_new, w.io_dtype, device)
-        self.value_new = None if w.value_new is None else np_to_dev(w.value_new, w.io_dtype, device)
-        self.k_scale = None if w.k_scale is None else t.from_numpy(w.k_scale).to(device)
-        self.v_scale = None if w.v_scale is None else t.from_numpy(w.v_scale).to(device)
-        self.slot_mapping = None if w.slot_mapping is None else t.from_numpy(w.slot_mapping).to(device)
-        self.prefix_blocks = (t.from_numpy(w.prefix_blocks).to(device)
-                              if w.common_prefix_len > 0 else None)
-        self.out = t.empty_like(self.q)
-        self.lse = t.empty(self.q.shape[0], self.q.shape[1], dtype=t.float32, device=device)
-
-
-def run(dw: DevWorkload, partition_size=None, lse=True, write=True):
+def run(dw: DevWorkload, partition_size=None, lse=True, write=True, options=None):
     """One step of the hot path on the GPU: the slot write (if the workload
-    has new tokens) and attention.  Returns the output tensor."""
+    has new tokens) and attention.  options: launch choices for the attention
+    call (pagedkv.CallOptions or a dict of its fields).  Returns the output
+    tensor."""
     from paged_kv_cache_50_amd import pagedkv
     w = dw.w
     ps = w.partition_size if partition_size is None else partition_size
@@ -83,18 +58,20 @@ def run(dw: DevWorkload, partition_size=None, lse=True, write=True):
         pagedkv.paged_attention_decode(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
                                        dw.seq_lens, w.scale, w.max_seq_len, partition_size=ps,
                                        lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
-                                       v_scale=dw.v_scale, window_left=w.window_left)
+                                       v_scale=dw.v_scale, window_left=w.window_left,
+                                       options=options)
     else:
         pagedkv.paged_attention_varlen(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.cu_seqlens_q,
                                        dw.seq_lens, dw.block_tables, w.scale, w.max_query_len,
                                        w.max_seq_len, causal=w.causal, partition_size=ps,
                                        lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
-                                       v_scale=dw.v_scale, window_left=w.window_left)
+                                       v_scale=dw.v_scale, window_left=w.window_left,
+                                       options=options)
     return dw.out
 
 
 def run_cascade(dw: DevWorkload, partition_size=None, lse=True, write=True,
-                common_prefix_len=None):
+                common_prefix_len=None, options=None):
     """One cascade step: the slot write, then cascade attention with the
     workload's shared prefix (or common_prefix_len tokens of it)."""
     from paged_kv_cache_50_amd import pagedkv
@@ -109,7 +86,7 @@ def run_cascade(dw: DevWorkload, partition_size=None, lse=True, write=True,
                               dw.block_tables, pre, cpl, w.scale, w.max_query_len, w.max_seq_len,
                               causal=w.causal, partition_size=ps,
                               lse_out=dw.lse if lse else None, k_scale=dw.k_scale,
-                              v_scale=dw.v_scale)
+                              v_scale=dw.v_scale, options=options)
     return dw.out
 
 
@@ -135,6 +112,65 @@ def reference(w: W.Workload, pairs=None):
                                   w.dtype, cu_seqlens_q=w.cu_seqlens_q, causal=w.causal,
                                   pairs=pairs, k_scale=w.k_scale, v_scale=w.v_scale,
                                   window_left=w.window_left)
+
+
+def reference_full(w: W.Workload, threads=None, what=""):
+    """The oracle over every (sequence, kv head) pair of a workload, in a
+    thread pool (the per-pair oracle spends its time in NumPy calls that
+    release the GIL).  Returns out, lse as reference() does, and prints the
+    oracle's wall time."""
+    import concurrent.futures as cf
+    import os
+    import time
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+    kc, vc = oracle_inputs(w)
+    Hkv = w.num_kv_heads
+    g = w.num_heads // Hkv
+    cu = w.cu_seqlens_q
+
+    def rows(s):
+        return (s, s + 1) if cu is None else (int(cu[s]), int(cu[s + 1]))
+
+    pairs = [(s, h) for s in range(w.num_seqs) for h in range(Hkv)]
+    # longest work first, so the pool's tail is short
+    pairs.sort(key=lambda p: -int(w.seq_lens[p[0]]) * (rows(p[0])[1] - rows(p[0])[0] + 8))
+    out = np.full(w.q.shape, np.nan)
+    lse = np.full(w.q.shape[:2], np.nan)
+
+    def job(p):
+        s, h = p
+        r0, r1 = rows(s)
+        if r1 <= r0:
+            return
+        o, l = oracle.attention_seq_kvhead(w.q, kc, vc, w.block_tables[s], int(w.seq_lens[s]),
+                                           r0, r1, h, w.num_heads, w.scale, w.block_size, w.dtype,
+                                           w.causal, k_scale=w.k_scale, v_scale=w.v_scale,
+                                           window_left=w.window_left)
+        out[r0:r1, h * g:(h + 1) * g] = o
+        lse[r0:r1, h * g:(h + 1) * g] = l
+
+    n = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with threadpool_limits(1), cf.ThreadPoolExecutor(n) as ex:
+        list(ex.map(job, pairs))
+    el = time.perf_counter() - t0
+    ORACLE_TIMES.append((what or w.name, len(pairs), el, n))
+    print(f"[oracle] {what or w.name}: {len(pairs)} (sequence, kv head) pairs in "
+          f"{el:.1f} s on {n} threads", flush=True)
+    return out, lse
+
+
+def assert_all_rows(gpu: np.ndarray, gpu_lse: np.ndarray, ref: np.ndarray, ref_lse: np.ndarray,
+                    dtype: str, what=""):
+    """Every output element finite and within tolerance, every lse within
+    tolerance, for rows that belong to a sequence (the oracle leaves other
+    rows NaN)."""
+    owned = ~np.isnan(ref_lse)
+    assert np.isfinite(gpu[owned]).all(), f"{what}: non-finite GPU output"
+    assert_close(gpu, ref, dtype, what)
+    lse_close(gpu_lse, ref_lse, what)
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):

@@ -94,7 +94,7 @@ def cache(k=A16, v=A16 + 4096, dtype=1, nb=100, bs=16, hkv=8, d=128, stride=0):
 def decode(L, c, out=A16, q=A16, bt=A16, sl=A16, S=4, Hq=32, max_len=1000, ps=0, ws=None, wsb=0,
            mb=64, win=-1):
     return L.pkv_paged_attention_decode(out, q, ctypes.byref(c), bt, mb, sl, S, Hq, max_len, 0.1,
-                                        win, ps, None, ws, wsb, None)
+                                        win, ps, None, ws, wsb, None, None)
 
 
 def test_decode_error_codes(L):
@@ -126,11 +126,17 @@ def test_varlen_and_write_error_codes(L):
     c = cache()
     f = L.pkv_paged_attention_varlen
     assert f(A16, A16, ctypes.byref(c), None, A16, A16, 64, 4, 10, 32, 5, 1000, 0.1, 1, -1, 0,
-             None, None, 0, None) == 1                           # NULL cu_seqlens_q
+             None, None, 0, None, None) == 1                           # NULL cu_seqlens_q
     assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, -1, 1000, 0.1, 1, -1, 0,
-             None, None, 0, None) == 2                           # negative max_query_len
+             None, None, 0, None, None) == 2                           # negative max_query_len
     assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 0, 32, 5, 1000, 0.1, 1, -1, 0,
-             None, None, 0, None) == 0                           # no tokens: no-op
+             None, None, 0, None, None) == 0                           # no tokens: no-op
+    # the prefill kernels need a positive scale; the decode kernels take any
+    for scale in (0.0, -0.1):
+        assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, 5, 1000, scale, 1, -1, 0,
+                 None, None, 0, None, None) == 2
+    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, 5, 1000, float("nan"), 1,
+             -1, 0, None, None, 0, None, None) == 2
     w = L.pkv_kv_cache_write
     assert w(ctypes.byref(c), None, A16, A16, 10, None) == 1
     assert w(ctypes.byref(c), A_ODD, A16, A16, 10, None) == 4
@@ -189,3 +195,43 @@ def test_binding_refuses_cpu_tensors(L):
     k = torch.zeros(4, 16, 2, 64)
     with pytest.raises(ValueError):
         pagedkv.cache_descriptor(k, k)
+
+
+def test_call_options_are_checked_and_reported(L):
+    c = cache()
+    for field, bad in (("decode_kernel", 3), ("decode_kernel", -1), ("prefill_kernel", 2),
+                       ("fp8_head_pairs", 2), ("mixed_launch", 2), ("cascade_launch", -1)):
+        o = pagedkv.CallOptions(**{field: bad})
+        o.launched = 0xFFFF
+        assert L.pkv_paged_attention_decode(A16, A16, ctypes.byref(c), A16, 64, A16, 4, 32, 1000,
+                                            0.1, -1, 0, None, None, 0, ctypes.byref(o),
+                                            None) == 2, field
+        assert o.launched == 0                   # the report is written on every path
+    o = pagedkv.CallOptions(decode_kernel=2)
+    o.launched = 7
+    assert decode(L, c, S=0) == 0                 # an empty batch launches nothing
+    assert L.pkv_paged_attention_decode(A16, A16, ctypes.byref(c), A16, 64, A16, 0, 32, 1000,
+                                        0.1, -1, 0, None, None, 0, ctypes.byref(o), None) == 0
+    assert o.launched == 0 and o.ran() == []
+    assert pagedkv.CallOptions(launched=pagedkv.RAN_MIXED | pagedkv.RAN_SPLIT_MERGE).ran() == \
+        ["mixed_one_launch", "split_merge"]
+
+
+def test_cascade_needs_positive_scale(L):
+    c = cache()
+    f = L.pkv_cascade_attention
+    need = pagedkv.cascade_workspace_bytes(4, 10, 32, 8, 128, 1000, 256)
+    for scale in (0.0, -1.0):
+        assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, A16, 4, 10, 32, 5, 1000, 256, scale,
+                 1, 0, None, A16, need, None, None) == 2
+
+
+def test_lse_out_must_be_float32():
+    torch = pytest.importorskip("torch")
+    pagedkv._check_lse(None, 4, 8, "num_seqs")
+    pagedkv._check_lse(torch.empty(4, 8, dtype=torch.float32), 4, 8, "num_seqs")
+    for bad in (torch.empty(4, 8, dtype=torch.bfloat16), torch.empty(4, 8, dtype=torch.float16),
+                torch.empty(4, 8, dtype=torch.float64), torch.empty(8, 4, dtype=torch.float32),
+                torch.empty(8, 4, dtype=torch.float32).t()):
+        with pytest.raises(ValueError):
+            pagedkv._check_lse(bad, 4, 8, "num_seqs")

@@ -15,7 +15,7 @@ from tests.test_abi_cpu import A16, A_ODD, L, cache  # noqa: F401  (fixture)
 def cascade(Lib, c, out=A16, q=A16, cu=A16, sl=A16, bt=A16, mb=400, pre=A16, S=16, T=16,
             Hq=32, mq=1, max_len=5000, cpl=4096, ps=0, ws=A16, wsb=1 << 40):
     return Lib.pkv_cascade_attention(out, q, ctypes.byref(c), cu, sl, bt, mb, pre, S, T, Hq, mq,
-                                     max_len, cpl, 0.1, 1, ps, None, ws, wsb, None)
+                                     max_len, cpl, 0.1, 1, ps, None, ws, wsb, None, None)
 
 
 def test_cascade_error_codes(L):
