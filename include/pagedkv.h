@@ -222,6 +222,36 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
                                       void* stream);
 
 /*
+ * pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc.  It runs the same kernels with the
+ * same results; the split partials and the sequence order that the workspace
+ * would hold live instead in a scratch array of PKV_NOALLOC_SCRATCH_BYTES in
+ * the library's device memory, one per GPU, held from the first call on that
+ * GPU to the end of the process.  The call allocates nothing.
+ *   Limit: a call for which pkv_attention_workspace_bytes(num_seqs,
+ *   num_heads, num_kv_heads, head_size, max_seq_len, partition_size) exceeds
+ *   PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_WORKSPACE (128 MiB holds, for
+ *   example, 256 sequences of 32 query heads up to 8192 tokens with
+ *   512-token partitions).
+ *   Every call on one GPU shares that GPU's array: calls that may overlap in
+ *   time on one GPU (on different streams, or from threads that do not
+ *   order them) race and give undefined results.  Order them on one stream.
+ *   Nothing in the array needs to be cleared between calls.
+ * Arguments and errors otherwise as for pkv_paged_attention_decode; PKV_ERR_HIP
+ * also when the device's scratch address cannot be obtained.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const pkv_kv_cache* cache,
+                                              const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                              int32_t num_seqs, int32_t num_heads,
+                                              int32_t max_seq_len, float scale,
+                                              int32_t window_left, int32_t partition_size,
+                                              float* lse_out, pkv_call_options* options,
+                                              void* stream);
+
+/*
  * Variable-length attention over a flattened batch (ch. 6 "Structure des
  * métadonnées": query_start_loc / seq_lens; «Khám phá vLLM» "Chạy forward
  * pass": all sequences flattened into one super-sequence).  Sequence s owns

@@ -56,6 +56,7 @@ RAN_NAMES = {RAN_PLANNER: "planner", RAN_DECODE_VALU: "decode_valu",
              RAN_MIXED: "mixed_one_launch", RAN_PREFIX: "cascade_prefix_pass",
              RAN_CASCADE_ONE: "cascade_one_launch", RAN_SPLIT_MERGE: "split_merge",
              RAN_CASCADE_MERGE: "cascade_merge"}
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class CallOptions(ctypes.Structure):
@@ -99,6 +100,9 @@ _SIGS = {
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _i32, _vp,
                                           _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp, _sz,
                                           ctypes.POINTER(CallOptions), _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _i32,
+                                                  _vp, _i32, _i32, _i32, _f32, _i32, _i32, _vp,
+                                                  ctypes.POINTER(CallOptions), _vp]),
     "pkv_paged_attention_varlen": (_i32, [_vp, _vp, ctypes.POINTER(PkvKvCache), _vp, _vp, _vp,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
                                           _vp, _vp, _sz, ctypes.POINTER(CallOptions), _vp]),
@@ -321,6 +325,25 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, seq_lens, sca
         int(window_left), int(partition_size), _ptr(lse_out), _ptr(workspace), ws_bytes,
         _byref(options), _stream(q)),
         "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                   scale: float, max_seq_len: int, partition_size: int = 0,
+                                   lse_out=None, k_scale=None, v_scale=None,
+                                   window_left: int = -1, options=None):
+    """paged_attention_decode without a workspace: the split partials live in
+    the library's per-GPU scratch array (NOALLOC_SCRATCH_BYTES), so neither
+    the library nor this wrapper allocates device memory.  Calls on one GPU
+    that may overlap in time race; order them on one stream."""
+    desc, S, Hq, D = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, lse_out,
+                                  k_scale, v_scale)
+    options = _opts(options)
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        out.data_ptr(), q.data_ptr(), ctypes.byref(desc), block_tables.data_ptr(),
+        block_tables.shape[1], seq_lens.data_ptr(), S, Hq, int(max_seq_len), float(scale),
+        int(window_left), int(partition_size), _ptr(lse_out), _byref(options), _stream(q)),
+        "paged_attention_decode_noalloc")
     return out
 
 

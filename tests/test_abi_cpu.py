@@ -235,3 +235,21 @@ def test_lse_out_must_be_float32():
                 torch.empty(8, 4, dtype=torch.float32).t()):
         with pytest.raises(ValueError):
             pagedkv._check_lse(bad, 4, 8, "num_seqs")
+
+
+def test_noalloc_decode_host_errors(L):
+    f = L.pkv_paged_attention_decode_noalloc
+    c = cache()
+    args = lambda cc, S, max_len: (A16, A16, cc, A16, 64, A16, S, 32, max_len, 0.1, -1, 0, None,
+                                   None, None)
+    assert f(*args(None, 4, 1000)) == 1                               # NULL cache
+    # a call whose split workspace exceeds the scratch array is refused before any launch
+    big_S = 2048
+    assert pagedkv.workspace_bytes(big_S, 32, 8, 128, 8192, 0) > pagedkv.NOALLOC_SCRATCH_BYTES
+    assert f(*args(ctypes.byref(c), big_S, 8192)) == 5
+    assert f(*args(ctypes.byref(cache(dtype=3)), 4, 1000)) == 3       # the decode call's checks
+    assert f(*args(ctypes.byref(c), -1, 1000)) == 2
+    assert f(*args(ctypes.byref(c), 0, 1000)) == 0                    # empty batch: no-op
+    # sizes the scratch array holds: the headline decode batches
+    for S, Hq, Hkv, max_len in ((64, 32, 32, 4096), (256, 32, 8, 8192), (8, 64, 8, 131072)):
+        assert pagedkv.workspace_bytes(S, Hq, Hkv, 128, max_len, 512) <= pagedkv.NOALLOC_SCRATCH_BYTES

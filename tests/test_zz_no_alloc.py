@@ -1,0 +1,100 @@
+"""pkv_paged_attention_decode_noalloc through the C ABI: the decode entry
+point whose split partials live in the library's per-GPU scratch array
+instead of a caller workspace.  Its outputs must be those of
+pkv_paged_attention_decode on the same inputs (the same kernels run), on
+consecutive calls where the second is smaller than the first, and meet the
+oracle's tolerance; neither the library nor the binding allocates.
+"""
+import numpy as np
+import pytest
+
+from paged_kv_cache_50_amd import pagedkv
+from paged_kv_cache_50_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pagedkv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _both(w, ps=None, opts=None):
+    """The workspace entry point and the no-alloc one on the same inputs;
+    returns both outputs and lse as numpy, and the kernels each launched."""
+    torch = G.torch()
+    ps = w.partition_size if ps is None else ps
+    dw = G.DevWorkload(w)
+    o1 = pagedkv.CallOptions(**(opts or {}))
+    G.run(dw, partition_size=ps, options=o1)
+    torch.cuda.synchronize()
+    out1, lse1 = G.dev_to_bits(dw.out).copy(), G.dev_to_f64(dw.lse).copy()
+    dw.out.fill_(7.0)
+    dw.lse.fill_(7.0)
+    torch.cuda.synchronize()
+    o2 = pagedkv.CallOptions(**(opts or {}))
+    before = torch.cuda.memory_allocated()
+    pagedkv.paged_attention_decode_noalloc(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
+                                           dw.seq_lens, w.scale, w.max_seq_len, partition_size=ps,
+                                           lse_out=dw.lse, k_scale=dw.k_scale, v_scale=dw.v_scale,
+                                           window_left=w.window_left, options=o2)
+    assert torch.cuda.memory_allocated() == before
+    torch.cuda.synchronize()
+    out2, lse2 = G.dev_to_bits(dw.out).copy(), G.dev_to_f64(dw.lse).copy()
+    return out1, lse1, out2, lse2, o1.launched, o2.launched, G.dev_to_f64(dw.out)
+
+
+def _check(w, ps=None, opts=None, what=""):
+    out1, lse1, out2, lse2, l1, l2, out_f64 = _both(w, ps, opts)
+    print(f"[gpu-test] no-alloc {what}: kernels {pagedkv.CallOptions(launched=l2).ran()}",
+          flush=True)
+    assert l1 == l2
+    assert np.array_equal(out1, out2), f"{what}: output differs from the workspace entry point"
+    assert np.array_equal(lse1, lse2), f"{what}: lse differs from the workspace entry point"
+    ref, ref_lse = G.reference_full(w, what=what)
+    G.assert_all_rows(out_f64, lse2, ref, ref_lse, "f32" if w.dtype == "f32" else "bf16", what)
+    return l2
+
+
+def test_noalloc_matches_workspace_entry_point_twice_shrinking():
+    # a large GQA decode batch (split, planner, merge), then a smaller one
+    w = W.make_config(3, num_seqs=200, max_len=8192)
+    assert pagedkv.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size,
+                                   w.max_seq_len, 0) > 16 << 20
+    ran = _check(w, what="GQA 200 seqs")
+    assert ran & pagedkv.RAN_PLANNER and ran & pagedkv.RAN_SPLIT_MERGE
+    _check(W.make_config(3, num_seqs=17, max_len=2000), what="GQA 17 seqs")
+
+
+def test_noalloc_other_kernels_consecutive():
+    # the VALU kernel (MHA), then the long-context split, then fp8, then a
+    # batch too short to split (no scratch use at all)
+    _check(W.make_config(2, num_seqs=24, max_len=4096), what="MHA 24 seqs")
+    _check(W.make_config(4, num_seqs=2, max_len=40000), what="long context 2 seqs")
+    _check(W.make_config(7, num_seqs=30, max_len=3000), ps=256, what="fp8 GQA 30 seqs")
+    _check(W.make_config(2, num_seqs=5, max_len=400), ps=-1, what="MHA unsplit")
+    _check(W.make_config(3, num_seqs=9, max_len=1000), ps=128, opts=dict(decode_kernel=1),
+           what="GQA on the VALU kernel")
+
+
+def test_noalloc_refuses_batches_beyond_the_scratch_array():
+    torch = G.torch()
+    w = W.make_config(3, num_seqs=4, max_len=600)
+    dw = G.DevWorkload(w)
+    # claim a longer max_seq_len and a small partition: the split workspace
+    # this would need exceeds the array, so the call is refused before launch
+    S, Hq = w.num_seqs, w.num_heads
+    big = 1 << 20
+    assert pagedkv.choose_partition_size(S, Hq, w.num_kv_heads, big, 256) == 256
+    assert pagedkv.workspace_bytes(S, Hq, w.num_kv_heads, 128, big, 256) > pagedkv.NOALLOC_SCRATCH_BYTES
+    bt = torch.zeros(S, big // w.block_size, dtype=torch.int32, device="cuda")
+    with pytest.raises(pagedkv.PagedKVError) as e:
+        pagedkv.paged_attention_decode_noalloc(dw.out, dw.q, dw.k_cache, dw.v_cache, bt,
+                                               dw.seq_lens, w.scale, big, partition_size=256)
+    assert e.value.status == 5
