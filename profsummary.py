@@ -140,8 +140,10 @@ def main() -> int:
         unit = roof["unit"]
         lines += ["", f"The same run's bench line: {rec['value']} GB/s per step "
                   f"({rec['pct_of_peak']} % of 8 TB/s), {rec['us_per_step']} µs per step; "
-                  f"dominant kernel {roof['kernel_ms'] * 1e3:.2f} µs by the library's HIP events "
-                  f"({roof['launches']} timed launches) = {roof['achieved']} {unit}, "
+                  f"dominant kernel ({roof['kernel']}, launches {', '.join(rec['kernels_launched'])}) "
+                  f"{roof['kernel_ms'] * 1e3:.2f} µs by the library's HIP events "
+                  f"({roof['launches_timed']} timed launches; {roof['kernel_ms_method']}) = "
+                  f"{roof['achieved']} {unit}, "
                   f"{100 * roof['frac']:.1f} % of {roof['peak']} {unit}; trace average "
                   f"{dom[3] / 1e3:.2f} µs.", "",
                   "## HBM traffic (separate counter runs, then a copy calibration)", "", "```",
