@@ -98,3 +98,47 @@ def test_noalloc_refuses_batches_beyond_the_scratch_array():
         pagedkv.paged_attention_decode_noalloc(dw.out, dw.q, dw.k_cache, dw.v_cache, bt,
                                                dw.seq_lens, w.scale, big, partition_size=256)
     assert e.value.status == 5
+
+
+def test_noalloc_graph_capture_replays():
+    """Captured in a HIP graph (the callers this entry point is for), the call
+    replays to its eager result bit for bit, with another no-alloc call run
+    eagerly between the replays (it overwrites the shared scratch array,
+    which holds nothing from one call to the next)."""
+    torch = G.torch()
+    w = W.make_config(3, num_seqs=70, max_len=3000)           # planner, split, merge
+    w2 = W.make_config(2, num_seqs=8, max_len=2500)
+    d, d2 = G.DevWorkload(w), G.DevWorkload(w2)
+
+    def call(dw, ww):
+        pagedkv.paged_attention_decode_noalloc(dw.out, dw.q, dw.k_cache, dw.v_cache,
+                                               dw.block_tables, dw.seq_lens, ww.scale,
+                                               ww.max_seq_len, partition_size=256,
+                                               lse_out=dw.lse)
+
+    call(d, w)
+    torch.cuda.synchronize()
+    want, want_lse = G.dev_to_bits(d.out).copy(), d.lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(d, w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(d, w)
+    for i in range(3):
+        call(d2, w2)
+        d.out.zero_()
+        d.lse.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(G.dev_to_bits(d.out), want), f"replay {i}"
+        assert torch.equal(d.lse, want_lse), f"replay {i} lse"
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(d.out), ref, "bf16", "graph-captured no-alloc decode")
+    ref2, _ = G.reference(w2)
+    G.assert_close(G.dev_to_f64(d2.out), ref2, "bf16", "eager no-alloc decode between replays")
+    del g
