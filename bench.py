@@ -13,7 +13,8 @@ MHA decode unless --workload names another); `roofline` is the dominant
 kernel's achieved rate against the MI355X peak, from per-launch HIP events
 recorded by the library inside the timed region; `per_workload` repeats the
 measurement, in the same run, for the GQA decode, the long-context split
-decode and the mixed chunked-prefill step (default run only); `cpu_baseline`
+decode, the mixed chunked-prefill step and workloads 6-10 (fp8 caches, a
+sliding window, a shared-prefix cascade; default run only); `cpu_baseline`
 times the fp64 CPU oracle on the headline workload (BLAS threads = the
 host cores this process may use) and, single-threaded, on the three small
 decode workloads.
@@ -40,7 +41,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20         # MI355X last-level (Infinity) cache
 
 HEADLINE = 2                   # Llama-7B-shaped MHA decode
-PER_WORKLOAD = (3, 4, 5)       # GQA decode, long-context split decode, mixed step
+# GQA decode, long-context split decode, mixed step, then the fp8, sliding-window and
+# shared-prefix workloads
+PER_WORKLOAD = (3, 4, 5, 6, 7, 8, 9, 10)
 
 WORKLOAD_DESC = {
     1: "4 seqs, 8/8 heads, head 64, block 16, fp32, seq_lens U[1,256], seed 0",
@@ -486,7 +489,7 @@ def main() -> int:
     ap.add_argument("--warmup-s", type=float, default=1.0)
     ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 11)),
                     help="measure only this workload (default: the headline MHA decode, plus "
-                         "the GQA, long-context and mixed workloads as per_workload)")
+                         "workloads 3-10 as per_workload)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -584,6 +587,8 @@ def main() -> int:
             rc = record(wc, mc, args.steps, pc)
             rc["description"] = WORKLOAD_DESC[cfg]
             rc["algorithmic_bytes"] = int(mc["bytes"])
+            if wc.common_prefix_len > 0 and mc["plain_us"]:
+                rc["plain_call_us_per_step"] = round(mc["plain_us"], 2)
             per[wc.name] = rc
             print(f"[bench] {wc.name}: {rc['us_per_step']} us/step", file=sys.stderr, flush=True)
             if cfg in (1, 2, 3):
