@@ -78,3 +78,46 @@ def test_random_case_matches_oracle(i):
     ref, ref_lse = G.reference(w)
     G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse,
                       "f32" if w.dtype == "f32" else "bf16", desc)
+
+
+N_CASCADE = 64
+
+
+def draw_cascade(i: int):
+    """Cascade case i: a shared prefix of whole blocks in every non-empty
+    sequence's context, then each sequence's own keys and query rows."""
+    rng = np.random.default_rng(30_000 + i)
+    dtype = str(rng.choice(["bf16", "bf16", "fp8"]))
+    bs = int(rng.choice([8, 16, 32]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 4, 8]))
+    S = int(rng.integers(1, 14))
+    cpl = bs * int(rng.integers(1, 48))
+    decode_only = bool(rng.random() < 0.5)
+    causal = bool(rng.random() < 0.75)
+    ctx = cpl + rng.integers(0, 700, S)
+    ql = np.ones(S, dtype=np.int64) if decode_only else \
+        np.where(rng.random(S) < 0.5, 1, rng.integers(2, 100, S))
+    empty = rng.random(S) < 0.1
+    ql[empty] = 0
+    ctx[empty] = 0
+    if empty.all():
+        ql[0], ctx[0] = 1, cpl
+    w = W.make_varlen(f"random_cascade{i}", ctx, ql, hkv * group, hkv, 128, bs, dtype,
+                      seed=40_000 + i, causal=causal, common_prefix_len=cpl)
+    ps = int(rng.choice([0, -1, 64, 256]))
+    opts = {"cascade_launch": int(rng.integers(0, 2))}
+    desc = (f"cascade {i}: {dtype} bs{bs} {hkv * group}/{hkv} heads, {S} seqs, prefix {cpl}, "
+            f"{'decode rows' if decode_only else 'mixed rows'}{' causal' if causal else ' non-causal'}, "
+            f"ps {ps}, options {opts}")
+    return w, ps, opts, desc
+
+
+@pytest.mark.parametrize("i", range(N_CASCADE))
+def test_random_cascade_matches_oracle(i):
+    w, ps, opts, desc = draw_cascade(i)
+    print(f"[gpu-test] {desc}", flush=True)
+    dw = G.DevWorkload(w)
+    G.run_cascade(dw, partition_size=ps, options=pagedkv.CallOptions(**opts))
+    ref, ref_lse = G.reference(w)
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "bf16", desc)
