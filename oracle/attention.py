@@ -30,6 +30,11 @@ Sources (the vLLM pages):
     (ch. 2, "Le système de spécifications du KV Cache": conservative
     allocation, exact computation).
 
+  * element formats: the flash-attention backend takes fp16 and bf16
+    models, and its caches may also be fp8: ch. 6, "Sélection du backend",
+    "Matrice de capacités : les champs comme contrat"; stored values are
+    widened exactly (IEEE binary16 here from its own definition).
+
 Readings where the pages are silent (each is pinned by a test):
   * slot = physical_block * block_size + offset;
   * query head h uses kv head h // (num_heads // num_kv_heads);
@@ -46,15 +51,32 @@ import numpy as np
 from .fp8 import e4m3_decode
 
 
+def binary16_decode(bits: np.ndarray) -> np.ndarray:
+    """Value of IEEE 754 binary16 bit patterns (uint16), in float64, from
+    the format's definition: 1 sign bit, 5 exponent bits with bias 15, 10
+    fraction bits; exponent field 0 holds zero and the subnormals
+    (fraction * 2^-24), field 31 the infinities (fraction 0) and NaNs."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, f * 2.0 ** -24, (1.0 + f / 1024.0) * np.exp2(e - 15.0))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     """Exact float64 value of stored elements: float32 arrays, bfloat16 bit
-    patterns (uint16) whose value is the float32 with those high bits, or
-    e4m3 codes (uint8; the value before the per-head scale)."""
+    patterns (uint16) whose value is the float32 with those high bits,
+    binary16 bit patterns (uint16), or e4m3 codes (uint8; the value before
+    the per-head scale)."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return binary16_decode(x)
     if dtype == "fp8":
         return e4m3_decode(x)
     raise ValueError(dtype)

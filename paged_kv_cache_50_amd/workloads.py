@@ -22,7 +22,8 @@ Random recipe (all integer draws inclusive):
   lengths and then the block permutation; spawned child streams draw q and,
   per sequence, that sequence's K then V values; C5 uses one more child for
   the new tokens' K, V and q. Values are standard_normal(float32) * sigma,
-  rounded to bfloat16 by round-to-nearest-even for bf16 workloads.
+  rounded to bfloat16 (bf16 workloads) or IEEE binary16 (f16 workloads) by
+  round-to-nearest-even.
 Every cache slot that holds no valid token (block 0, spare pool blocks, the
 tail of each sequence's last block) is filled with a quiet NaN.
 """
@@ -37,6 +38,7 @@ from typing import Optional
 import numpy as np
 
 BF16_QNAN = np.uint16(0x7FC0)
+F16_QNAN = np.uint16(0x7E00)
 E4M3_NAN = np.uint8(0x7F)
 F32_QNAN_BITS = np.uint32(0x7FC00000)
 
@@ -60,6 +62,19 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (round to nearest, ties to even;
+    overflow to infinity, gradual underflow).  Returns the bit patterns as
+    uint16.  NaN inputs map to the quiet NaN 0x7E00."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        r = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = F16_QNAN
+    return r
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
@@ -69,13 +84,14 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 class Workload:
     """One attention-layer step: cache contents, metadata and queries.
 
-    Floating-point arrays are float32 for dtype 'f32' and raw bfloat16 bits
-    (uint16) for dtype 'bf16'.  dtype 'fp8': the caches hold e4m3 codes
+    Floating-point arrays are float32 for dtype 'f32', raw bfloat16 bits
+    (uint16) for dtype 'bf16' and raw binary16 bits (uint16) for dtype
+    'f16'.  dtype 'fp8': the caches hold e4m3 codes
     (uint8) with per-kv-head float32 scales k_scale / v_scale; q and the new
     key/value rows are bfloat16 bits.
     """
     name: str
-    dtype: str                       # 'f32' | 'bf16' | 'fp8'
+    dtype: str                       # 'f32' | 'bf16' | 'f16' | 'fp8'
     num_heads: int
     num_kv_heads: int
     head_size: int
@@ -135,7 +151,7 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         """Bytes of one cached element."""
-        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+        return {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}[self.dtype]
 
     @property
     def io_dtype(self) -> str:
@@ -167,6 +183,8 @@ def _poison(shape, dtype: str) -> np.ndarray:
         return np.full(shape, F32_QNAN_BITS, dtype=np.uint32).view(np.float32)
     if dtype == "fp8":
         return np.full(shape, E4M3_NAN, dtype=np.uint8)
+    if dtype == "f16":
+        return np.full(shape, F16_QNAN, dtype=np.uint16)
     return np.full(shape, BF16_QNAN, dtype=np.uint16)
 
 
@@ -189,6 +207,8 @@ def _draw(rng: np.random.Generator, n: int, sigma: float, dtype: str) -> np.ndar
     x = rng.standard_normal(n, dtype=np.float32)
     if sigma != 1.0:
         x *= np.float32(sigma)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
     return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
@@ -528,10 +548,13 @@ def attention_flops(w: Workload) -> int:
 
 def np_to_dev(x: np.ndarray, dtype: str, device="cuda"):
     """A device tensor holding the bits of x: bfloat16 bits (uint16) as
-    torch.bfloat16, e4m3 codes (uint8) as torch.float8_e4m3fn, else as is."""
+    torch.bfloat16, binary16 bits as torch.float16, e4m3 codes (uint8) as
+    torch.float8_e4m3fn, else as is."""
     import torch as t
     if dtype == "bf16":
         return t.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(t.bfloat16).to(device)
+    if dtype == "f16":
+        return t.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(t.float16).to(device)
     if dtype == "fp8":
         return t.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device).view(t.float8_e4m3fn)
     return t.from_numpy(np.ascontiguousarray(x)).to(device)

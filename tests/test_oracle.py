@@ -475,6 +475,60 @@ def test_widen_bf16_matches_torch_for_all_patterns():
     assert np.array_equal(mine[~nan], ref[~nan])
 
 
+def test_binary16_decode_closed_forms():
+    """IEEE 754 binary16 values fixed by the format: bias 15, 10 fraction
+    bits, subnormals below 2^-14, 65504 the largest finite value."""
+    cases = {
+        0x0000: 0.0, 0x3C00: 1.0, 0xBC00: -1.0, 0x4000: 2.0, 0xC000: -2.0, 0x3800: 0.5,
+        0x3555: 0.333251953125, 0x3E00: 1.5, 0x4900: 10.0, 0x7BFF: 65504.0,
+        0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x0400: 2.0 ** -14,
+        0x3BFF: 1.0 - 2.0 ** -11, 0x3C01: 1.0 + 2.0 ** -10,
+        0x7C00: math.inf, 0xFC00: -math.inf,
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = oracle.widen(bits, "f16")
+    assert got.tolist() == list(cases.values())
+    assert math.copysign(1.0, oracle.widen(np.array([0x8000], np.uint16), "f16")[0]) == -1.0
+    nan_bits = np.array([0x7E00, 0x7C01, 0xFE00, 0x7FFF], dtype=np.uint16)
+    assert np.isnan(oracle.widen(nan_bits, "f16")).all()
+
+
+def test_binary16_decode_matches_numpy_for_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # sign symmetry, and the positive codes increase strictly up to infinity
+    assert np.array_equal(mine[0x8000:0xFC01], -mine[:0x7C01])
+    assert (np.diff(mine[:0x7C01]) > 0).all()
+
+
+def test_oracle_f16_cache_equals_f32_cache_of_same_values():
+    """A binary16 cache and q give exactly the attention of the float32
+    arrays holding the same values (every binary16 value is a float32), also
+    through the causal varlen and cascade forms, and with NaN-poisoned
+    unused slots."""
+    w = W.make_varlen("t", [0, 9, 40, 17], [5, 1, 3, 1], 4, 2, 16, 8, "f16", seed=3)
+    f32 = lambda b: oracle.widen(b, "f16").astype(np.float32)
+    args = (w.block_tables, w.seq_lens, w.scale, w.block_size)
+    for dt, q, kc, vc in (("f16", w.q, w.k_cache, w.v_cache),
+                          ("f32", f32(w.q), f32(w.k_cache), f32(w.v_cache))):
+        k2, v2 = kc.copy(), vc.copy()
+        key = w.key_new if dt == "f16" else f32(w.key_new)
+        val = w.value_new if dt == "f16" else f32(w.value_new)
+        oracle.kv_cache_write(k2, v2, key, val, w.slot_mapping, w.block_size)
+        o, l = oracle.paged_attention(q, k2, v2, *args, dt, cu_seqlens_q=w.cu_seqlens_q,
+                                      causal=True)
+        if dt == "f16":
+            ref_o, ref_l = o, l
+            assert np.isfinite(o).all()
+            assert W.F16_QNAN in w.k_cache          # unused slots really are poisoned
+    np.testing.assert_array_equal(o, ref_o)
+    np.testing.assert_array_equal(l, ref_l)
+
+
 def test_page_facts():
     facts = json.load(open(GOLDEN))
     ex = facts["allocate_slots_example"]

@@ -32,6 +32,35 @@ def test_bf16_roundtrip_widen():
     assert np.array_equal(W.f32_to_bf16_bits(f[ok]), b[ok])
 
 
+def test_f16_rne_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-6).astype(np.float32),           # binary16 subnormals
+        (rng.standard_normal(2000) * 3e4).astype(np.float32),            # near overflow
+        np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.0, 65520.0, 1e6, -1e6,
+                  np.inf, -np.inf], np.float32),
+    ])
+    # exact ties between neighbouring binary16 values of both parities:
+    # k/2 ulp with k odd, at exponent 0 (ulp 2^-10) and among subnormals (ulp 2^-24)
+    k = rng.integers(0, 1 << 11, 2000) * 2 + 1
+    ties = np.concatenate([1.0 + k[:1000] * 2.0 ** -11, k[1000:] * 2.0 ** -25]).astype(np.float32)
+    x = np.concatenate([x, ties])
+    mine = W.f32_to_f16_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_f16_rounding_closed_forms():
+    x = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 65519.0, 65520.0, 2.0 ** -25,
+                  3 * 2.0 ** -26, -2.0 ** -26, np.nan], np.float32)
+    # ties go to the even neighbour; 65520 lies halfway to 2^16 and overflows;
+    # 2^-25 is half the smallest subnormal and rounds to zero
+    assert W.f32_to_f16_bits(x).tolist() == [0x3C00, 0x3C02, 0x7BFF, 0x7C00, 0x0000,
+                                             0x0001, 0x8000, 0x7E00]
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_deterministic_per_seed(cfg):
     kw = dict(num_seqs=3, max_len=300) if cfg != 5 else dict(num_seqs=3, max_len=200,
