@@ -12,6 +12,9 @@
  *     results are merged by log-sum-exp: ch. 6 "Structure des métadonnées",
  *     "build() étape par étape" (split buffer), "Flux des paramètres du chemin
  *     non-cascadé" and "forward()" (merge of partial attention states);
+ *   - element formats: fp16 and bf16 models, caches also in fp8 (the
+ *     backend's capability fields, ch. 6 "Sélection du backend", "Matrice de
+ *     capacités : les champs comme contrat");
  *   - block bytes = 2 * block_size * num_kv_heads * head_size * dtype_bytes:
  *     «Khám phá vLLM: Giải phẫu hệ thống suy luận LLM thông lượng cao», §1 note.
  *
@@ -35,8 +38,8 @@
  *   Causal (varlen only): query row i of a sequence with q_len rows sits at
  *     absolute position i + seq_len - q_len and sees keys j <= that position
  *     (ch. 6 "Branche de masque").
- *   Output: written in place, same dtype and layout as q; float32 results are
- *     rounded to bfloat16 by round-to-nearest-even.
+ *   Output: written in place, same dtype and layout as q; the float32
+ *     results are rounded to bfloat16 or binary16 by round-to-nearest-even.
  *   lse_out (optional, may be NULL): float32 [rows, num_heads], natural-log
  *     log-sum-exp of the scaled logits each row saw; -inf for an empty row.
  *
@@ -90,9 +93,13 @@ typedef enum {
 typedef enum {
   PKV_F32 = 0,
   PKV_BF16 = 1,
-  PKV_FP8_E4M3 = 2   /* cache only: e4m3 codes (OCP "fn" variant: bias 7, max 448,
+  PKV_FP8_E4M3 = 2,  /* cache only: e4m3 codes (OCP "fn" variant: bias 7, max 448,
                         no infinities, 0x7F/0xFF NaN) with per-kv-head float32
                         scales; q, out, key and value are then bfloat16 */
+  PKV_F16 = 3        /* IEEE 754 binary16 (fp16) caches, q, out, key and value;
+                        outputs are rounded to nearest even (magnitudes past
+                        65504 would become infinities: attention outputs are
+                        weighted means of V rows, so they stay in range) */
 } pkv_dtype;
 
 /* Descriptor of one layer's paged KV cache (no ownership is transferred). */

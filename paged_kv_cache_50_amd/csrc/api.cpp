@@ -28,6 +28,8 @@ constexpr int64_t kMaxGridY = 65535;
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_FP8_E4M3 ? 1 : 2; }
 bool is_fp8(const pkv_kv_cache* c) { return c->dtype == PKV_FP8_E4M3; }
+// bfloat16 or binary16: the two 16-bit formats the matrix-core kernels take
+bool is16(int32_t dtype) { return dtype == PKV_BF16 || dtype == PKV_F16; }
 // dtype of q / out (and of the split merge's output)
 int32_t io_dtype(int32_t dtype) { return dtype == PKV_FP8_E4M3 ? PKV_BF16 : dtype; }
 
@@ -72,8 +74,8 @@ struct Report {
 
 const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t num_heads,
                    int32_t num_kv_heads) {
-  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3)
-    return "dtype must be PKV_F32, PKV_BF16 or PKV_FP8_E4M3";
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_F16 && dtype != PKV_FP8_E4M3)
+    return "dtype must be PKV_F32, PKV_BF16, PKV_F16 or PKV_FP8_E4M3";
   if (dtype == PKV_FP8_E4M3 && head_size != 128) return "fp8 caches need head_size 128";
   if (head_size != 64 && head_size != 128) return "head_size must be 64 or 128";
   if (block_size != 8 && block_size != 16 && block_size != 32)
@@ -119,19 +121,20 @@ constexpr int64_t kWgFixedTokens = 128;    // a workgroup's fixed cost in stream
 
 bool use_mfma_decode(const pkv_kv_cache* c, int group, const Choice& ch) {
   if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
-  if (c->dtype != PKV_BF16 || c->head_size != 128) return false;
+  if (!is16(c->dtype) || c->head_size != 128) return false;
   if (ch.decode_kernel == 1) return false;
   if (ch.decode_kernel == 2) return true;
   return group >= kMfmaMinGroup;
 }
 
-// Prefill kernel choice: the matrix-core kernel for bfloat16 or e4m3 caches
-// with head 128 (the only prefill kernel for e4m3); a call's options may
-// force the generic row kernel for bfloat16 (A/B measurements).
+// Prefill kernel choice: the matrix-core kernel for bfloat16, binary16 or
+// e4m3 caches with head 128 (the only prefill kernel for e4m3); a call's
+// options may force the generic row kernel for 16-bit caches (A/B
+// measurements).
 bool use_mfma_prefill(const pkv_kv_cache* c, const Choice& ch) {
   if (c->head_size != 128) return false;
   if (c->dtype == PKV_FP8_E4M3) return true;
-  if (c->dtype != PKV_BF16) return false;
+  if (!is16(c->dtype)) return false;
   return ch.prefill_kernel != 1;
 }
 
@@ -244,7 +247,7 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
-      if (pkv::launch_attn_mfma_decode(a, cache->block_size, is_fp8(cache), dim3(gx, gz, gparts),
+      if (pkv::launch_attn_mfma_decode(a, cache->block_size, cache->dtype, dim3(gx, gz, gparts),
                                        st) != hipSuccess)
         return PKV_ERR_HIP;
     }
@@ -554,7 +557,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
       int tslot = 0;
       const bool timed = timing_begin(s, &tslot);
       ch.ran |= PKV_RAN_MIXED;
-      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, is_fp8(cache), s) != hipSuccess)
+      if (pkv::launch_attn_mixed(r, d, g, cache->block_size, cache->dtype, s) != hipSuccess)
         st = PKV_ERR_HIP;
       if (timed) timing_end(s, tslot);
       if (st != PKV_OK) return st;
@@ -581,7 +584,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
       for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
         r.z_base = (int32_t)z0;
         const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, num_seqs - z0);
-        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, is_fp8(cache), dim3(qtiles, gy, gz),
+        if (pkv::launch_attn_mfma_prefill(r, cache->block_size, cache->dtype, dim3(qtiles, gy, gz),
                                           s) != hipSuccess)
           st = PKV_ERR_HIP;
       }
@@ -796,8 +799,8 @@ size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t
 const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int32_t num_tokens,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                int32_t dtype, int32_t window_left) {
-  if ((dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) || head_size != 128)
-    return "cascade attention needs bfloat16 or fp8 caches with head_size 128";
+  if ((!is16(dtype) && dtype != PKV_FP8_E4M3) || head_size != 128)
+    return "cascade attention needs bfloat16, fp16 or fp8 caches with head_size 128";
   if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
     return "num_heads must be a positive multiple of num_kv_heads";
   if (window_left >= 0) return "sliding-window attention does not use the cascade";
@@ -842,7 +845,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
-  if ((cache->dtype != PKV_BF16 && cache->dtype != PKV_FP8_E4M3) || cache->head_size != 128)
+  if ((!is16(cache->dtype) && cache->dtype != PKV_FP8_E4M3) || cache->head_size != 128)
     return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   const int32_t cpl = common_prefix_len;
@@ -925,7 +928,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     int tslot = 0;
     const bool timed = timing_begin(s, &tslot);
     ch.ran |= PKV_RAN_CASCADE_ONE;
-    if (pkv::launch_attn_cascade(p, d, mg, cache->block_size, is_fp8(cache), s) != hipSuccess)
+    if (pkv::launch_attn_cascade(p, d, mg, cache->block_size, cache->dtype, s) != hipSuccess)
       st = PKV_ERR_HIP;
     if (timed) timing_end(s, tslot);
     if (st != PKV_OK) return st;
@@ -933,7 +936,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     if (st != PKV_OK) return st;
   } else {
     ch.ran |= PKV_RAN_PREFIX;
-    if (pkv::launch_attn_mfma_prefix(p, cache->block_size, is_fp8(cache),
+    if (pkv::launch_attn_mfma_prefix(p, cache->block_size, cache->dtype,
                                      dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
       return PKV_ERR_HIP;
     // 2. suffix pass: each row against its own keys (from the prefix end on)
@@ -948,7 +951,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   m.cu_seqlens_q = cu_seqlens_q;
   m.lse_out = lse_out;
   ch.ran |= PKV_RAN_CASCADE_MERGE;
-  if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, io_dtype(cache->dtype), s) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 

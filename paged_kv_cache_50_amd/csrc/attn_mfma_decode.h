@@ -7,7 +7,8 @@
 // non-cascadé": one kernel gathering K/V through the block table).  Each kv
 // head's K/V tile is loaded once and shared by the group's query heads.
 //
-// Layout (v_mfma_f32_16x16x32_bf16, N = 16 query-head columns, g <= 16 used):
+// Layout (v_mfma_f32_16x16x32_bf16, or _f16 over binary16 caches; N = 16
+// query-head columns, g <= 16 used):
 //   S^T[32 tok x 16 heads] = K[32 x 128] . Q^T[128 x 16]: the K tile is read
 //     from HBM as whole 256-byte token rows (16 lanes x 16 bytes per row, the
 //     most efficient gather pattern), staged in LDS with an XOR swizzle of the
@@ -64,11 +65,6 @@ template <int HP>
 constexpr int kLdsBytesHp = HP * kLdsBytes;
 static_assert(kWaveLds >= 16 * kD * 4, "the final merge stages [16 heads][D] floats per wave");
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
 __device__ __forceinline__ float xmax16_32(float x) {
   // max over the 4 lanes {l, l^16, l^32, l^48}: the token groups of a column
   auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -97,15 +93,21 @@ __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (
 // rows of both heads (16 lanes a row, the gather pattern of bfloat16 rows),
 // each lane converts into the K or V tile of its head, and the products and
 // softmax states run per head.
+// DT is the cache's pkv_dtype: PKV_BF16, PKV_F16 (the products then take
+// binary16 operands and the output is binary16) or PKV_FP8_E4M3.
 // One workgroup's work: kv-head chunk bx (kv-head pair with HP = 2), row
 // item zi (before the dispatch order is applied), key range bz of nz.  The
 // caller provides the LDS areas (kLdsBytesHp<HP>, 16-byte aligned, and the
 // two [kWaves][32] merge arrays).
-template <int BS, bool FP8, int HP>
+template <int BS, int DT, int HP>
 __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, int bz, int nz,
                                              char* __restrict__ s_lds, float (*s_m)[32],
                                              float (*s_l)[32]) {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(DT == PKV_BF16 || DT == PKV_F16 || DT == PKV_FP8_E4M3, "cache dtype");
+  constexpr bool FP8 = DT == PKV_FP8_E4M3;
+  using H = Fmt16<DT == PKV_F16>;                    // operand format of the products
+  using x8 = typename H::x8;
   static_assert(HP == 1 || (HP == 2 && FP8), "two heads per wave: e4m3 caches");
   constexpr int kBlkPerTile = kTile / BS;
   constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
@@ -147,7 +149,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int pbegin = it.L_begin;                 // first visible key (sliding window)
 
   // Q^T B operands: lane (kg, n) holds q[h0+n][(4j+kg)*8 .. +8] for k-step j.
-  bf16x8_t qb[HP][4];
+  x8 qb[HP][4];
 #pragma unroll
   for (int hp = 0; hp < HP; ++hp) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
@@ -156,7 +158,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (n < G) v = *reinterpret_cast<const u32x4*>(qrow + (4 * j + kg) * 8);
-      qb[hp][j] = as_bf16x8(v);
+      qb[hp][j] = H::as_x8(v);
     }
   }
 
@@ -275,7 +277,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 ka = *reinterpret_cast<const u32x4*>(klds + ktile_off(tt * 16 + n, 4 * j + kg));
-        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[hp][j], sacc[tt], 0, 0, 0);
+        sacc[tt] = H::mfma(H::as_x8(ka), qb[hp][j], sacc[tt]);
       }
     }
     // lane holds tokens tt*16 + 4kg + i of head column n
@@ -296,13 +298,13 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     const float mref = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = fast_exp2(m[hp] - mref);
     m[hp] = mn;
-    bf16x8_t pb;
+    x8 pb;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = fast_exp2(s[e] - mref);
       psum += p;
-      pb[e] = (__bf16)p;
+      pb[e] = (typename H::elem)p;
     }
     lsum[hp] = lsum[hp] * alpha + psum;
 #pragma unroll
@@ -314,17 +316,17 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   // O^T += V^T P^T for head hp of a tile whose V rows are staged, one 16-dim
   // tile at a time; the transposed reads give lane (kg, n) V[4kg + jj][16jd + n]
   // and V[16 + 4kg + jj][16jd + n].
-  auto pv = [&](const bf16x8_t pb, int hp) {
+  auto pv = [&](const x8 pb, int hp) {
     {
       const int jj = n >> 2, q4 = n & 3;
       const char* r0 = wlds + hp * kWaveLds + (4 * kg + jj) * kVPitch + q4 * 8;
       const char* r1 = r0 + 16 * kVPitch;
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) {
-        bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r0 + jd * 32));
-        bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(r1 + jd * 32));
-        bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[hp][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[hp][jd], 0, 0, 0);
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + jd * 32));
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r1 + jd * 32));
+        const x8 va = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[hp][jd] = H::mfma(va, pb, o[hp][jd]);
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -360,7 +362,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     const int nt = tile + tstep;
     stage_k(kr);
     if (nt < tend) issue(kc, ids, kr);
-    bf16x8_t pb[HP];
+    x8 pb[HP];
 #pragma unroll
     for (int hp = 0; hp < HP; ++hp) pb[hp] = logits(tile, hp);
     stage_v(tile, vr);
@@ -411,7 +413,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     if (it.nranges == 1) {
       const float v = Ls > 0.f ? O / Ls * out_scale : 0.f;
       static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * kD + d] =
-          static_cast<uint16_t>(f32_to_bf16_rne(v));
+          static_cast<uint16_t>(H::rne(v));
       if (d == 0 && a.lse_out)
         a.lse_out[(int64_t)it.row * a.num_heads + head] =
             Ls > 0.f ? (M + acc_log2(Ls)) * kLn2 : -INFINITY;

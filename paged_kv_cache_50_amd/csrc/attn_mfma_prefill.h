@@ -78,11 +78,8 @@ static_assert(kRingBytes8 + 2 * kStageBytes <= kLdsBytes, "fp8 layout fits the L
 // written interleaved stays interleaved.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 // 16-byte slot of chunk c of token row t: K rows are swizzled so 16 lanes
 // reading one chunk of 16 rows (MFMA A operand) hit distinct bank groups; V
 // rows so the transposed reads (16 rows x 32 bytes) spread over all banks.
@@ -144,9 +141,16 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // as the bfloat16 stages are (each thread converts the 16 + 16 codes it
 // loaded itself), and the products read those.  The per-kv-head k_scale is
 // folded into the logit scale and v_scale into the output.
-template <int BS, bool PREFIX = false, bool FP8 = false>
+// DT is the cache's pkv_dtype: PKV_BF16, PKV_F16 (binary16 operands and
+// output; the unscaled probabilities stay below 2^8, well inside its range)
+// or PKV_FP8_E4M3.
+template <int BS, bool PREFIX, int DT>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
+  static_assert(DT == PKV_BF16 || DT == PKV_F16 || DT == PKV_FP8_E4M3, "cache dtype");
+  constexpr bool FP8 = DT == PKV_FP8_E4M3;
+  using H = Fmt16<DT == PKV_F16>;                    // operand format of the products
+  using x8 = typename H::x8;
   int qs, q_len, L, off;
   const int part = PREFIX ? seq : 0;
   if constexpr (PREFIX) {
@@ -220,7 +224,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   const int wave_first_key = max(win >= 0 ? min(rowb[0], rowb[1]) + off - win : 0, key_lo);
 
   // Q^T B operands, lane (kg, n): row rowb + n, dims (4j + kg)*8 .. +8
-  bf16x8_t qb[2][4];
+  x8 qb[2][4];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int row = rowb[c] + n;
@@ -230,7 +234,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ok) v = *reinterpret_cast<const u32x4*>(qp + (4 * j + kg) * 8);
-      qb[c][j] = as_bf16x8(v);
+      qb[c][j] = H::as_x8(v);
     }
   }
   // the queries must be resident before any tile load is issued: otherwise
@@ -378,12 +382,12 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     // every LDS read of the tile issued up front: K chunks for the A
     // operands, then the transposed V rows (waited for before the first PV
     // product)
-    bf16x8_t ka[2][4];
+    x8 ka[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        ka[tt][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + koff[j] + tt * 4096));
+        ka[tt][j] = H::as_x8(*reinterpret_cast<const u32x4*>(buf + koff[j] + tt * 4096));
     u32x2 vr[8][2];
     if constexpr (SO >= 0) {
       const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)s_lds;
@@ -409,7 +413,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
         sacc[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sacc[c][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tt][j], qb[c][j], sacc[c][tt], 0, 0, 0);
+          sacc[c][tt] = H::mfma(ka[tt][j], qb[c][j], sacc[c][tt]);
       }
     // masked raw logits (the scale is applied inside the exponent), row
     // maxima and the reference decisions of both column tiles
@@ -428,7 +432,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[c][tt * 4 + i] = sacc[c][tt][i];
-      auto full_step = [&](int c, bf16x8_t& pb, float& psum) {
+      auto full_step = [&](int c, x8& pb, float& psum) {
         float mx = vmax(vmax(vmax(s[c][0], s[c][1]), vmax(s[c][2], s[c][3])),
                         vmax(vmax(s[c][4], s[c][5]), vmax(s[c][6], s[c][7])));
         mx = xmax16_32(mx) * sl2;
@@ -444,40 +448,40 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
         for (int e = 0; e < 8; ++e) {
           const float p = fast_exp2(fmaf(s[c][e], sl2, -m[c]));
           psum += p;
-          pb[e] = (__bf16)p;
+          pb[e] = (typename H::elem)p;
         }
       };
-      bf16x8_t pb0, pb1;
+      x8 pb0, pb1;
       float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = fast_exp2(fmaf(s[0][e], sl2, -m[0]));
         psum0 += p;
-        pb0[e] = (__bf16)p;
+        pb0[e] = (typename H::elem)p;
       }
       if (__builtin_amdgcn_ballot_w64(!(psum0 <= kSlackSum))) full_step(0, pb0, psum0);
       lsum[0] += psum0;
       lds_results_ready(vr);
-      bf16x8_t va[8];
+      x8 va[8];
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) {
         const u32x4 w = {vr[jd][0][0], vr[jd][0][1], vr[jd][1][0], vr[jd][1][1]};
-        va[jd] = as_bf16x8(w);
+        va[jd] = H::as_x8(w);
       }
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) {
         sched_fence();
-        o[0][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb0, o[0][jd], 0, 0, 0);
+        o[0][jd] = H::mfma(va[jd], pb0, o[0][jd]);
         const float p = fast_exp2(fmaf(s[1][jd], sl2, -m[1]));
         psum1 += p;
-        pb1[jd] = (__bf16)p;
+        pb1[jd] = (typename H::elem)p;
       }
       sched_fence();
       if (__builtin_amdgcn_ballot_w64(!(psum1 <= kSlackSum))) full_step(1, pb1, psum1);
       lsum[1] += psum1;
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd)
-        o[1][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb1, o[1][jd], 0, 0, 0);
+        o[1][jd] = H::mfma(va[jd], pb1, o[1][jd]);
       return;
     }
 #pragma unroll
@@ -518,35 +522,35 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     // exponentials, then its eight products, each followed (in program
     // order, fenced so that the compiler keeps it) by one exponential of the
     // second column tile, whose products come last
-    bf16x8_t pb0, pb1;
+    x8 pb0, pb1;
     float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = fast_exp2(fmaf(s[0][e], sl2, -m[0]));
       psum0 += p;
-      pb0[e] = (__bf16)p;
+      pb0[e] = (typename H::elem)p;
     }
     lsum[0] += psum0;
     lds_results_ready(vr);
-    bf16x8_t va[8];
+    x8 va[8];
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
       const u32x4 w = {vr[jd][0][0], vr[jd][0][1], vr[jd][1][0], vr[jd][1][1]};
-      va[jd] = as_bf16x8(w);
+      va[jd] = H::as_x8(w);
     }
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
       sched_fence();
-      o[0][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb0, o[0][jd], 0, 0, 0);
+      o[0][jd] = H::mfma(va[jd], pb0, o[0][jd]);
       const float p = fast_exp2(fmaf(s[1][jd], sl2, -m[1]));
       psum1 += p;
-      pb1[jd] = (__bf16)p;
+      pb1[jd] = (typename H::elem)p;
     }
     sched_fence();
     lsum[1] += psum1;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd)
-      o[1][jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[jd], pb1, o[1][jd], 0, 0, 0);
+      o[1][jd] = H::mfma(va[jd], pb1, o[1][jd]);
   };
 
   // LDS ring: tile t lives in stage t % kStages.  bfloat16: before
@@ -680,8 +684,8 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + row) * a.num_heads + head[c]) * kD;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
-      const uint32_t w0 = pack_bf16x2(o[c][jd][0] * inv, o[c][jd][1] * inv);
-      const uint32_t w1 = pack_bf16x2(o[c][jd][2] * inv, o[c][jd][3] * inv);
+      const uint32_t w0 = pack16x2<DT == PKV_F16>(o[c][jd][0] * inv, o[c][jd][1] * inv);
+      const uint32_t w1 = pack16x2<DT == PKV_F16>(o[c][jd][2] * inv, o[c][jd][3] * inv);
       *reinterpret_cast<uint2*>(op + 16 * jd + 4 * kg) = make_uint2(w0, w1);
     }
     if (kg == 0 && a.lse_out)

@@ -26,9 +26,9 @@ static_assert(pf::kThreads == dec::kThreads, "one block shape");
 
 // CASCADE: the first kind of work is the cascade prefix pass (items = query
 // tile x head group x prefix partition, a fixed count) instead of the
-// listed prefill chunks.  FP8: e4m3 caches (both kinds of work; the decode
-// rows with one kv head per wave).
-template <int BS, bool CASCADE, bool FP8>
+// listed prefill chunks.  DT: the cache's pkv_dtype (bfloat16, binary16 or
+// e4m3, for both kinds of work; the decode rows with one kv head per wave).
+template <int BS, bool CASCADE, int DT>
 __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const AttnArgs pre,
                                                                        const AttnArgs dcd,
                                                                        const MixedGrid g) {
@@ -67,50 +67,59 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int part = (int)(t / g.pre_y);
-      pf::prefill_block<BS, true, FP8>(pre, bx, by, part, s_lds);
+      pf::prefill_block<BS, true, DT>(pre, bx, by, part, s_lds);
     } else if (role == 0) {
       // the last query tiles of a chunk see the most keys: they go first
       const int bx = g.pre_x - 1 - (int)(item % g.pre_x);
       const int64_t t = item / g.pre_x;
       const int by = (int)(t % g.pre_y);
       const int li = (int)(t / g.pre_y);
-      pf::prefill_block<BS, false, FP8>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
+      pf::prefill_block<BS, false, DT>(pre, bx, by, load_uniform_i32(g.pre_list, li), s_lds);
     } else {
       const int bx = (int)(item % g.dec_x);
       const int64_t t = item / g.dec_x;
       const int zi = (int)(t % g.dec_y);
       const int bz = (int)(t / g.dec_y);
-      dec::decode_block<BS, FP8, 1>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
+      dec::decode_block<BS, DT, 1>(dcd, bx, zi, bz, g.dec_z, s_lds, s_m, s_l);
     }
   }
 }
 
-template <bool CASCADE, bool FP8>
+template <bool CASCADE, int DT>
 hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, int block_size,
                   hipStream_t stream) {
   if (g.workgroups <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)g.workgroups), block(dec::kThreads);
   switch (block_size) {
-    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
-    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
-    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE, FP8>), grid, block, 0, stream, pre, dcd, g); break;
+    case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
+    case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
+    case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool CASCADE>
+hipError_t launch_dt(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, int block_size,
+                     int dtype, hipStream_t stream) {
+  switch (dtype) {
+    case PKV_BF16: return launch<CASCADE, PKV_BF16>(pre, dcd, g, block_size, stream);
+    case PKV_F16: return launch<CASCADE, PKV_F16>(pre, dcd, g, block_size, stream);
+    case PKV_FP8_E4M3: return launch<CASCADE, PKV_FP8_E4M3>(pre, dcd, g, block_size, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                             int block_size, bool fp8, hipStream_t stream) {
-  return fp8 ? launch<false, true>(pre, dcd, g, block_size, stream)
-             : launch<false, false>(pre, dcd, g, block_size, stream);
+                             int block_size, int dtype, hipStream_t stream) {
+  return launch_dt<false>(pre, dcd, g, block_size, dtype, stream);
 }
 
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                               int block_size, bool fp8, hipStream_t stream) {
-  return fp8 ? launch<true, true>(pre, dcd, g, block_size, stream)
-             : launch<true, false>(pre, dcd, g, block_size, stream);
+                               int block_size, int dtype, hipStream_t stream) {
+  return launch_dt<true>(pre, dcd, g, block_size, dtype, stream);
 }
 
 }  // namespace pkv

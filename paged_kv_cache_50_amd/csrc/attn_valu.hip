@@ -3,10 +3,10 @@
 // Computes, for one query row, the query heads of one kv-head chunk and one
 // key partition, the online-softmax attention over the row's cached tokens
 // reached through its block-table row (vLLM book, ch. 6 "Flux des paramètres
-// du chemin non-cascadé": cu_seqlens_q, seqused_k, block_table).  Used for
-// float32 caches, for MHA decode (one query head per kv head, where the work
-// is a matrix-vector product and matrix cores would idle) and as the generic
-// varlen path.
+// du chemin non-cascadé": cu_seqlens_q, seqused_k, block_table).  Takes
+// float32, bfloat16 and binary16 caches.  Used for float32 caches, for MHA
+// decode (one query head per kv head, where the work is a matrix-vector
+// product and matrix cores would idle) and as the generic varlen path.
 //
 // Work decomposition
 //   grid.x = kv head * head chunks, grid.y = sequence (or query row in
@@ -47,6 +47,10 @@ template <>
 struct Elem<uint16_t> {
   static constexpr int kBytes = 2;
 };
+template <>
+struct Elem<_Float16> {
+  static constexpr int kBytes = 2;
+};
 
 // Dot product of a 16-byte K fragment with the query fragment of one head.
 template <typename T>
@@ -71,6 +75,15 @@ __device__ __forceinline__ float frag_dot<uint16_t>(const u32x4& k, const u32x4&
   return s;
 }
 
+template <>
+__device__ __forceinline__ float frag_dot<_Float16>(const u32x4& k, const u32x4& q) {
+  // binary16 pairs, products exact, fp32 accumulation.
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s = __builtin_amdgcn_fdot2(as_f16x2(k[w]), as_f16x2(q[w]), s, false);
+  return s;
+}
+
 // Widen a 16-byte V fragment to fp32 (4 or 8 values).
 template <typename T>
 __device__ __forceinline__ void frag_widen(const u32x4& v, float* out);
@@ -90,6 +103,15 @@ __device__ __forceinline__ void frag_widen<uint16_t>(const u32x4& v, float* out)
   }
 }
 
+template <>
+__device__ __forceinline__ void frag_widen<_Float16>(const u32x4& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = f16_lo(v[i]);
+    out[2 * i + 1] = f16_hi(v[i]);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v);
 template <>
@@ -99,6 +121,10 @@ __device__ __forceinline__ void store_out<float>(void* out, int64_t idx, float v
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(void* out, int64_t idx, float v) {
   static_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+}
+template <>
+__device__ __forceinline__ void store_out<_Float16>(void* out, int64_t idx, float v) {
+  static_cast<uint16_t*>(out)[idx] = static_cast<uint16_t>(f32_to_f16_rne(v));
 }
 
 template <typename T, int D, int BS, int GT>
@@ -342,12 +368,15 @@ static hipError_t launch_bs(const AttnArgs& a, int bs, int gt, dim3 grid, hipStr
 
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream) {
-  if (dtype == 0) {
+  if (dtype == PKV_F32) {
     if (head_size == 64) return launch_bs<float, 64>(a, block_size, heads_per_chunk, grid, stream);
     if (head_size == 128) return launch_bs<float, 128>(a, block_size, heads_per_chunk, grid, stream);
-  } else if (dtype == 1) {
+  } else if (dtype == PKV_BF16) {
     if (head_size == 64) return launch_bs<uint16_t, 64>(a, block_size, heads_per_chunk, grid, stream);
     if (head_size == 128) return launch_bs<uint16_t, 128>(a, block_size, heads_per_chunk, grid, stream);
+  } else if (dtype == PKV_F16) {
+    if (head_size == 64) return launch_bs<_Float16, 64>(a, block_size, heads_per_chunk, grid, stream);
+    if (head_size == 128) return launch_bs<_Float16, 128>(a, block_size, heads_per_chunk, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -4,7 +4,7 @@
 // cascade calls in the vLLM book, ch. 6 "forward()".
 //
 // For one (row, query head) the suffix pass left its normalised output in
-// `out` (bfloat16) and its log-sum-exp (natural log) in lse_suffix; the
+// `out` (bfloat16 or binary16, F16) and its log-sum-exp (natural log) in lse_suffix; the
 // prefix pass left num_parts normalised fp32 partials o_p with log-sum-exps
 // lse_p in log2 units.  With every lse in log2 units and M their maximum:
 //   out = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M),
@@ -24,7 +24,7 @@ constexpr int kMaxPrefixParts = 16;
 // one query head and issues all of its loads at once.  NP (a power of two,
 // at least num_parts) fixes how many partial slots are loaded; slots past
 // num_parts are clamped in bounds and weighted 0.
-template <int D, int NP>
+template <int D, int NP, bool F16>
 __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
                                                             const float* __restrict__ lse_suffix,
                                                             int num_parts) {
@@ -60,8 +60,8 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
   const int64_t oi = (int64_t)row * a.num_heads + head;
   uint16_t* op = static_cast<uint16_t*>(a.out) + oi * D + 4 * c;
   const uint2 sb = *reinterpret_cast<const uint2*>(op);
-  const f32x4 vs = {__uint_as_float(sb.x << 16), __uint_as_float(sb.x & 0xFFFF0000u),
-                    __uint_as_float(sb.y << 16), __uint_as_float(sb.y & 0xFFFF0000u)};
+  using H = Fmt16<F16>;
+  const f32x4 vs = {H::lo(sb.x), H::hi(sb.x), H::lo(sb.y), H::hi(sb.y)};
   const float ls = lse_suffix[oi] * kLog2e;
   float M = ls;
 #pragma unroll
@@ -78,30 +78,41 @@ __global__ void __launch_bounds__(256) cascade_merge_kernel(const AttnArgs a,
     wsum += w;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const uint32_t w0 = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  const uint32_t w1 = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  const uint32_t w0 = pack16x2<F16>(acc[0] * inv, acc[1] * inv);
+  const uint32_t w1 = pack16x2<F16>(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
   if (c == 0 && a.lse_out) a.lse_out[oi] = wsum > 0.f ? (M + acc_log2(wsum)) * kLn2 : -INFINITY;
+}
+
+template <bool F16>
+hipError_t launch_np(const AttnArgs& a, const float* lse_suffix, int num_parts,
+                     hipStream_t stream) {
+  constexpr int D = 128;
+  constexpr int NG = 256 / (D / 4);
+  const dim3 grid(a.num_tokens, (a.num_heads + NG - 1) / NG), block(256);
+  if (num_parts <= 2)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 2, F16>), grid, block, 0, stream, a, lse_suffix,
+                       num_parts);
+  else if (num_parts <= 4)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 4, F16>), grid, block, 0, stream, a, lse_suffix,
+                       num_parts);
+  else if (num_parts <= 8)
+    hipLaunchKernelGGL((cascade_merge_kernel<D, 8, F16>), grid, block, 0, stream, a, lse_suffix,
+                       num_parts);
+  else
+    hipLaunchKernelGGL((cascade_merge_kernel<D, kMaxPrefixParts, F16>), grid, block, 0, stream, a,
+                       lse_suffix, num_parts);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_cascade_merge(const AttnArgs& a, const float* lse_suffix, int num_parts,
-                                hipStream_t stream) {
+                                int out_dtype, hipStream_t stream) {
   if (num_parts < 1 || num_parts > kMaxPrefixParts) return hipErrorInvalidValue;
-  constexpr int D = 128;
-  constexpr int NG = 256 / (D / 4);
-  const dim3 grid(a.num_tokens, (a.num_heads + NG - 1) / NG), block(256);
-  if (num_parts <= 2)
-    hipLaunchKernelGGL((cascade_merge_kernel<D, 2>), grid, block, 0, stream, a, lse_suffix, num_parts);
-  else if (num_parts <= 4)
-    hipLaunchKernelGGL((cascade_merge_kernel<D, 4>), grid, block, 0, stream, a, lse_suffix, num_parts);
-  else if (num_parts <= 8)
-    hipLaunchKernelGGL((cascade_merge_kernel<D, 8>), grid, block, 0, stream, a, lse_suffix, num_parts);
-  else
-    hipLaunchKernelGGL((cascade_merge_kernel<D, kMaxPrefixParts>), grid, block, 0, stream, a,
-                       lse_suffix, num_parts);
-  return hipGetLastError();
+  if (out_dtype == PKV_BF16) return launch_np<false>(a, lse_suffix, num_parts, stream);
+  if (out_dtype == PKV_F16) return launch_np<true>(a, lse_suffix, num_parts, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

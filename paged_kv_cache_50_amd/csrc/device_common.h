@@ -1,5 +1,5 @@
-// Device helpers shared by the gfx950 kernels: bfloat16 conversions, DPP
-// lane reductions, 16-byte vector types.
+// Device helpers shared by the gfx950 kernels: bfloat16 and binary16
+// conversions, DPP lane reductions, 16-byte vector types.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,7 +10,11 @@ namespace pkv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -33,6 +37,57 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- IEEE binary16 (cache dtype fp16) <-> float32.  Widening is exact;
+// narrowing rounds to nearest even (the default rounding mode), NaN stays a
+// NaN and magnitudes past 65504 round to infinity.
+__device__ __forceinline__ f16x2_t as_f16x2(uint32_t x) { return __builtin_bit_cast(f16x2_t, x); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// The two 16-bit formats of q, out and 16-bit caches, as the matrix-core
+// kernels use them: F16 = false is bfloat16, true is binary16.  Both have a
+// 16x16x32 MFMA with fp32 accumulation on gfx950.
+template <bool F16>
+struct Fmt16;
+
+template <>
+struct Fmt16<false> {
+  typedef __bf16 elem;
+  typedef bf16x8_t x8;
+  static __device__ __forceinline__ x8 as_x8(u32x4 v) { return __builtin_bit_cast(x8, v); }
+  static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  static __device__ __forceinline__ uint32_t rne(float f) { return f32_to_bf16_rne(f); }
+};
+
+template <>
+struct Fmt16<true> {
+  typedef _Float16 elem;
+  typedef f16x8_t x8;
+  static __device__ __forceinline__ x8 as_x8(u32x4 v) { return __builtin_bit_cast(x8, v); }
+  static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+  static __device__ __forceinline__ uint32_t rne(float f) { return f32_to_f16_rne(f); }
+};
+
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+  return Fmt16<F16>::rne(lo) | (Fmt16<F16>::rne(hi) << 16);
 }
 
 // ---- e4m3 (OCP "fn" variant) <-> float32, with the gfx950 converters, which

@@ -101,23 +101,24 @@ void timing_end(hipStream_t st, int slot);
 // fp8 = true: bfloat16 key/value quantised into e4m3 caches.
 hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8, hipStream_t stream);
 
-// General VALU attention kernel: float32 or bfloat16 caches, head size 64/128,
-// block size 8/16/32, any GQA ratio.
+// General VALU attention kernel: float32, bfloat16 or binary16 caches (dtype
+// is the pkv_dtype), head size 64/128, block size 8/16/32, any GQA ratio.
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream);
 
-// Grouped-query decode on the matrix cores: bfloat16 (or e4m3 with fp8 =
-// true) caches, head size 128, up to 16 query heads per kv-head chunk
-// (head_chunks = ceil(group / 16)).
+// The matrix-core kernels below take the cache's pkv_dtype: PKV_BF16,
+// PKV_F16 or PKV_FP8_E4M3 (any other value: hipErrorInvalidValue).
+// Grouped-query decode on the matrix cores: head size 128, up to 16 query
+// heads per kv-head chunk (head_chunks = ceil(group / 16)).
 // grid = (num_kv_heads * head_chunks, sequences, ceil(partitions / parts_per_wg)).
-hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
+hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, int dtype, dim3 grid,
                                    hipStream_t stream);
 
 // Chunked prefill on the matrix cores (rows of sequences with > 1 query
-// rows): bfloat16 (or e4m3 with fp8 = true) caches, head size 128.
+// rows): head size 128.
 // grid = (query tiles of 128 / head_chunks_gc rows, num_kv_heads * group /
 // head_chunks_gc, sequences).
-hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
+hipError_t launch_attn_mfma_prefill(const AttnArgs& a, int block_size, int dtype, dim3 grid,
                                     hipStream_t stream);
 
 // Permutation of 0..num_seqs-1 ordering sequences longest first (one
@@ -142,29 +143,27 @@ struct MixedGrid {
   const int32_t* pre_count;        // [1] how many
   int32_t* queues;                 // [2] item counters (prefill, decode), zeroed by the planner
 };
-// bfloat16 or (fp8 = true) e4m3 caches.
 hipError_t launch_attn_mixed(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                             int block_size, bool fp8, hipStream_t stream);
+                             int block_size, int dtype, hipStream_t stream);
 // The same persistent grid for a cascade of decode rows: prefix-pass items
-// (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`);
-// bfloat16 or (fp8 = true) e4m3 caches.
+// (args `pre`, mode kModePrefix) and the suffix pass's decode rows (`dcd`).
 hipError_t launch_attn_cascade(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g,
-                               int block_size, bool fp8, hipStream_t stream);
+                               int block_size, int dtype, hipStream_t stream);
 
-// Cascade prefix pass on the matrix cores (mode kModePrefix, bfloat16 or
-// e4m3 caches, head size 128): grid = (query tiles of 128 / head_chunks_gc rows over all
+// Cascade prefix pass on the matrix cores (mode kModePrefix, head size
+// 128): grid = (query tiles of 128 / head_chunks_gc rows over all
 // num_tokens rows, num_kv_heads * group / head_chunks_gc, key partitions).
 // Writes normalised fp32 partials to ws_o [part][head][row][D] and their
 // log2-domain log-sum-exps to ws_lse [part][head][row].
-hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, bool fp8, dim3 grid,
+hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, int dtype, dim3 grid,
                                    hipStream_t stream);
 
 // Cascade merge: out (the suffix result, in place) and its natural-log lse
 // `lse_suffix` [rows, heads] are combined with `num_parts` prefix partials
 // (layout of launch_attn_mfma_prefix); rows of sequences with seq_len 0 keep
-// the suffix result (zeros).  bfloat16 out, head size 128.
+// the suffix result (zeros).  out_dtype PKV_BF16 or PKV_F16, head size 128.
 hipError_t launch_cascade_merge(const AttnArgs& a, const float* lse_suffix, int num_parts,
-                                hipStream_t stream);
+                                int out_dtype, hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,

@@ -10,12 +10,18 @@
 // already merged by the same rule inside the workgroup).  Rows with a single
 // range were written by the partition kernel and are skipped here.  Only partitions that start before the row's last key are
 // read, so stale workspace entries from earlier calls are never used.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
+
+// T: the output element, float, uint16_t (bfloat16 bits) or _Float16.
+template <typename T>
+constexpr bool kIsF16 = std::is_same<T, _Float16>::value;
 
 // One workgroup per (sequence, query head).  The partials of one row are
 // read in parallel: lanes of a group of D/4 lanes hold 4 dims of one
@@ -73,7 +79,7 @@ __global__ void __launch_bounds__(256) splitkv_reduce_kernel(const AttnArgs a) {
     if constexpr (sizeof(T) == 4)
       static_cast<float*>(a.out)[oidx] = v;
     else
-      static_cast<uint16_t*>(a.out)[oidx] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+      static_cast<uint16_t*>(a.out)[oidx] = static_cast<uint16_t>(Fmt16<kIsF16<T>>::rne(v));
     if (tid == 0 && a.lse_out)
       a.lse_out[(int64_t)it.row * a.num_heads + head] =
           Ls > 0.f ? (M + acc_log2(Ls)) * kLn2 : -INFINITY;
@@ -125,8 +131,8 @@ __global__ void __launch_bounds__(256) splitkv_reduce_few_kernel(const AttnArgs 
   if constexpr (sizeof(T) == 4) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oidx) = acc * inv;
   } else {
-    const uint32_t w0 = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    const uint32_t w1 = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    const uint32_t w0 = pack16x2<kIsF16<T>>(acc[0] * inv, acc[1] * inv);
+    const uint32_t w1 = pack16x2<kIsF16<T>>(acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oidx) = make_uint2(w0, w1);
   }
   if (c == 0 && a.lse_out)
@@ -151,10 +157,13 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
-  if (dtype == 0 && head_size == 64) return launch_typed<float, 64>(a, st);
-  if (dtype == 0 && head_size == 128) return launch_typed<float, 128>(a, st);
-  if (dtype == 1 && head_size == 64) return launch_typed<uint16_t, 64>(a, st);
-  if (dtype == 1 && head_size == 128) return launch_typed<uint16_t, 128>(a, st);
+  const bool d64 = head_size == 64, d128 = head_size == 128;
+  if (dtype == PKV_F32 && d64) return launch_typed<float, 64>(a, st);
+  if (dtype == PKV_F32 && d128) return launch_typed<float, 128>(a, st);
+  if (dtype == PKV_BF16 && d64) return launch_typed<uint16_t, 64>(a, st);
+  if (dtype == PKV_BF16 && d128) return launch_typed<uint16_t, 128>(a, st);
+  if (dtype == PKV_F16 && d64) return launch_typed<_Float16, 64>(a, st);
+  if (dtype == PKV_F16 && d128) return launch_typed<_Float16, 128>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -19,6 +19,7 @@ PKV_OK = 0
 PKV_F32 = 0
 PKV_BF16 = 1
 PKV_FP8_E4M3 = 2
+PKV_F16 = 3
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
                 4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_METADATA", 7: "PKV_ERR_HIP"}
 
@@ -185,6 +186,8 @@ def _dtype_code(t) -> int:
         return PKV_F32
     if t.dtype == torch.bfloat16:
         return PKV_BF16
+    if t.dtype == torch.float16:
+        return PKV_F16
     if t.dtype == torch.float8_e4m3fn:
         return PKV_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")

@@ -389,9 +389,12 @@ CONFIG_NAMES = {
     8: "long_context_sliding_window_decode_bf16",
     9: "shared_prefix_cascade_decode_bf16",
     10: "mixed_chunked_prefill_decode_fp8",
+    11: "gqa_decode_f16",
+    12: "mixed_chunked_prefill_decode_f16",
 }
 
-DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3, 9: 5, 10: 4}   # 6, 7: the lengths and pools of 2, 3
+# 6, 7, 11: the lengths and pools of 2, 3, 3; 10, 12: those of 5
+DEFAULT_SEEDS = {1: 0, 2: 1, 3: 2, 4: 3, 5: 4, 6: 1, 7: 2, 8: 3, 9: 5, 10: 4, 11: 2, 12: 4}
 
 
 def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=None):
@@ -418,7 +421,7 @@ def config_lengths(cfg: int, rng: np.random.Generator, num_seqs=None, max_len=No
 def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = None,
                 max_len: Optional[int] = None, num_chunks: Optional[int] = None,
                 chunk_len: Optional[int] = None) -> Workload:
-    """Build workload `cfg` (1..10).  num_seqs / max_len / num_chunks /
+    """Build workload `cfg` (1..12).  num_seqs / max_len / num_chunks /
     chunk_len shrink it for quick parity runs; None keeps the full size."""
     if seed is None:
         seed = DEFAULT_SEEDS[cfg]
@@ -439,8 +442,9 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         L = config_lengths(4, meta, num_seqs, max_len)
         return make_decode(name, L, 64, 8, 128, 16, "bf16", seed, sigma=0.5,
                            partition_size=512, meta_rng=meta, root=root)
-    if cfg in (5, 10):
-        # 10: the same step over an fp8 cache (same lengths and pool)
+    if cfg in (5, 10, 12):
+        # 10, 12: the same step over an fp8 or a binary16 cache (same lengths
+        # and pool)
         nc = 4 if num_chunks is None else num_chunks
         cl = 512 if chunk_len is None else chunk_len
         nd = 128 if num_seqs is None else num_seqs
@@ -450,7 +454,7 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         dec_L = meta.integers(min(64, dec_hi), dec_hi, size=nd, endpoint=True)
         context = np.concatenate([ctx, dec_L - 1]).astype(np.int64)
         qlens = np.concatenate([np.full(nc, cl), np.ones(nd)]).astype(np.int64)
-        return make_varlen(name, context, qlens, 32, 8, 128, 32, "bf16" if cfg == 5 else "fp8",
+        return make_varlen(name, context, qlens, 32, 8, 128, 32, {5: "bf16", 10: "fp8", 12: "f16"}[cfg],
                            seed, causal=True, meta_rng=meta, root=root)
     if cfg == 8:
         # the shapes, lengths and pool of workload 4 with a 4096-key window
@@ -475,6 +479,10 @@ def make_config(cfg: int, seed: Optional[int] = None, num_seqs: Optional[int] = 
         L = config_lengths(cfg - 4, meta, num_seqs, max_len)
         hq, hkv = (32, 32) if cfg == 6 else (32, 8)
         return make_decode(name, L, hq, hkv, 128, 16, "fp8", seed, meta_rng=meta, root=root)
+    if cfg == 11:
+        # the GQA decode step of workload 3 over a binary16 cache
+        L = config_lengths(3, meta, num_seqs, max_len)
+        return make_decode(name, L, 32, 8, 128, 16, "f16", seed, meta_rng=meta, root=root)
     raise ValueError(cfg)
 
 

@@ -13,6 +13,16 @@ from paged_kv_cache_50_amd.workloads import DevWorkload, np_to_dev  # noqa: F401
 #   bfloat16 inputs, fp32 accumulation: |gpu - ref| <= 2e-2 + 1e-2 * |ref| per
 #   element, plus a relative L2 gate ||gpu - ref|| / ||ref|| <= 1e-2 so that a
 #   near-zero output cannot pass on the absolute term alone.
+#   binary16 inputs (no tolerance is stated for them; this one follows from
+#   the arithmetic): the output is rounded to binary16 (relative error <=
+#   2^-11), the matrix-core products take the probabilities as binary16
+#   operands (each rounded by <= 2^-11 relative, so the output moves by <=
+#   2^-11 max|V|), and a probability below binary16's normal range (2^-14)
+#   is off by at most 2^-25 absolute (<= n_keys 2^-25 max|V| in total, the
+#   largest probability being 1); everything else is fp32.  Per element:
+#   |gpu - ref| <= 2 (2^-11 |ref| + (2^-11 + n_keys 2^-25) max|V|) + 1e-6,
+#   and the relative L2 error <= 2e-3 (about 7x the 2^-11 / sqrt(3) a
+#   rounding of uniform error gives).
 # (label, pairs, seconds, threads) of every full oracle run, for the summary
 # that tests/conftest.py prints at the end of a session
 ORACLE_TIMES = []
@@ -21,6 +31,18 @@ F32_ATOL = 1e-5
 BF16_ATOL = 2e-2
 BF16_RTOL = 1e-2
 BF16_REL_L2 = 1e-2
+F16_REL_L2 = 2e-3
+
+
+def f16_bounds(w: W.Workload):
+    """(max |V| over the values attention may read, the most keys a row
+    sees) for the binary16 tolerance."""
+    vals = [w.v_cache[w.valid_slot_mask()]]
+    if w.value_new is not None:
+        vals.append(w.value_new.reshape(-1))
+    v = np.concatenate([x.reshape(-1) for x in vals]).view(np.float16).astype(np.float64)
+    v = v[np.isfinite(v)]          # slots the slot write has yet to fill hold NaN
+    return float(np.abs(v).max(initial=0.0)), int(w.max_seq_len)
 
 
 def torch():
@@ -32,7 +54,7 @@ def dev_to_bits(t_):
     """Raw storage bits of a device tensor as a numpy array (uint16/float32)."""
     t = torch()
     x = t_.detach().cpu()
-    if x.dtype == t.bfloat16:
+    if x.dtype in (t.bfloat16, t.float16):
         return x.view(t.int16).numpy().view(np.uint16)
     if x.dtype == t.float8_e4m3fn:
         return x.view(t.uint8).numpy()
@@ -163,23 +185,35 @@ def reference_full(w: W.Workload, threads=None, what=""):
 
 
 def assert_all_rows(gpu: np.ndarray, gpu_lse: np.ndarray, ref: np.ndarray, ref_lse: np.ndarray,
-                    dtype: str, what=""):
+                    dtype: str, what="", w: W.Workload = None):
     """Every output element finite and within tolerance, every lse within
     tolerance, for rows that belong to a sequence (the oracle leaves other
-    rows NaN)."""
+    rows NaN).  dtype 'f16' needs the workload w (its tolerance depends on
+    the values)."""
     owned = ~np.isnan(ref_lse)
     assert np.isfinite(gpu[owned]).all(), f"{what}: non-finite GPU output"
-    assert_close(gpu, ref, dtype, what)
+    assert_close(gpu, ref, dtype, what, w=w)
     lse_close(gpu_lse, ref_lse, what)
 
 
-def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what="", w: W.Workload = None):
     mask = ~np.isnan(ref)
     g, r = gpu[mask], ref[mask]
     assert np.isfinite(g).all(), f"{what}: non-finite GPU output"
     err = np.abs(g - r)
     if dtype == "f32":
         assert err.max(initial=0.0) <= F32_ATOL, f"{what}: max abs err {err.max():.3e} > {F32_ATOL}"
+    elif dtype == "f16":
+        assert w is not None, "the binary16 tolerance needs the workload"
+        vmax, nkeys = f16_bounds(w)
+        bound = 2.0 * (2.0 ** -11 * np.abs(r) + (2.0 ** -11 + nkeys * 2.0 ** -25) * vmax) + 1e-6
+        bad = err > bound
+        assert not bad.any(), (f"{what}: {bad.sum()} elements over the binary16 bound "
+                               f"(worst err {err.max():.3e}, max|V| {vmax:.3g}, keys {nkeys})")
+        nr = np.linalg.norm(r)
+        if nr > 0:
+            rel = np.linalg.norm(g - r) / nr
+            assert rel <= F16_REL_L2, f"{what}: relative L2 error {rel:.3e} > {F16_REL_L2}"
     else:
         bound = BF16_ATOL + BF16_RTOL * np.abs(r)
         bad = err > bound

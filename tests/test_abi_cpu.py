@@ -49,7 +49,10 @@ def test_binding_signatures_cover_header(L):
 def test_unsupported_reason(L):
     assert pagedkv.unsupported_reason(1, 128, 16, 32, 8) is None
     assert pagedkv.unsupported_reason(0, 64, 8, 8, 8) is None
+    assert pagedkv.unsupported_reason(pagedkv.PKV_F16, 64, 8, 8, 8) is None
+    assert pagedkv.unsupported_reason(pagedkv.PKV_F16, 128, 32, 32, 8) is None
     assert "dtype" in pagedkv.unsupported_reason(5, 128, 16, 32, 8)
+    assert "dtype" in pagedkv.unsupported_reason(4, 128, 16, 32, 8)
     assert "head_size" in pagedkv.unsupported_reason(1, 96, 16, 32, 8)
     assert "block_size" in pagedkv.unsupported_reason(1, 128, 64, 32, 8)
     assert "multiple" in pagedkv.unsupported_reason(1, 128, 16, 30, 8)
@@ -101,7 +104,8 @@ def test_decode_error_codes(L):
     assert decode(L, cache(k=0)) == 1                            # NULL cache
     assert decode(L, cache(), out=None) == 1
     assert decode(L, cache(), bt=None) == 1
-    assert decode(L, cache(dtype=3)) == 3                        # unsupported dtype
+    assert decode(L, cache(dtype=4)) == 3                        # unsupported dtype
+    assert decode(L, cache(dtype=-1)) == 3
     assert decode(L, cache(d=96)) == 3
     assert decode(L, cache(bs=64)) == 3
     assert decode(L, cache(), Hq=30) == 3                        # 30 % 8 != 0
@@ -247,7 +251,7 @@ def test_noalloc_decode_host_errors(L):
     big_S = 2048
     assert pagedkv.workspace_bytes(big_S, 32, 8, 128, 8192, 0) > pagedkv.NOALLOC_SCRATCH_BYTES
     assert f(*args(ctypes.byref(c), big_S, 8192)) == 5
-    assert f(*args(ctypes.byref(cache(dtype=3)), 4, 1000)) == 3       # the decode call's checks
+    assert f(*args(ctypes.byref(cache(dtype=4)), 4, 1000)) == 3       # the decode call's checks
     assert f(*args(ctypes.byref(c), -1, 1000)) == 2
     assert f(*args(ctypes.byref(c), 0, 1000)) == 0                    # empty batch: no-op
     # sizes the scratch array holds: the headline decode batches

@@ -89,6 +89,7 @@ def test_cascade_reason_thresholds(L):
     assert "8 requests" in r(4096, 7, 7, 32, 8, 128)
     assert "window" in r(4096, 256, 256, 32, 8, 128, window_left=100)
     assert r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_FP8_E4M3) is None
+    assert r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_F16) is None
     assert "bfloat16" in r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_F32)
     assert "bfloat16" in r(4096, 256, 256, 32, 8, 64)
     # long prefill chunks: every row recomputes the prefix on the matrix

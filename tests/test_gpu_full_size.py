@@ -4,8 +4,9 @@ configuration it times, against the oracle on EVERY (sequence, kv head) pair.
 For each of the Llama-7B-shaped MHA decode (64 sequences), the GQA decode
 (256 sequences, lognormal lengths), the long-context split decode (8
 sequences of 32k-131k tokens), the mixed chunked-prefill step, the fp8 forms
-of the first two and of the mixed step, the 4096-key sliding-window decode
-and the shared-prefix cascade: the GPU runs the whole batch once through the
+of the first two and of the mixed step, the 4096-key sliding-window decode,
+the shared-prefix cascade and the binary16 forms of the GQA decode and of the
+mixed step: the GPU runs the whole batch once through the
 C ABI, then every output element is checked to be finite and within the
 tolerance, and every lse against the oracle's.  The oracle runs per
 (sequence, kv head) pair in a thread pool and prints its wall time.
@@ -48,10 +49,12 @@ EXPECTED = {
     8: pagedkv.RAN_DECODE_MFMA,
     9: pagedkv.RAN_PLANNER | pagedkv.RAN_CASCADE_ONE | pagedkv.RAN_CASCADE_MERGE,
     10: pagedkv.RAN_PLANNER | pagedkv.RAN_MIXED,
+    11: pagedkv.RAN_PLANNER | pagedkv.RAN_DECODE_MFMA,
+    12: pagedkv.RAN_PLANNER | pagedkv.RAN_MIXED,
 }
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6, 7, 8, 9, 10])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12])
 def test_full_size_every_pair(cfg):
     torch = G.torch()
     w = W.make_config(cfg)
@@ -70,5 +73,5 @@ def test_full_size_every_pair(cfg):
     assert opts.launched & ~pagedkv.RAN_SPLIT_MERGE == EXPECTED[cfg], (opts.ran(), cfg)
     ref, ref_lse = G.reference_full(w)
     assert not np.isnan(ref_lse).any()               # every row belongs to a sequence
-    G.assert_all_rows(out, lse, ref, ref_lse, "f32" if w.dtype == "f32" else "bf16",
-                      f"workload {cfg} full size")
+    tol = w.dtype if w.dtype in ("f32", "f16") else "bf16"
+    G.assert_all_rows(out, lse, ref, ref_lse, tol, f"workload {cfg} full size", w=w)

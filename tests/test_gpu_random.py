@@ -1,5 +1,5 @@
 """A seeded random sweep of small batches against the oracle: cache dtype
-(fp32, bf16, fp8), head size, block size, kv heads and GQA group, decode
+(fp32, bf16, fp8; and a sweep of its own over binary16), head size, block size, kv heads and GQA group, decode
 batches and varlen batches mixing decode rows, prefill chunks and empty
 sequences, causal or not, sliding windows, partition sizes, and a forced
 kernel variant through the call's options.  Every case is reproducible from
@@ -15,6 +15,7 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 N_CASES = 256
+N_F16 = 64
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,10 +28,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def draw_case(i: int):
-    """Case i: (workload, partition_size, options, description)."""
-    rng = np.random.default_rng(10_000 + i)
-    dtype = str(rng.choice(["f32", "bf16", "bf16", "fp8"]))
+def draw_case(i: int, dtype=None, base=10_000):
+    """Case i: (workload, partition_size, options, description).  dtype, if
+    given, replaces the drawn cache dtype (base then keeps the seeds apart
+    from the mixed-dtype sweep)."""
+    rng = np.random.default_rng(base + i)
+    drawn = str(rng.choice(["f32", "bf16", "bf16", "fp8"]))
+    dtype = dtype or drawn
     head = 128 if dtype == "fp8" else int(rng.choice([64, 128]))
     bs = int(rng.choice([8, 16, 32]))
     hkv = int(rng.choice([1, 2, 4, 8]))
@@ -41,7 +45,7 @@ def draw_case(i: int):
     if decode:
         L = rng.integers(0, 1600, S)
         L[rng.random(S) < 0.15] = 0                    # padding rows
-        w = W.make_decode(f"random{i}", L, hkv * group, hkv, head, bs, dtype, seed=20_000 + i)
+        w = W.make_decode(f"random{i}", L, hkv * group, hkv, head, bs, dtype, seed=2 * base + i)
     else:
         ctx = rng.integers(0, 1500, S)
         ql = np.where(rng.random(S) < 0.5, 1, rng.integers(2, 130, S))
@@ -49,7 +53,7 @@ def draw_case(i: int):
         ql[empty] = 0
         ctx[empty] = 0
         w = W.make_varlen(f"random{i}", ctx, ql, hkv * group, hkv, head, bs, dtype,
-                          seed=20_000 + i, causal=causal)
+                          seed=2 * base + i, causal=causal)
     if rng.random() < 0.3:
         w.window_left = int(rng.integers(0, 700))
     ps = int(rng.choice([0, -1, 32, 96, 256, 512]))
@@ -80,14 +84,26 @@ def test_random_case_matches_oracle(i):
                       "f32" if w.dtype == "f32" else "bf16", desc)
 
 
+@pytest.mark.parametrize("i", range(N_F16))
+def test_random_f16_case_matches_oracle(i):
+    w, ps, opts, desc = draw_case(i, dtype="f16", base=50_000)
+    print(f"[gpu-test] {desc}", flush=True)
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=ps, options=pagedkv.CallOptions(**opts))
+    ref, ref_lse = G.reference(w)
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "f16", desc, w=w)
+
+
 N_CASCADE = 64
+N_CASCADE_F16 = 32
 
 
-def draw_cascade(i: int):
+def draw_cascade(i: int, dtype=None, base=30_000):
     """Cascade case i: a shared prefix of whole blocks in every non-empty
     sequence's context, then each sequence's own keys and query rows."""
-    rng = np.random.default_rng(30_000 + i)
-    dtype = str(rng.choice(["bf16", "bf16", "fp8"]))
+    rng = np.random.default_rng(base + i)
+    drawn = str(rng.choice(["bf16", "bf16", "fp8"]))
+    dtype = dtype or drawn
     bs = int(rng.choice([8, 16, 32]))
     hkv = int(rng.choice([1, 2, 4, 8]))
     group = int(rng.choice([1, 4, 8]))
@@ -104,7 +120,7 @@ def draw_cascade(i: int):
     if empty.all():
         ql[0], ctx[0] = 1, cpl
     w = W.make_varlen(f"random_cascade{i}", ctx, ql, hkv * group, hkv, 128, bs, dtype,
-                      seed=40_000 + i, causal=causal, common_prefix_len=cpl)
+                      seed=base + 10_000 + i, causal=causal, common_prefix_len=cpl)
     ps = int(rng.choice([0, -1, 64, 256]))
     opts = {"cascade_launch": int(rng.integers(0, 2))}
     desc = (f"cascade {i}: {dtype} bs{bs} {hkv * group}/{hkv} heads, {S} seqs, prefix {cpl}, "
@@ -121,3 +137,13 @@ def test_random_cascade_matches_oracle(i):
     G.run_cascade(dw, partition_size=ps, options=pagedkv.CallOptions(**opts))
     ref, ref_lse = G.reference(w)
     G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "bf16", desc)
+
+
+@pytest.mark.parametrize("i", range(N_CASCADE_F16))
+def test_random_f16_cascade_matches_oracle(i):
+    w, ps, opts, desc = draw_cascade(i, dtype="f16", base=70_000)
+    print(f"[gpu-test] {desc}", flush=True)
+    dw = G.DevWorkload(w)
+    G.run_cascade(dw, partition_size=ps, options=pagedkv.CallOptions(**opts))
+    ref, ref_lse = G.reference(w)
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "f16", desc, w=w)

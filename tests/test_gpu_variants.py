@@ -37,7 +37,8 @@ def _check(w, dw, opts, want, ps, what, key_span=None):
     batch needs the merge launch depends on the launch geometry: a row whose
     partitions all fall to one workgroup is finished by it.)"""
     ref, ref_lse = G.reference(w)
-    G.assert_close(G.dev_to_f64(dw.out), ref, "f32" if w.dtype == "f32" else "bf16", what)
+    tol = w.dtype if w.dtype in ("f32", "f16") else "bf16"
+    G.assert_close(G.dev_to_f64(dw.out), ref, tol, what, w=w)
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, what)
     assert opts.launched & ~P.RAN_SPLIT_MERGE == want, (what, opts.ran())
     span = w.max_seq_len if key_span is None else key_span
@@ -76,6 +77,20 @@ CASES = [
      P.RAN_PLANNER | P.RAN_MIXED),
     (10, dict(num_seqs=9, max_len=900, num_chunks=2, chunk_len=70), 0, dict(mixed_launch=1),
      P.RAN_PREFILL_MFMA | P.RAN_DECODE_MFMA | P.RAN_DECODE_PAIRS),
+    # binary16 caches: the same choices as bfloat16
+    (11, dict(num_seqs=70, max_len=1200), 0, {},
+     P.RAN_PLANNER | P.RAN_DECODE_MFMA),
+    (11, dict(num_seqs=70, max_len=1200), 0, dict(decode_kernel=1),
+     P.RAN_DECODE_VALU),
+    (11, dict(num_seqs=10, max_len=1200), 128, {}, P.RAN_DECODE_MFMA),
+    (12, dict(num_seqs=9, max_len=900, num_chunks=2, chunk_len=70), 0, {},
+     P.RAN_PLANNER | P.RAN_MIXED),
+    (12, dict(num_seqs=9, max_len=900, num_chunks=2, chunk_len=70), 0, dict(mixed_launch=1),
+     P.RAN_PREFILL_MFMA | P.RAN_DECODE_MFMA),
+    (12, dict(num_seqs=9, max_len=900, num_chunks=2, chunk_len=70), 0, dict(prefill_kernel=1),
+     P.RAN_PREFILL_VALU | P.RAN_DECODE_MFMA),
+    (12, dict(num_seqs=9, max_len=900, num_chunks=2, chunk_len=70), 0,
+     dict(prefill_kernel=1, decode_kernel=1), P.RAN_PREFILL_VALU | P.RAN_DECODE_VALU),
 ]
 
 
