@@ -13,13 +13,14 @@ MHA decode unless --workload names another); `roofline` is the dominant
 kernel's achieved rate against the MI355X peak, from per-launch HIP events
 recorded by the library inside the timed region; `per_workload` repeats the
 measurement, in the same run, for the GQA decode, the long-context split
-decode, the mixed chunked-prefill step and workloads 6-10 (fp8 caches, a
-sliding window, a shared-prefix cascade; default run only); `cpu_baseline`
+decode, the mixed chunked-prefill step and workloads 6-12 (fp8 caches, a
+sliding window, a shared-prefix cascade, binary16 caches; default run
+only); `cpu_baseline`
 times the fp64 CPU oracle on the headline workload (BLAS threads = the
 host cores this process may use) and, single-threaded, on the three small
 decode workloads.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..10]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..12]
 """
 from __future__ import annotations
 
@@ -37,13 +38,13 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + µs/step, 1 MI355X"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 (and fp16) MFMA, published
 MALL_BYTES = 256 << 20         # MI355X last-level (Infinity) cache
 
 HEADLINE = 2                   # Llama-7B-shaped MHA decode
-# GQA decode, long-context split decode, mixed step, then the fp8, sliding-window and
-# shared-prefix workloads
-PER_WORKLOAD = (3, 4, 5, 6, 7, 8, 9, 10)
+# GQA decode, long-context split decode, mixed step, then the fp8, sliding-window,
+# shared-prefix and binary16 workloads
+PER_WORKLOAD = (3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
 
 WORKLOAD_DESC = {
     1: "4 seqs, 8/8 heads, head 64, block 16, fp32, seq_lens U[1,256], seed 0",
@@ -56,6 +57,8 @@ WORKLOAD_DESC = {
     8: "workload 4 (same lengths and pool) with a 4096-key sliding window (window_left 4095)",
     9: "slot write + cascade attention: 256 decode requests sharing a 4096-token prefix, own context U[0,1023] + 1 new token, 32/8 heads, head 128, block 16, bf16, seed 5",
     10: "workload 5 (same lengths and pool) over an fp8 e4m3 cache with per-kv-head scales; q/out bf16",
+    11: "workload 3 (same lengths and pool) over a binary16 (fp16) cache; q/out fp16",
+    12: "workload 5 (same lengths and pool) over a binary16 (fp16) cache; q/out fp16",
 }
 
 
@@ -487,9 +490,9 @@ def main() -> int:
     # and at least this long: after 10 steps the mixed and fp8 steps still
     # ran 4-6 % slower than after a second of them
     ap.add_argument("--warmup-s", type=float, default=1.0)
-    ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 11)),
+    ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 13)),
                     help="measure only this workload (default: the headline MHA decode, plus "
-                         "workloads 3-10 as per_workload)")
+                         "workloads 3-12 as per_workload)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
@@ -557,7 +560,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8 e4m3 cache, bf16 q/out"}[w.dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "f16": "f16",
+                  "fp8": "fp8 e4m3 cache, bf16 q/out"}[w.dtype],
         "data": "synthetic (seeded; shapes and length distributions of the workload)",
         "config": {"workload": w.name, "description": WORKLOAD_DESC[head],
                    "num_seqs": w.num_seqs, "query_rows": w.num_q_rows, "num_heads": w.num_heads,

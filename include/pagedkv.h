@@ -134,8 +134,8 @@ typedef struct pkv_kv_cache {
  */
 typedef struct pkv_call_options {
   int32_t decode_kernel;   /* 0 library choice; 1 the VALU kernel; 2 the matrix-core
-                              kernel (bfloat16 caches with head_size 128)          */
-  int32_t prefill_kernel;  /* 0 library choice; 1 the VALU row kernel (bfloat16)     */
+                              kernel (16-bit caches with head_size 128)            */
+  int32_t prefill_kernel;  /* 0 library choice; 1 the VALU row kernel (16-bit)       */
   int32_t fp8_head_pairs;  /* 0 library choice; 1 one kv head per wave in fp8 decode  */
   int32_t mixed_launch;    /* 0 library choice; 1 prefill rows and decode rows of a
                               varlen batch in separate launches                     */
@@ -317,14 +317,15 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
  *                  block_tables will do)
  *   other arguments as for pkv_paged_attention_varlen
  *   workspace      >= pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned
- * Needs a bfloat16 or fp8 (e4m3) cache with head_size 128
+ * Needs a bfloat16, binary16 or fp8 (e4m3) cache with head_size 128
  * (PKV_ERR_UNSUPPORTED otherwise) and, when common_prefix_len > 0, a
  * positive scale (PKV_ERR_SHAPE otherwise) and positive fp8 k_scale entries,
  * as for the prefill rows of pkv_paged_attention_varlen: the prefix pass is
  * the prefill kernel.  common_prefix_len 0 is the plain varlen call.
  * Asynchronous on `stream`.
- * The suffix result is rounded to bfloat16 before the merge, as the output of
- * the pages' suffix call is; the prefix partials stay fp32.
+ * The suffix result is rounded to the output dtype (bfloat16 or binary16)
+ * before the merge, as the output of the pages' suffix call is; the prefix
+ * partials stay fp32.
  */
 pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* cache,
                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens,
