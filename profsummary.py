@@ -26,6 +26,7 @@ import collections
 import csv
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -43,11 +44,40 @@ COPY_CMD = ("rocprofv3 --pmc {ctr} --output-format csv -d $REPO/gpurun_out/prof/
             "-- python3 $REPO/bench.py --copy-calibration 1024")
 
 
+# Itanium-mangled template arguments of this library's kernels, for names the
+# profiler leaves mangled (it does not demangle _Float16, "DF16_").
+_MANGLED_ARGS = [(r"Li(-?\d+)E", r"\1"), (r"Lb0E", "false"), (r"Lb1E", "true"),
+                 (r"DF16_", "_Float16"), (r"^t", "unsigned short"), (r"^f", "float")]
+
+
+def _demangle_pkv(name: str) -> str:
+    """`_ZN3pkv12_GLOBAL__N_1<len><ident>I<args>EEvNS_8AttnArgsE` ->
+    `<ident><args>`; other names are returned unchanged."""
+    m = re.match(r"_ZN3pkv12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    rest = name[m.end():]
+    ident, rest = rest[:int(m.group(1))], rest[int(m.group(1)):]
+    if not rest.startswith("I"):
+        return ident
+    rest, args = rest[1:], []
+    while rest and not rest.startswith("E"):
+        for pat, rep in _MANGLED_ARGS:
+            a = re.match(pat if pat.startswith("^") else "^" + pat, rest)
+            if a:
+                args.append(a.expand(rep) if "\\" in rep else rep)
+                rest = rest[a.end():]
+                break
+        else:
+            return name
+    return f"{ident}<{', '.join(args)}>"
+
+
 def short(name: str) -> str:
     """`void pkv::(anonymous namespace)::attn_valu_kernel<...>(pkv::AttnArgs)` -> base name."""
     n = name.split("(pkv::")[0]
     n = n.replace("void ", "").replace("pkv::(anonymous namespace)::", "")
-    return n
+    return _demangle_pkv(n)
 
 
 def base(name: str) -> str:
