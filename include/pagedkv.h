@@ -107,7 +107,7 @@ typedef struct pkv_kv_cache {
   void*   k_cache;       /* device [num_blocks, block_size, num_kv_heads, head_size] */
   void*   v_cache;       /* device, same shape, dtype and block_stride as k_cache    */
   int64_t num_blocks;    /* pool size, > 0                                          */
-  int32_t block_size;    /* tokens per block: 8, 16 or 32                           */
+  int32_t block_size;    /* tokens per block: 8, 16, 32, 64 or 128                  */
   int32_t num_kv_heads;  /* > 0                                                     */
   int32_t head_size;     /* 64 or 128                                               */
   int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value, which

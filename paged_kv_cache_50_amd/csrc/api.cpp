@@ -78,8 +78,9 @@ const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t
     return "dtype must be PKV_F32, PKV_BF16, PKV_F16 or PKV_FP8_E4M3";
   if (dtype == PKV_FP8_E4M3 && head_size != 128) return "fp8 caches need head_size 128";
   if (head_size != 64 && head_size != 128) return "head_size must be 64 or 128";
-  if (block_size != 8 && block_size != 16 && block_size != 32)
-    return "block_size must be 8, 16 or 32";
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 &&
+      block_size != 128)
+    return "block_size must be 8, 16, 32, 64 or 128";
   if (num_kv_heads <= 0) return "num_kv_heads must be positive";
   if (num_heads <= 0) return "num_heads must be positive";
   if (num_heads % num_kv_heads != 0) return "num_heads must be a multiple of num_kv_heads";

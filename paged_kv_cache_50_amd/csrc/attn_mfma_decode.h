@@ -103,13 +103,15 @@ template <int BS, int DT, int HP>
 __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, int bz, int nz,
                                              char* __restrict__ s_lds, float (*s_m)[32],
                                              float (*s_l)[32]) {
-  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64 || BS == 128, "block size");
   static_assert(DT == PKV_BF16 || DT == PKV_F16 || DT == PKV_FP8_E4M3, "cache dtype");
   constexpr bool FP8 = DT == PKV_FP8_E4M3;
   using H = Fmt16<DT == PKV_F16>;                    // operand format of the products
   using x8 = typename H::x8;
   static_assert(HP == 1 || (HP == 2 && FP8), "two heads per wave: e4m3 caches");
-  constexpr int kBlkPerTile = kTile / BS;
+  // blocks a 32-token tile spans; a tile of larger blocks lies inside one
+  // block (tiles start at multiples of 32 positions), at offset tbase % BS
+  constexpr int kBlkPerTile = BS < kTile ? kTile / BS : 1;
   constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
   // bytes of one token's row as a wave reads it: HP adjacent kv heads
   constexpr int kRowBytes = HP * kD * kEB;
@@ -192,19 +194,22 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   // the wave's LDS: HP areas of kWaveLds bytes, one per head
   char* wlds = s_lds + wave * HP * kWaveLds;
 
-  // Block ids of one tile (wave uniform, scalar loads), fetched a step early.
+  // Block ids of one tile (wave uniform, scalar loads), fetched a step
+  // early, as byte offsets of the tile's first token row in each block.
   auto fetch_ids = [&](int tile, int64_t* ids) {
     const int tbase = pstart + tile * kTile;
 #pragma unroll
     for (int b = 0; b < kBlkPerTile; ++b) {
       const int bi = __builtin_amdgcn_readfirstlane(min(tbase / BS + b, last_bi));
       ids[b] = min((int64_t)max(load_uniform_i32(bt, bi), 0), max_blk) * blk_stride;
+      if constexpr (BS > kTile) ids[b] += (int64_t)(tbase % BS) * tok_stride;
     }
   };
 
   // K (or V) loads of one tile: kLoads natural loads, each kRowsPerLoad
   // whole token rows (row kRowsPerLoad * i + lrow, 16 bytes at lbyte).  Each
-  // such group of rows lies in one block.
+  // such group of rows lies in one block (for blocks larger than the tile,
+  // tok % BS = tok and ids[0] already points at the tile's first row).
   auto issue = [&](const char* cache, const int64_t* ids, u32x4* R) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {

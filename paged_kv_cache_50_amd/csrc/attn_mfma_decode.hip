@@ -25,6 +25,8 @@ hipError_t launch_typed(const AttnArgs& a, int block_size, dim3 grid, hipStream_
     case 8: hipLaunchKernelGGL((attn_mfma_decode_kernel<8, DT, HP>), grid, dim3(dec::kThreads), 0, stream, a); break;
     case 16: hipLaunchKernelGGL((attn_mfma_decode_kernel<16, DT, HP>), grid, dim3(dec::kThreads), 0, stream, a); break;
     case 32: hipLaunchKernelGGL((attn_mfma_decode_kernel<32, DT, HP>), grid, dim3(dec::kThreads), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((attn_mfma_decode_kernel<64, DT, HP>), grid, dim3(dec::kThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((attn_mfma_decode_kernel<128, DT, HP>), grid, dim3(dec::kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -289,7 +289,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // tid loads codes 16 (tid%8) .. +15 of token r = tid/8 (each wave covers 8
   // consecutive tokens, inside one block), into the stage row r.
   // Lane part (bytes) of the loads of a tile inside the key range: token
-  // t * 32 + r sits at offset r % BS of its block (32 is a multiple of BS).
+  // t * 32 + r sits at offset r % BS of its block when 32 is a multiple of
+  // BS; with larger blocks at offset (t * 32) % BS + r, the first term added
+  // per tile.
   constexpr int kEB = FP8 ? 1 : 2;                   // cache element bytes
   uint32_t klane[2], vlane[2];
 #pragma unroll
@@ -309,6 +311,9 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
   // the last valid one, which stays in the block of the wave's first token
   auto issue = [&](int t, const int32_t* raw, char* buf, auto full_tag) {
     const bool full = decltype(full_tag)::value || (t + 1) * kTile <= kv_end;
+    // blocks larger than a tile: the tile's first row within its block
+    uint32_t toff = 0;
+    if constexpr (BS > kTile) toff = ((uint32_t)(t * kTile) % BS) * tok_stride * kEB;
 #pragma unroll
     for (int u = 0; u < (FP8 ? 1 : 2); ++u) {
       const uint64_t boff = (uint64_t)min((uint32_t)max(raw[u], 0), max_blk) * blk_bytes;
@@ -317,8 +322,8 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
       char* kdst = buf + (FP8 ? 0 : u * 4096) + wave * 1024;
       char* vdst = buf + (FP8 ? kKBytes8 : kKBytes + u * 4096) + wave * 1024;
       if (full) {
-        __builtin_amdgcn_global_load_lds(kb + klane[u], (lds_void*)kdst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + vlane[u], (lds_void*)vdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kb + toff + klane[u], (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + toff + vlane[u], (lds_void*)vdst, 16, 0, 0);
       } else if constexpr (FP8) {
         const int r = tid >> 3;
         const int tok = min(t * kTile + r, last_tok);

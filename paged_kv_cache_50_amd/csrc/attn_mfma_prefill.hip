@@ -35,6 +35,8 @@ hipError_t launch_bs(const AttnArgs& a, int block_size, dim3 grid, hipStream_t s
     case 8: return launch_one<PREFIX, 8, DT>(a, grid, stream);
     case 16: return launch_one<PREFIX, 16, DT>(a, grid, stream);
     case 32: return launch_one<PREFIX, 32, DT>(a, grid, stream);
+    case 64: return launch_one<PREFIX, 64, DT>(a, grid, stream);
+    case 128: return launch_one<PREFIX, 128, DT>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

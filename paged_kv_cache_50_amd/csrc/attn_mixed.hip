@@ -94,6 +94,8 @@ hipError_t launch(const AttnArgs& pre, const AttnArgs& dcd, const MixedGrid& g, 
     case 8: hipLaunchKernelGGL((attn_mixed_kernel<8, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
     case 16: hipLaunchKernelGGL((attn_mixed_kernel<16, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
     case 32: hipLaunchKernelGGL((attn_mixed_kernel<32, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
+    case 64: hipLaunchKernelGGL((attn_mixed_kernel<64, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
+    case 128: hipLaunchKernelGGL((attn_mixed_kernel<128, CASCADE, DT>), grid, block, 0, stream, pre, dcd, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -362,6 +362,8 @@ static hipError_t launch_bs(const AttnArgs& a, int bs, int gt, dim3 grid, hipStr
     case 8: return launch_gt<T, D, 8>(a, gt, grid, st);
     case 16: return launch_gt<T, D, 16>(a, gt, grid, st);
     case 32: return launch_gt<T, D, 32>(a, gt, grid, st);
+    case 64: return launch_gt<T, D, 64>(a, gt, grid, st);
+    case 128: return launch_gt<T, D, 128>(a, gt, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

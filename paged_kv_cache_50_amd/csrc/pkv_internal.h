@@ -102,7 +102,8 @@ void timing_end(hipStream_t st, int slot);
 hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8, hipStream_t stream);
 
 // General VALU attention kernel: float32, bfloat16 or binary16 caches (dtype
-// is the pkv_dtype), head size 64/128, block size 8/16/32, any GQA ratio.
+// is the pkv_dtype), head size 64/128, block size 8/16/32/64/128, any GQA
+// ratio.
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream);
 

@@ -54,7 +54,10 @@ def test_unsupported_reason(L):
     assert "dtype" in pagedkv.unsupported_reason(5, 128, 16, 32, 8)
     assert "dtype" in pagedkv.unsupported_reason(4, 128, 16, 32, 8)
     assert "head_size" in pagedkv.unsupported_reason(1, 96, 16, 32, 8)
-    assert "block_size" in pagedkv.unsupported_reason(1, 128, 64, 32, 8)
+    for bs in (8, 16, 32, 64, 128):
+        assert pagedkv.unsupported_reason(1, 128, bs, 32, 8) is None
+    for bs in (4, 48, 96, 256):
+        assert "block_size" in pagedkv.unsupported_reason(1, 128, bs, 32, 8)
     assert "multiple" in pagedkv.unsupported_reason(1, 128, 16, 30, 8)
 
 
@@ -107,7 +110,8 @@ def test_decode_error_codes(L):
     assert decode(L, cache(dtype=4)) == 3                        # unsupported dtype
     assert decode(L, cache(dtype=-1)) == 3
     assert decode(L, cache(d=96)) == 3
-    assert decode(L, cache(bs=64)) == 3
+    assert decode(L, cache(bs=48)) == 3
+    assert decode(L, cache(bs=256)) == 3
     assert decode(L, cache(), Hq=30) == 3                        # 30 % 8 != 0
     assert decode(L, cache(k=A_ODD)) == 4                        # misaligned cache
     assert decode(L, cache(), q=A_ODD) == 4

@@ -198,14 +198,15 @@ def test_oracle_block_permutation_invariant():
 
 
 def test_oracle_block_size_equivalence():
-    """The same logical K/V stored with block size 8, 16 and 32 gives
-    bit-identical outputs."""
+    """The same logical K/V stored with block size 8, 16, 32, 64 and 128
+    gives bit-identical outputs (sequences shorter than, equal to and longer
+    than one large block)."""
     rng = np.random.default_rng(6)
-    seq_lens = [5, 31, 70, 96]
+    seq_lens = [5, 31, 70, 96, 128, 200]
     Kc, Vc, bt, _, _ = tiny_pool(rng, seq_lens, 2, 16, 8)
-    q = rng.standard_normal((4, 2, 16)).astype(np.float32)
+    q = rng.standard_normal((6, 2, 16)).astype(np.float32)
     ref = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), 0.3, 8, "f32")
-    for bs in (16, 32):
+    for bs in (16, 32, 64, 128):
         K2, V2, bt2 = repack(Kc, bt, seq_lens, 8, bs, rng, Vc)
         got = oracle.paged_attention(q, K2, V2, bt2, np.array(seq_lens), 0.3, bs, "f32")
         assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
