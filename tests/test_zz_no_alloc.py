@@ -58,7 +58,8 @@ def _check(w, ps=None, opts=None, what=""):
     assert np.array_equal(out1, out2), f"{what}: output differs from the workspace entry point"
     assert np.array_equal(lse1, lse2), f"{what}: lse differs from the workspace entry point"
     ref, ref_lse = G.reference_full(w, what=what)
-    G.assert_all_rows(out_f64, lse2, ref, ref_lse, "f32" if w.dtype == "f32" else "bf16", what)
+    tol = w.dtype if w.dtype in ("f32", "f16") else "bf16"
+    G.assert_all_rows(out_f64, lse2, ref, ref_lse, tol, what, w=w)
     return l2
 
 
@@ -78,6 +79,9 @@ def test_noalloc_other_kernels_consecutive():
     _check(W.make_config(2, num_seqs=24, max_len=4096), what="MHA 24 seqs")
     _check(W.make_config(4, num_seqs=2, max_len=40000), what="long context 2 seqs")
     _check(W.make_config(7, num_seqs=30, max_len=3000), ps=256, what="fp8 GQA 30 seqs")
+    _check(W.make_config(11, num_seqs=40, max_len=3000), what="fp16 GQA 40 seqs")
+    w = W.make_decode("noalloc_bs128", [700, 1500, 129, 3000], 32, 8, 128, 128, "bf16", seed=12)
+    _check(w, what="GQA over 128-token blocks")
     _check(W.make_config(2, num_seqs=5, max_len=400), ps=-1, what="MHA unsplit")
     _check(W.make_config(3, num_seqs=9, max_len=1000), ps=128, opts=dict(decode_kernel=1),
            what="GQA on the VALU kernel")
