@@ -487,9 +487,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
-    # and at least this long: after 10 steps the mixed and fp8 steps still
-    # ran 4-6 % slower than after a second of them
-    ap.add_argument("--warmup-s", type=float, default=1.0)
+    # and at least this long: under sustained load the GPU settles within
+    # about 3 s (the headline decode measured 352-355 us per step in the
+    # first 2.5 s of a process and 342-345 us after 3 s; the mixed and fp8
+    # steps were 4-6 % slower after 10 steps than after a second)
+    ap.add_argument("--warmup-s", type=float, default=3.0)
     ap.add_argument("--workload", type=int, default=None, choices=list(range(1, 13)),
                     help="measure only this workload (default: the headline MHA decode, plus "
                          "workloads 3-12 as per_workload)")

@@ -140,8 +140,12 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int n = lane & 15;     // MFMA column (query head) / A row (token or dim)
   const int kg = lane >> 4;    // k group / token row of a natural load
   const int group = a.num_heads / a.num_kv_heads;
-  // HP == 2: bx is a pair of kv heads (head_chunks is 1), 2 bx and 2 bx + 1
-  const int kvh = HP == 2 ? 2 * bx : bx / a.head_chunks;
+  // HP == 2: bx is a pair of kv heads (head_chunks is 1), 2 bx and 2 bx + 1.
+  // With one column per kv head (or pair), adjacent 256-byte rows swap
+  // columns (column_head).
+  const int kvh = HP == 2 ? 2 * column_head(bx, a.num_kv_heads / 2, kRowBytes)
+                          : (a.head_chunks == 1 ? column_head(bx, a.num_kv_heads, kRowBytes)
+                                                : bx / a.head_chunks);
   const int chunk = HP == 2 ? 0 : bx % a.head_chunks;
   const int h0 = kvh * group + chunk * 16;           // first query head of head hp: h0 + hp * group
   const int G = min(16, group - chunk * 16);

@@ -151,7 +151,9 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int group = a.num_heads / a.num_kv_heads;
-  const int kvh = blockIdx.x / a.head_chunks;
+  // one column per kv head: adjacent heads swap columns (column_head)
+  const int kvh = a.head_chunks == 1 ? column_head(blockIdx.x, a.num_kv_heads, D * E)
+                                     : blockIdx.x / a.head_chunks;
   const int h0 = kvh * group + (blockIdx.x % a.head_chunks) * GT;
 
   const int pstart = it.base + part * it.P;
