@@ -203,12 +203,19 @@ def spin_cycles_for(us: float, dev) -> int:
     return max(1000, int(us / max(per_cycle_us, 1e-9)))
 
 
-def measure(w, args, dev, ps, cpu_label=False) -> dict:
+def measure(w, args, dev, ps, cpu_label=False, graph=False) -> dict:
     """Warm-up, then exactly args.steps timed steps between two events on the
     stream (HIP events around the dominant kernel of one step in ten inside
-    that region), then, outside it: the per-step distribution, a HIP-graph
-    replay, and for kernels under 50 us a re-timing of the dominant kernel
-    with the queue kept ahead of the GPU."""
+    that region), then, outside it: the per-step distribution, for kernels
+    under 50 us a re-timing of the dominant kernel with the queue kept ahead
+    of the GPU, and with graph=True a HIP-graph replay.  Before the timed
+    region a probe records the XCD the dispatcher starts launches on.
+
+    Everything runs on the current stream except the graph capture, which
+    needs streams of its own; capturing moves where the dispatcher starts
+    the current stream's later launches, and the decode kernels' speed
+    depends on that start by a few per cent, so callers measure every
+    workload before they ask for a graph replay."""
     import numpy as np
     import torch
     from paged_kv_cache_50_amd import pagedkv, workloads as W
@@ -272,6 +279,7 @@ def measure(w, args, dev, ps, cpu_label=False) -> dict:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     launched = opts.launched
+    dispatch_xcds = pagedkv.xcd_probe(8)  # where this stream's launches start
     pagedkv.timing_read()                 # drop anything recorded before
     # HIP events around the dominant kernel of one step in ten (each record
     # adds a few microseconds of stream time, so they are sampled)
@@ -301,30 +309,31 @@ def measure(w, args, dev, ps, cpu_label=False) -> dict:
     torch.cuda.synchronize()
     per_step_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
     graph_us = None
-    try:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()                                  # warm the side stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_us = g0.elapsed_time(g1) * 1e3 / args.steps
-        del g
-    except Exception as exc:                        # reported, never fatal
-        print(f"[bench] graph replay unavailable: {exc}", file=sys.stderr, flush=True)
+    if graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()                                  # warm the side stream
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for _ in range(args.steps):
+                g.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            graph_us = g0.elapsed_time(g1) * 1e3 / args.steps
+            del g
+        except Exception as exc:                        # reported, never fatal
+            print(f"[bench] graph replay unavailable: {exc}", file=sys.stderr, flush=True)
 
     # A HIP event that the GPU reaches before the host has queued the next
     # launch also times the host's launch latency, which is not negligible
@@ -373,6 +382,7 @@ def measure(w, args, dev, ps, cpu_label=False) -> dict:
             "kernel_launches_timed": len(kern_ms), "launched": launched,
             "per_step_us": per_step_us, "graph_us": graph_us, "plain_us": plain_us,
             "warmup_steps_run": n_warm, "cache_copies": n_copies,
+            "dispatch_xcds": dispatch_xcds,
             "cache_resident": cache_resident, "bytes": B}
 
 
@@ -472,6 +482,9 @@ def record(w, m, steps, ps) -> dict:
            "graph_replay_us_per_step": round(m["graph_us"], 2) if m["graph_us"] else None,
            "kernels_launched": P.CallOptions(launched=m["launched"]).ran(),
            "warmup_steps_run": m["warmup_steps_run"],
+           # XCD of the first workgroup of a launch on the timed stream: the
+           # decode kernels lay out their columns for a start at XCD 0
+           "dispatch_start_xcd": m["dispatch_xcds"][0],
            "roofline": roofline(w, m)}
     if m["cache_copies"] > 1:
         rec["cache_copies_rotated"] = m["cache_copies"]
@@ -559,6 +572,7 @@ def main() -> int:
         "tokens_per_s": r["tokens_per_s"],
         "step_us_p10_p50_p90": r["step_us_p10_p50_p90"],
         "graph_replay_us_per_step": r["graph_replay_us_per_step"],
+        "dispatch_start_xcd": r["dispatch_start_xcd"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -602,6 +616,12 @@ def main() -> int:
             else:
                 del wc
         rec["per_workload"] = per
+    # The headline's step replayed as a HIP graph, last: capturing a graph
+    # moves where the dispatcher starts later launches on this stream.
+    warm = argparse.Namespace(**{**vars(args), "warmup": 10, "warmup_s": 0.2})
+    rec["graph_replay_us_per_step"] = measure(w, warm, dev, ps, graph=True)["graph_us"]
+    if rec["graph_replay_us_per_step"] is not None:
+        rec["graph_replay_us_per_step"] = round(rec["graph_replay_us_per_step"], 2)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, hosts)

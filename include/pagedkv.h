@@ -426,6 +426,20 @@ pkv_status pkv_timing_enable(int32_t every_n);
 int32_t pkv_timing_read(float* ms, int32_t cap);
 
 /*
+ * Dispatch probe (benchmark support): launches n one-wave workgroups on
+ * `stream`; workgroup i writes to xcd_out[i] the index (0-7) of the XCD it
+ * ran on.  The hardware places consecutive workgroups of a launch on
+ * consecutive XCDs from a start that is dispatcher state (the same for
+ * consecutive launches on a queue; it can change when other queues run),
+ * and the decode kernels' speed depends on it by a few per cent, so a
+ * benchmark records it beside its timings.
+ *   xcd_out  device int32 [n], 1 <= n <= 1024
+ * Returns PKV_ERR_NULL, PKV_ERR_SHAPE (n out of range) or PKV_ERR_HIP.
+ * Asynchronous on `stream`.
+ */
+pkv_status pkv_xcd_probe(int32_t* xcd_out, int32_t n, void* stream);
+
+/*
  * Host KV block pool: the step before the attention calls, which hands out
  * the cache's physical blocks to requests and produces their block tables
  * and slot mappings (vLLM book, ch. 4.1 and 4.4; «Khám phá vLLM»,

@@ -100,3 +100,23 @@ int32_t pkv_timing_read(float* ms, int32_t cap) {
 }
 
 }  // extern "C"
+
+// ---- dispatch probe
+
+namespace {
+
+// Workgroup i writes the XCD it runs on (hardware register XCC_ID, bits 3:0).
+__global__ void __launch_bounds__(64) xcd_probe_kernel(int32_t* out, int32_t n) {
+  if (threadIdx.x == 0 && (int32_t)blockIdx.x < n)
+    out[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_xcd_probe(int32_t* xcd_out, int32_t n, void* stream) {
+  if (!xcd_out) return PKV_ERR_NULL;
+  if (n < 1 || n > 1024) return PKV_ERR_SHAPE;
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(n), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     xcd_out, n);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

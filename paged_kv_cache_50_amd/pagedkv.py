@@ -120,6 +120,7 @@ _SIGS = {
                                      _i32, ctypes.c_char_p, _sz]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_read": (_i32, [ctypes.POINTER(ctypes.c_float), _i32]),
+    "pkv_xcd_probe": (_i32, [_vp, _i32, _vp]),
     "pkv_pool_create": (_vp, [_i64, _i32, _i32]),
     "pkv_pool_destroy": (None, [_vp]),
     "pkv_pool_num_free": (_i64, [_vp]),
@@ -495,6 +496,15 @@ def timing_read(cap: int = 4096):
     if n < 0:
         raise PagedKVError(7, "timing_read")
     return [buf[i] for i in range(n)]
+
+
+def xcd_probe(n: int = 8):
+    """The XCD (0-7) that each of n one-wave workgroups of one launch on the
+    current stream ran on: where the dispatcher starts a launch."""
+    torch = _torch()
+    out = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    _check(lib().pkv_xcd_probe(_ptr(out), int(n), _stream(out)), "xcd_probe")
+    return out.tolist()
 
 
 def default_scale(head_size: int) -> float:

@@ -261,3 +261,12 @@ def test_noalloc_decode_host_errors(L):
     # sizes the scratch array holds: the headline decode batches
     for S, Hq, Hkv, max_len in ((64, 32, 32, 4096), (256, 32, 8, 8192), (8, 64, 8, 131072)):
         assert pagedkv.workspace_bytes(S, Hq, Hkv, 128, max_len, 512) <= pagedkv.NOALLOC_SCRATCH_BYTES
+
+
+def test_xcd_probe_host_errors(L):
+    f = L.pkv_xcd_probe
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 8, None) == 1
+    assert f(A16, 0, None) == 2
+    assert f(A16, 1025, None) == 2
