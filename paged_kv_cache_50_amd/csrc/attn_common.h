@@ -16,15 +16,24 @@ namespace pkv {
 // column c runs on an XCD of the parity of c + s.  A workgroup streams
 // measurably faster (2-3 % over a whole decode launch) when its XCD's parity
 // differs from that of the 256-byte slot its rows occupy.  With 256-byte rows
-// the slot's parity is the head's, so adjacent heads swap columns: at s = 0
-// every head then runs on an XCD of the other parity.  A fixed permutation of
-// the columns, correct whatever the dispatcher does; a head without a partner
-// keeps its column, and other row sizes (where each slot is shared or split)
-// keep the identity.
+// the slot's parity is the head's, so adjacent heads swap columns; with
+// 128-byte rows (two heads to a slot) the columns of each group of four take
+// heads 2, 0, 3, 1: at s = 0 every head then runs on an XCD of the other
+// parity.  A fixed permutation of the columns, correct whatever the
+// dispatcher does; heads of an incomplete pair or group keep their columns,
+// and other row sizes keep the identity.
 __device__ __forceinline__ int column_head(int col, int num, int row_bytes) {
-  if (row_bytes != 256) return col;
-  const int h = col ^ 1;
-  return h < num ? h : col;
+  if (row_bytes == 256) {
+    const int h = col ^ 1;
+    return h < num ? h : col;
+  }
+  if (row_bytes == 128) {
+    const int base = col & ~3;
+    if (base + 3 >= num) return col;
+    const int r = col & 3;
+    return base + (r == 0 ? 2 : r == 1 ? 0 : r == 2 ? 3 : 1);
+  }
+  return col;
 }
 
 // Resolved work item of one workgroup.
