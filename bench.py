@@ -598,6 +598,7 @@ def main() -> int:
                           "plain_call_us_per_step": round(m["plain_us"], 2) if m["plain_us"] else None,
                           "speedup_over_plain_call": round(m["plain_us"] / (m["ms_per_step"] * 1e3), 2)
                           if m["plain_us"] else None}
+    kept = []              # (workload, partition size, record) for the graph replays
     if args.workload is None:
         per = {}
         for cfg in PER_WORKLOAD:
@@ -611,17 +612,17 @@ def main() -> int:
                 rc["plain_call_us_per_step"] = round(mc["plain_us"], 2)
             per[wc.name] = rc
             print(f"[bench] {wc.name}: {rc['us_per_step']} us/step", file=sys.stderr, flush=True)
+            kept.append((wc, pc, rc))
             if cfg in (1, 2, 3):
                 hosts[cfg] = wc
-            else:
-                del wc
         rec["per_workload"] = per
-    # The headline's step replayed as a HIP graph, last: capturing a graph
-    # moves where the dispatcher starts later launches on this stream.
+    # Each step replayed as a HIP graph, after every timed region: capturing
+    # a graph moves where the dispatcher starts later launches on this stream.
     warm = argparse.Namespace(**{**vars(args), "warmup": 10, "warmup_s": 0.2})
-    rec["graph_replay_us_per_step"] = measure(w, warm, dev, ps, graph=True)["graph_us"]
-    if rec["graph_replay_us_per_step"] is not None:
-        rec["graph_replay_us_per_step"] = round(rec["graph_replay_us_per_step"], 2)
+    for wg, pg, target in [(w, ps, rec)] + kept:
+        g_us = measure(wg, warm, dev, pg, graph=True)["graph_us"]
+        target["graph_replay_us_per_step"] = round(g_us, 2) if g_us is not None else None
+    del kept
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, hosts)
