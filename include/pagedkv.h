@@ -106,7 +106,7 @@ typedef enum {
 typedef struct pkv_kv_cache {
   void*   k_cache;       /* device [num_blocks, block_size, num_kv_heads, head_size] */
   void*   v_cache;       /* device, same shape, dtype and block_stride as k_cache    */
-  int64_t num_blocks;    /* pool size, > 0                                          */
+  int64_t num_blocks;    /* pool size, 1 .. INT32_MAX (block ids are int32)         */
   int32_t block_size;    /* tokens per block: 8, 16, 32, 64 or 128                  */
   int32_t num_kv_heads;  /* > 0                                                     */
   int32_t head_size;     /* 64 or 128                                               */
@@ -205,11 +205,15 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
  *   out, q        device [num_seqs, num_heads, head_size], cache dtype
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs]
- *   max_seq_len   host upper bound of seq_lens (sizes the launch and the split)
+ *   max_seq_len   host upper bound of seq_lens (sizes the launch and the split),
+ *                 at most 2^30 (PKV_ERR_SHAPE above; the same bound holds for
+ *                 the varlen and cascade calls)
  *   scale         logit scale (usually 1/sqrt(head_size)), finite; any sign
  *   window_left   sliding window (vLLM book, ch. 6 "forward()": the window
  *                 symmetrisation): the row at position p = seq_len - 1 sees
- *                 keys p - window_left .. p; -1 = no window.  Key tiles start
+ *                 keys p - window_left .. p; -1 = no window.  A window of
+ *                 max_seq_len - 1 or more excludes no key (any int32 width is
+ *                 taken, as that one).  Key tiles start
  *                 at a multiple of 32 positions, so at most 31 keys before the
  *                 window start are read (and masked out); blocks that hold
  *                 none of those and none of the window are never read.
@@ -277,7 +281,8 @@ pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const pk
  *   window_left   sliding window, -1 = none: a row at absolute position p sees
  *                 keys p - window_left .. p when causal, and
  *                 p - window_left .. p + window_left when not (the causal
- *                 window (w, 0) made symmetric, ch. 6 "forward()")
+ *                 window (w, 0) made symmetric, ch. 6 "forward()"); widths of
+ *                 max_seq_len - 1 or more exclude no key, as for decode
  *   lse_out       optional device float32 [num_tokens, num_heads]
  *   options       optional launch choices and report (pkv_call_options)
  * Over an fp8 cache the prefill kernels fold k_scale into the logit scale,
@@ -369,7 +374,11 @@ const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int3
  * a whole number of blocks, distinct prefix blocks, every sequence with
  * seq_len > 0 starting its table with them and holding the prefix in its
  * context, and its other blocks neither prefix blocks nor another sequence's.
- * Returns PKV_OK or PKV_ERR_METADATA (message as pkv_validate_metadata).
+ * Arrays the caller must supply in full (their lengths are not passed):
+ * block_tables [num_seqs, max_blocks_per_seq], seq_lens [num_seqs],
+ * cu_seqlens_q [num_seqs + 1], prefix_blocks [common_prefix_len / block_size]
+ * (may be NULL when that is 0).  Returns PKV_OK or PKV_ERR_METADATA (message
+ * as pkv_validate_metadata).
  */
 pkv_status pkv_validate_cascade(const int32_t* block_tables, int32_t max_blocks_per_seq,
                                 const int32_t* seq_lens, int32_t num_seqs,
@@ -385,8 +394,9 @@ pkv_status pkv_validate_cascade(const int32_t* block_tables, int32_t max_blocks_
 const char* pkv_unsupported_reason(int32_t dtype, int32_t head_size, int32_t block_size,
                                    int32_t num_heads, int32_t num_kv_heads);
 
-/* Static, human-readable name of a status code. */
-const char* pkv_status_string(pkv_status status);
+/* Static, human-readable name of a status code (a pkv_status value; any
+ * other integer gives "unknown status"). */
+const char* pkv_status_string(int32_t status);
 
 /*
  * Debug check of HOST copies of the metadata (synchronous, no GPU use):
@@ -396,6 +406,10 @@ const char* pkv_status_string(pkv_status status);
  * be NULL for decode) starting at 0, non-decreasing, ending at num_tokens,
  * query lengths <= min(seq_len, max_query_len), and slot_mapping (may be NULL)
  * entries either -1 or inside the pool, with no slot repeated.
+ * Arrays the caller must supply in full (their lengths are not passed, and
+ * the check reads up to these extents): block_tables
+ * [num_seqs, max_blocks_per_seq], seq_lens [num_seqs], cu_seqlens_q
+ * [num_seqs + 1], slot_mapping [num_slots].
  * Returns PKV_OK or PKV_ERR_METADATA; when `msg` is not NULL a description of
  * the first problem (or "") is written there, truncated to msg_len bytes.
  */

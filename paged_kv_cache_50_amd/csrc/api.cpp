@@ -25,6 +25,16 @@ constexpr int32_t kDefaultPartition = 512;
 constexpr int32_t kPartitionQuantum = 32;
 constexpr int64_t kMaxGridZ = 65535;
 constexpr int64_t kMaxGridY = 65535;
+// Longest sequence a call takes: key positions plus a window (clamped below
+// max_seq_len) and a tile then stay inside int32 in every kernel.
+constexpr int32_t kMaxSeqLen = 1 << 30;
+
+// Rows sit at positions below max_seq_len, so a window of max_seq_len - 1
+// keys or more excludes no key: such windows are clamped to that width, which
+// keeps the kernels' position + window sums inside int32.
+int32_t clamp_window(int32_t window_left, int32_t max_seq_len) {
+  return window_left >= max_seq_len ? std::max(0, max_seq_len - 1) : window_left;
+}
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_FP8_E4M3 ? 1 : 2; }
 bool is_fp8(const pkv_kv_cache* c) { return c->dtype == PKV_FP8_E4M3; }
@@ -89,7 +99,9 @@ const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t
 
 pkv_status check_cache(const pkv_kv_cache* c, int32_t num_heads) {
   if (!c || !c->k_cache || !c->v_cache) return PKV_ERR_NULL;
-  if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_size <= 0)
+  // block ids are int32 in block tables and slot arithmetic stays in int64
+  if (c->num_blocks <= 0 || c->num_blocks > INT32_MAX || c->block_size <= 0 ||
+      c->num_kv_heads <= 0 || c->head_size <= 0)
     return PKV_ERR_SHAPE;
   if (reason(c->dtype, c->head_size, c->block_size, num_heads > 0 ? num_heads : c->num_kv_heads,
              c->num_kv_heads))
@@ -103,6 +115,13 @@ pkv_status check_cache(const pkv_kv_cache* c, int32_t num_heads) {
   if (stride > (int64_t)INT32_MAX / elem_bytes(c->dtype)) return PKV_ERR_SHAPE;
   if ((stride * elem_bytes(c->dtype)) % 16 != 0) return PKV_ERR_ALIGN;
   return PKV_OK;
+}
+
+// Product of two non-negative sizes, saturating at INT64_MAX: the launch
+// planners' estimates stay ordered for arguments too large to launch.
+int64_t sat_mul(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
 }
 
 int64_t block_stride_elems(const pkv_kv_cache* c) {
@@ -191,14 +210,14 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // 320 workgroups of 1024 tokens instead of 576 of 512 (1.1 rounds of
     // 512 slots): 42 -> 29 us.  (Searching below the floor as well measured
     // slower on the large batches.)
-    int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, a.window_left + 1)
+    int64_t eff_len = a.window_left >= 0 ? std::min<int64_t>(a.max_seq_len, (int64_t)a.window_left + 1)
                                          : a.max_seq_len;
     eff_len = std::max<int64_t>(1, std::min<int64_t>(eff_len, a.max_seq_len - a.kv_start));
     const int64_t streams =
-        (int64_t)a.num_seqs * cache->num_kv_heads * a.head_chunks / a.heads_per_wave;
+        sat_mul((int64_t)a.num_seqs * cache->num_kv_heads, a.head_chunks) / a.heads_per_wave;
     const int tpw_max = kMfmaTokensPerWg;
     int tpw = tpw_max;
-    while (tpw > 256 && streams * eff_len / tpw < kMfmaTargetWgs) tpw >>= 1;
+    while (tpw > 256 && sat_mul(streams, eff_len) / tpw < kMfmaTargetWgs) tpw >>= 1;
     if (a.partition_size > 0) {
       const int P = a.partition_size;
       const int64_t span = eff_len + 31;             // the range starts at a multiple of 32
@@ -209,9 +228,9 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
       const int floor_tpw = tpw;
       for (int cand = tpw_max; cand >= floor_tpw; cand >>= 1) {
         const int ppw = (P <= cand / 4) ? 4 : std::max(1, cand / P);
-        const int64_t wgs = streams * ((nparts + ppw - 1) / ppw);
+        const int64_t wgs = sat_mul(streams, (nparts + ppw - 1) / ppw);
         const int64_t tok = std::min<int64_t>((int64_t)ppw * P, span);
-        const int64_t est = (wgs + slots - 1) / slots * (tok + kWgFixedTokens);
+        const int64_t est = sat_mul(wgs / slots + (wgs % slots != 0), tok + kWgFixedTokens);
         if (best < 0 || est < best) {
           best = est;
           tpw = cand;
@@ -441,13 +460,14 @@ PrefixGeometry prefix_geometry(int32_t num_tokens, int32_t num_heads, int32_t nu
   while (group % gc) gc >>= 1;
   g.gc = gc;
   const int rows_per_wg = 16 * (8 / gc);
-  g.qtiles = (unsigned)((num_tokens + rows_per_wg - 1) / rows_per_wg);
+  g.qtiles = (unsigned)(((int64_t)num_tokens + rows_per_wg - 1) / rows_per_wg);
   g.gy = (unsigned)(num_kv_heads * (group / gc));
   const int64_t base = (int64_t)g.qtiles * g.gy;
-  const int64_t most = std::min<int64_t>(kMaxPrefixParts, (cpl + kPrefixMinPart - 1) / kPrefixMinPart);
+  const int64_t most =
+      std::min<int64_t>(kMaxPrefixParts, ((int64_t)cpl + kPrefixMinPart - 1) / kPrefixMinPart);
   const int64_t want = std::max<int64_t>(1, std::min<int64_t>(most, (target_wgs + base - 1) / base));
   g.P = (int32_t)((((cpl + want - 1) / want) + 31) / 32 * 32);
-  g.parts = (cpl + g.P - 1) / g.P;
+  g.parts = (int32_t)(((int64_t)cpl + g.P - 1) / g.P);
   return g;
 }
 
@@ -468,7 +488,7 @@ CascadeLayout cascade_layout(const PrefixGeometry& g, int32_t num_seqs, int32_t 
   l.pre_lse = rows * head_size * sizeof(float);
   l.suf_lse = align16(l.pre_lse + rows * sizeof(float));
   l.plan = align16(l.suf_lse + (size_t)num_tokens * num_heads * sizeof(float));
-  l.varlen = align16(l.plan + (size_t)(num_seqs + 2) * sizeof(int32_t));
+  l.varlen = align16(l.plan + ((size_t)num_seqs + 2) * sizeof(int32_t));
   l.total = l.varlen + varlen_bytes;
   return l;
 }
@@ -488,7 +508,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   if (st != PKV_OK) return st;
   if (window_left < -1) return PKV_ERR_SHAPE;
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
-      max_query_len < 0 || max_blocks_per_seq <= 0)
+      max_seq_len > kMaxSeqLen || max_query_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
@@ -515,7 +535,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
                          num_tokens, num_heads, max_seq_len, std::max(max_query_len, 1), scale, P,
                          ns, lse_out, workspace);
   a.cu_seqlens_q = cu_seqlens_q;
-  a.window_left = window_left;
+  a.window_left = clamp_window(window_left, max_seq_len);
   a.causal = causal ? 1 : 0;
   a.kv_start = kv_start;
   const int group = num_heads / cache->num_kv_heads;
@@ -580,7 +600,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
       while (group % gc) gc >>= 1;
       r.head_chunks_gc = gc;
       const int rows_per_wg = 16 * (8 / gc);
-      const unsigned qtiles = (unsigned)((max_query_len + rows_per_wg - 1) / rows_per_wg);
+      const unsigned qtiles = (unsigned)(((int64_t)max_query_len + rows_per_wg - 1) / rows_per_wg);
       const unsigned gy = (unsigned)(cache->num_kv_heads * (group / gc));
       for (int64_t z0 = 0; z0 < num_seqs && st == PKV_OK; z0 += kMaxGridZ) {
         r.z_base = (int32_t)z0;
@@ -626,7 +646,8 @@ pkv_status decode_host_checks(const void* out, const void* q, const pkv_kv_cache
   st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
   if (window_left < -1) return PKV_ERR_SHAPE;
-  if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_blocks_per_seq <= 0)
+  if (num_seqs < 0 || num_heads <= 0 || max_seq_len < 0 || max_seq_len > kMaxSeqLen ||
+      max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;
@@ -650,7 +671,9 @@ const char* pkv_unsupported_reason(int32_t dtype, int32_t head_size, int32_t blo
   return reason(dtype, head_size, block_size, num_heads, num_kv_heads);
 }
 
-const char* pkv_status_string(pkv_status s) {
+const char* pkv_status_string(int32_t s) {
+  // an int, not the enum: C callers may pass any code, and C++ gives a value
+  // outside the enum's range no defined meaning
   switch (s) {
     case PKV_OK: return "ok";
     case PKV_ERR_NULL: return "a required pointer is NULL";
@@ -690,7 +713,7 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
   const int32_t ns = num_splits_for(max_seq_len, P);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)ns * num_heads * num_seqs;
-  return order_offset(rows, head_size) + align16((size_t)(2 * num_seqs + 3) * sizeof(int32_t));
+  return order_offset(rows, head_size) + align16((2 * (size_t)num_seqs + 3) * sizeof(int32_t));
 }
 
 pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
@@ -751,7 +774,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   AttnArgs a = base_args(out, q, cache, block_tables, max_blocks_per_seq, seq_lens, num_seqs,
                          num_seqs, num_heads, max_seq_len, 1, scale, P, ns, lse_out, workspace);
   a.mode = pkv::kModeDecode;
-  a.window_left = window_left;
+  a.window_left = clamp_window(window_left, max_seq_len);
   st = plan_seq_order(a, cache, workspace, s, ch);
   if (st != PKV_OK) return st;
   int tslot = 0;
@@ -842,7 +865,7 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   st = check_cache(cache, num_heads);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_seq_len < 0 ||
-      max_query_len < 0 || max_blocks_per_seq <= 0)
+      max_seq_len > kMaxSeqLen || max_query_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
     return PKV_ERR_UNSUPPORTED;

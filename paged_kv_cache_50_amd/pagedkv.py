@@ -449,6 +449,17 @@ def validate_cascade(block_tables, seq_lens, cu_seqlens_q, prefix_blocks, common
         return np.ascontiguousarray(x, dtype=np.int32)
 
     bt, sl, cu, pb = arr(block_tables), arr(seq_lens), arr(cu_seqlens_q), arr(prefix_blocks)
+    S = sl.shape[0]
+    # the library reads these arrays to the extents the sizes imply: refuse
+    # short ones here rather than let it read past them
+    if bt.ndim != 2 or bt.shape[0] < S:
+        raise ValueError(f"block_tables must be 2-D with at least {S} rows")
+    if cu.ndim != 1 or cu.shape[0] < S + 1:
+        raise ValueError(f"cu_seqlens_q must hold at least num_seqs + 1 = {S + 1} entries")
+    bs, cpl = int(block_size), int(common_prefix_len)
+    need = cpl // bs if bs > 0 and cpl >= 0 and cpl % bs == 0 else 0
+    if pb.size < need:
+        raise ValueError(f"prefix_blocks holds {pb.size} entries, the prefix needs {need}")
     msg = ctypes.create_string_buffer(256)
     st = lib().pkv_validate_cascade(bt.ctypes.data, bt.shape[1], sl.ctypes.data, sl.shape[0],
                                     cu.ctypes.data, pb.ctypes.data if pb.size else None,
@@ -473,6 +484,11 @@ def validate_metadata(block_tables, seq_lens, max_seq_len, num_blocks, block_siz
     sl = arr(seq_lens, np.int32)
     cu = arr(cu_seqlens_q, np.int32)
     sm = arr(slot_mapping, np.int64)
+    S = sl.shape[0]
+    if bt.ndim != 2 or bt.shape[0] < S:
+        raise ValueError(f"block_tables must be 2-D with at least {S} rows")
+    if cu is not None and (cu.ndim != 1 or cu.shape[0] < S + 1):
+        raise ValueError(f"cu_seqlens_q must hold at least num_seqs + 1 = {S + 1} entries")
     msg = ctypes.create_string_buffer(256)
     st = lib().pkv_validate_metadata(
         bt.ctypes.data, bt.shape[1], sl.ctypes.data, sl.shape[0],

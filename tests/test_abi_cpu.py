@@ -64,7 +64,8 @@ def test_unsupported_reason(L):
 def test_status_strings(L):
     for s in range(8):
         assert pagedkv.status_string(s)
-    assert pagedkv.status_string(99) == "unknown status"
+    for code in (99, -1, 2**31 - 1, -2**31):
+        assert pagedkv.status_string(code) == "unknown status"
 
 
 def test_partition_choice_and_workspace(L):
@@ -122,6 +123,8 @@ def test_decode_error_codes(L):
     assert decode(L, cache(dtype=0, stride=1 << 29)) == 2        # 2 GiB of fp32
     assert decode(L, cache(), ps=100) == 2                       # partition not a multiple of 32
     assert decode(L, cache(), win=-2) == 2                       # window below -1
+    assert decode(L, cache(), max_len=(1 << 30) + 1) == 2         # past the 2^30 bound
+    assert decode(L, cache(nb=(1 << 31))) == 2                   # block ids are int32
     need = pagedkv.workspace_bytes(4, 32, 8, 128, 1000, 0)
     assert need > 0
     assert decode(L, cache(), ws=None, wsb=0) == 5               # split needs a workspace
@@ -145,6 +148,8 @@ def test_varlen_and_write_error_codes(L):
                  None, None, 0, None, None) == 2
     assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, 5, 1000, float("nan"), 1,
              -1, 0, None, None, 0, None, None) == 2
+    assert f(A16, A16, ctypes.byref(c), A16, A16, A16, 64, 4, 10, 32, 5, (1 << 30) + 1, 0.1, 1,
+             -1, 0, None, None, 0, None, None) == 2                    # past the 2^30 bound
     w = L.pkv_kv_cache_write
     assert w(ctypes.byref(c), None, A16, A16, 10, None) == 1
     assert w(ctypes.byref(c), A_ODD, A16, A16, 10, None) == 4
@@ -270,3 +275,20 @@ def test_xcd_probe_host_errors(L):
     assert f(None, 8, None) == 1
     assert f(A16, 0, None) == 2
     assert f(A16, 1025, None) == 2
+
+
+def test_validate_metadata_refuses_short_arrays(L):
+    """The library reads the host arrays to the extents the sizes imply; the
+    binding refuses shorter ones before the call instead of letting it read
+    past their end."""
+    w = W.make_config(5, num_seqs=5, max_len=300, num_chunks=2, chunk_len=30)
+    base = dict(block_tables=w.block_tables, seq_lens=w.seq_lens, max_seq_len=w.max_seq_len,
+                num_blocks=w.num_blocks, block_size=w.block_size, cu_seqlens_q=w.cu_seqlens_q,
+                num_tokens=w.num_q_rows, max_query_len=w.max_query_len)
+    with pytest.raises(ValueError, match="block_tables"):
+        pagedkv.validate_metadata(**{**base, "block_tables": w.block_tables[:4]})
+    with pytest.raises(ValueError, match="block_tables"):
+        pagedkv.validate_metadata(**{**base, "block_tables": w.block_tables[0]})
+    with pytest.raises(ValueError, match="cu_seqlens_q"):
+        pagedkv.validate_metadata(**{**base, "cu_seqlens_q": w.cu_seqlens_q[:5]})
+    assert pagedkv.validate_metadata(**base) == ""

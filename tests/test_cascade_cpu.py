@@ -24,6 +24,7 @@ def test_cascade_error_codes(L):
     assert cascade(L, cache(), cpl=4095) == 2                   # not a whole number of blocks
     assert cascade(L, cache(), cpl=-16) == 2
     assert cascade(L, cache(), cpl=6000) == 2                   # longer than max_seq_len
+    assert cascade(L, cache(), max_len=(1 << 30) + 1) == 2      # past the 2^30 bound
     assert cascade(L, cache(), mb=100) == 2                     # longer than the tables
     assert cascade(L, cache(), pre=None) == 1                   # NULL prefix blocks
     assert cascade(L, cache(), cu=None) == 1
@@ -132,3 +133,24 @@ def test_cascade_traffic_saving_of_workload_9():
                                         w.head_size, e)
     plain = int(w.seq_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * e
     assert math.isclose(plain - casc, 31 * w.common_prefix_len * 2 * 8 * 128 * 2)
+
+
+def test_validate_cascade_refuses_short_arrays(L):
+    """prefix_blocks shorter than common_prefix_len / block_size, a short
+    cu_seqlens_q or too few block-table rows are refused by the binding
+    before the library would read past them."""
+    w = W.make_config(9, num_seqs=6, max_len=300)
+    nb = w.common_prefix_len // w.block_size
+    args = dict(block_tables=w.block_tables, seq_lens=w.seq_lens, cu_seqlens_q=w.cu_seqlens_q,
+                prefix_blocks=w.prefix_blocks, common_prefix_len=w.common_prefix_len,
+                block_size=w.block_size)
+    with pytest.raises(ValueError, match="prefix_blocks"):
+        pagedkv.validate_cascade(**{**args, "prefix_blocks": w.prefix_blocks[:nb - 1]})
+    with pytest.raises(ValueError, match="cu_seqlens_q"):
+        pagedkv.validate_cascade(**{**args, "cu_seqlens_q": w.cu_seqlens_q[:6]})
+    with pytest.raises(ValueError, match="block_tables"):
+        pagedkv.validate_cascade(**{**args, "block_tables": w.block_tables[:5]})
+    # an invalid prefix length is the library's to report, whatever the array
+    assert "whole number" in pagedkv.validate_cascade(**{**args, "prefix_blocks": [],
+                                                         "common_prefix_len": 100})
+    assert pagedkv.validate_cascade(**args) == ""

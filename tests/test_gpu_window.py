@@ -1,7 +1,8 @@
 """GPU parity of sliding-window attention: decode (VALU, matrix-core and fp8
 kernels, split or not), chunked prefill (causal and symmetric), the mixed
 one-launch step, exact window edges (a dominant key just inside counts, one
-just outside does not) and a wide window equal to none."""
+just outside does not) and wide windows, up to the largest int32 width,
+equal to none."""
 import numpy as np
 import pytest
 
@@ -135,19 +136,29 @@ def test_window_edges_exact(hq, hkv, ps):
     assert not np.allclose(G.dev_to_f64(dw.out), outside_v, atol=1e-3)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_wide_window_equals_none(cfg):
+@pytest.mark.parametrize("cfg", [2, 3, 5, "5nc"])
+@pytest.mark.parametrize("wide", ["max_seq_len-1", "max_seq_len+5", "int32_max"])
+def test_wide_window_equals_none(cfg, wide):
+    """A window of max_seq_len - 1 keys or more excludes no key: the output
+    equals the call without a window bit for bit, up to the largest int32
+    width (where a position + window sum would leave int32 unless clamped),
+    for decode, causal chunked prefill and symmetric (non-causal) rows."""
     torch = G.torch()
-    if cfg == 5:
+    if cfg in (5, "5nc"):
         w = W.make_config(5, num_seqs=8, max_len=900, num_chunks=2, chunk_len=70)
+        w.causal = cfg == 5
     else:
         w = W.make_config(cfg, num_seqs=8, max_len=2000)
+    win = {"max_seq_len-1": int(w.max_seq_len) - 1, "max_seq_len+5": int(w.max_seq_len) + 5,
+           "int32_max": 2**31 - 1}[wide]
+    _announce(f"wide window cfg={cfg} window={win}")
     dw = G.DevWorkload(w)
     _run(dw, 0, -1)
     torch.cuda.synchronize()
     a = G.dev_to_bits(dw.out).copy()
-    _run(dw, 0, int(w.max_seq_len) + 5)
+    ref, _ = _reference(w, -1)
+    G.assert_close(G.dev_to_f64(dw.out), ref, w.dtype, f"no window cfg={cfg}")
+    _run(dw, 0, win)
     torch.cuda.synchronize()
+    G.assert_close(G.dev_to_f64(dw.out), _reference(w, win)[0], w.dtype, f"window {win} cfg={cfg}")
     assert np.array_equal(G.dev_to_bits(dw.out), a)
-
-
