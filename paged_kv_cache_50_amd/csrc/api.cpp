@@ -294,6 +294,12 @@ pkv_status launch_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_
 
 size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
 
+// Workspace sizes are products of int32 arguments that can pass 2^64 for
+// sizes no launch could take; they are formed in 128 bits and such sizes
+// reported as (size_t)-1 rather than wrapped to a small number.
+using u128 = unsigned __int128;
+constexpr u128 kMaxWorkspace = (u128)1 << 62;
+
 // Split workspace: partial outputs [rows, head_size] fp32, their lse [rows]
 // fp32, then the sequence dispatch order int32 [num_seqs] (16-byte aligned).
 size_t order_offset(size_t rows, int32_t head_size) {
@@ -527,6 +533,7 @@ pkv_status varlen_impl(void* out, const void* q, const pkv_kv_cache* cache,
   if (ns > 1) {
     const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
                                                       cache->head_size, span, P);
+    if (need == (size_t)-1) return PKV_ERR_SHAPE;
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGN;
   }
@@ -712,8 +719,11 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
   if (P < 0) return (size_t)-1;
   const int32_t ns = num_splits_for(max_seq_len, P);
   if (ns <= 1) return 0;
-  const size_t rows = (size_t)ns * num_heads * num_seqs;
-  return order_offset(rows, head_size) + align16((2 * (size_t)num_seqs + 3) * sizeof(int32_t));
+  const u128 rows = (u128)ns * (u128)num_heads * (u128)num_seqs;
+  if (rows * ((u128)head_size + 1) * sizeof(float) + 4 * (u128)num_seqs > kMaxWorkspace)
+    return (size_t)-1;
+  return order_offset((size_t)rows, head_size) +
+         align16((2 * (size_t)num_seqs + 3) * sizeof(int32_t));
 }
 
 pkv_status pkv_kv_cache_write(const pkv_kv_cache* cache, const void* key, const void* value,
@@ -767,6 +777,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const pkv_kv_cac
   if (ns > 1) {
     const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, cache->num_kv_heads,
                                                       cache->head_size, max_seq_len, P);
+    if (need == (size_t)-1) return PKV_ERR_SHAPE;
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PKV_ERR_ALIGN;
   }
@@ -817,6 +828,10 @@ size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t
   if (vw == (size_t)-1) return vw;
   if (common_prefix_len == 0) return vw;
   const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, num_kv_heads, common_prefix_len);
+  // prefix partials, their lse, the suffix lse and the plan, bounded first
+  const u128 rows = (u128)g.parts * (u128)num_heads * (u128)num_tokens;
+  if (rows * ((u128)head_size + 2) * sizeof(float) + 4 * (u128)num_seqs + vw > kMaxWorkspace)
+    return (size_t)-1;
   return cascade_layout(g, num_seqs, num_tokens, num_heads, head_size, vw).total;
 }
 
@@ -892,6 +907,10 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   if (vw == (size_t)-1) return PKV_ERR_SHAPE;
   const PrefixGeometry g = prefix_geometry(num_tokens, num_heads, cache->num_kv_heads, cpl);
   if (g.parts < 1 || g.parts > kMaxPrefixParts || g.qtiles > (unsigned)INT32_MAX) return PKV_ERR_SHAPE;
+  if (pkv_cascade_workspace_bytes(num_seqs, num_tokens, num_heads, cache->num_kv_heads,
+                                  cache->head_size, max_seq_len, cpl, partition_size) ==
+      (size_t)-1)
+    return PKV_ERR_SHAPE;
   const CascadeLayout lay = cascade_layout(g, num_seqs, num_tokens, num_heads, cache->head_size, vw);
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_ALIGN;

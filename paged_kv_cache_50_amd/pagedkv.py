@@ -201,9 +201,17 @@ def _io_dtype(k_cache):
 
 
 def _require_gpu(*ts):
+    """Every given tensor on the GPU, and all on the same one."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("tensors must live on the GPU (no CPU fallback)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different GPUs ({dev} and {t.device})")
 
 
 def _ptr(t) -> Optional[int]:
@@ -250,7 +258,7 @@ def kv_cache_write(k_cache, v_cache, key, value, slot_mapping, k_scale=None, v_s
     (int64 [T], -1 = skip).  In place, asynchronous on the current stream.
     fp8 caches take bfloat16 rows and quantise them with k_scale / v_scale."""
     torch = _torch()
-    _require_gpu(key, value, slot_mapping)
+    _require_gpu(key, value, slot_mapping, k_cache)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous():
         raise TypeError("slot_mapping must be a contiguous int64 tensor")
@@ -266,7 +274,12 @@ def kv_cache_write(k_cache, v_cache, key, value, slot_mapping, k_scale=None, v_s
 
 
 def _workspace(ws, need: int, device):
+    """The workspace and its size in bytes (allocated here when not given).
+    A given one must be contiguous on the device of q: the library takes
+    numel * element_size bytes from its first element on."""
     torch = _torch()
+    if ws is not None and (not ws.is_contiguous() or ws.device != device):
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
     if need == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
@@ -295,7 +308,7 @@ def _byref(options):
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, lse_out, k_scale, v_scale):
-    _require_gpu(out, q, block_tables, seq_lens, lse_out)
+    _require_gpu(out, q, block_tables, seq_lens, lse_out, k_cache)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     _meta(block_tables, "block_tables")
     _meta(seq_lens, "seq_lens")
@@ -358,7 +371,7 @@ def paged_attention_varlen(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, blo
     """Variable-length attention over a flattened batch (q/out [T, Hq, D]).
     window_left >= 0: sliding window (symmetric when not causal).  options
     as for paged_attention_decode."""
-    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out)
+    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, workspace, lse_out, k_cache)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
         _meta(t, n)
@@ -409,7 +422,8 @@ def cascade_attention(out, q, k_cache, v_cache, cu_seqlens_q, seq_lens, block_ta
     with the prefix blocks (int32 [common_prefix_len / block_size], shared
     by every sequence's table) read once for the whole batch.  fp8 caches
     take k_scale / v_scale as in paged_attention_varlen."""
-    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, prefix_blocks, workspace, lse_out)
+    _require_gpu(out, q, cu_seqlens_q, seq_lens, block_tables, prefix_blocks, workspace, lse_out,
+                 k_cache)
     desc = cache_descriptor(k_cache, v_cache, k_scale, v_scale)
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"),
                  (block_tables, "block_tables"), (prefix_blocks, "prefix_blocks")):

@@ -86,6 +86,16 @@ def test_partition_choice_and_workspace(L):
     assert pagedkv.workspace_bytes(8, 64, 8, 128, 500, 512) == 0
     with pytest.raises(pagedkv.PagedKVError):
         pagedkv.workspace_bytes(8, 64, 8, 128, 1000, 100)
+    # sizes whose workspace passes 2^62 bytes are refused, not wrapped to a
+    # small number (2^25 splits x 2^31 heads x 2^31 sequences rows)
+    big = 2**31 - 1
+    with pytest.raises(pagedkv.PagedKVError):
+        pagedkv.workspace_bytes(big, big, 1, 128, 1 << 30, 32)
+    with pytest.raises(pagedkv.PagedKVError):
+        pagedkv.cascade_workspace_bytes(big, big, big, 1, 128, 1 << 30, 1 << 29, 32)
+    # the largest that fit stay exact
+    assert pagedkv.workspace_bytes(1 << 16, 64, 8, 128, 1 << 20, 512) == \
+        a16(2048 * 64 * (1 << 16) * 129 * 4) + a16((2 * (1 << 16) + 3) * 4)
 
 
 # Fake, never-dereferenced device addresses: every call below fails host

@@ -132,3 +132,40 @@ def test_report_is_per_call():
     o.decode_kernel = 0
     with pytest.raises(pagedkv.PagedKVError):
         G.run(dw, partition_size=-1, options=P.CallOptions(decode_kernel=3))
+
+
+def test_binding_refuses_bad_buffers():
+    """The binding refuses, before any launch, buffers the kernels would
+    write or read past: an overlapping (expanded) workspace that claims more
+    bytes than it spans, a workspace too small for the split, an lse_out in
+    another dtype, and prefix_blocks shorter than the shared prefix; the
+    call with proper buffers still matches the oracle afterwards."""
+    torch = G.torch()
+    w = W.make_config(3, num_seqs=6, max_len=1500)
+    dw = G.DevWorkload(w)
+    need = P.workspace_bytes(6, 32, 8, 128, int(w.max_seq_len), 512)
+    assert need > 0
+    args = (dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.seq_lens, w.scale,
+            int(w.max_seq_len))
+    over = torch.empty(1, dtype=torch.uint8, device="cuda").expand(need)
+    with pytest.raises(ValueError, match="workspace"):
+        P.paged_attention_decode(*args, partition_size=512, workspace=over)
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(P.PagedKVError):
+        P.paged_attention_decode(*args, partition_size=512, workspace=small)
+    bad_lse = torch.empty(6, 32, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="lse_out"):
+        P.paged_attention_decode(*args, partition_size=512, lse_out=bad_lse)
+    c = W.make_config(9, num_seqs=8, max_len=600)
+    dc = G.DevWorkload(c)
+    nb = c.common_prefix_len // c.block_size
+    short = torch.from_numpy(c.prefix_blocks[:nb - 1].copy()).cuda()
+    with pytest.raises(ValueError, match="prefix_blocks"):
+        P.cascade_attention(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.cu_seqlens_q, dc.seq_lens,
+                            dc.block_tables, short, c.common_prefix_len, c.scale,
+                            c.max_query_len, int(c.max_seq_len))
+    torch.cuda.synchronize()
+    G.run(dw, partition_size=512)
+    ref, ref_lse = G.reference(w)
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "bf16",
+                      "after refusals", w=w)
