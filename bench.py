@@ -242,7 +242,7 @@ def measure(w, args, dev, ps, cpu_label=False, graph=False) -> dict:
                 caches.append((dw.k_cache.clone(), dw.v_cache.clone()))
         else:
             cache_resident = True
-    opts = pagedkv.CallOptions()
+    opts = pagedkv.CallOptions(**getattr(args, "call_options", {}))
     it = [0]
 
     def step(plain=False):
@@ -511,10 +511,21 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--call-option", action="append", default=[], metavar="FIELD=VALUE",
+                    help="set a pkv_call_options field for the measured calls (e.g. "
+                         "mixed_launch=1: prefill chunks and decode rows in separate launches); "
+                         "repeatable; the JSON line records them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) to calibrate "
                          "HBM byte counters, then exit")
     args = ap.parse_args()
+    args.call_options = {}
+    fields = {"decode_kernel", "prefill_kernel", "fp8_head_pairs", "mixed_launch", "cascade_launch"}
+    for item in args.call_option:
+        name, _, value = item.partition("=")
+        if name not in fields or not value.lstrip("-").isdigit():
+            ap.error(f"--call-option takes FIELD=INT with FIELD one of {sorted(fields)}")
+        args.call_options[name] = int(value)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: runs on exactly one GPU; --gpus N > 1 is not supported (the "
@@ -587,6 +598,7 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "kernels_launched": r["kernels_launched"],
         "warmup_steps_run": r["warmup_steps_run"],
+        **({"call_options": args.call_options} if args.call_options else {}),
         "roofline": r["roofline"],
     }
     for k in ("cache_resident", "cache_copies_rotated"):
