@@ -2,7 +2,9 @@
 (fp32, bf16, fp8; and a sweep of its own over binary16), head size, block size, kv heads and GQA group, decode
 batches and varlen batches mixing decode rows, prefill chunks and empty
 sequences, causal or not, sliding windows, partition sizes, and a forced
-kernel variant through the call's options.  Every case is reproducible from
+kernel variant through the call's options; cascades; and a crossed sweep
+in which every dtype, block sizes up to 128 and all five launch options,
+each set or not on its own, meet in one draw.  Every case is reproducible from
 its index (the seed), and the combinations are drawn, not hand-picked, so
 that they reach pairings the targeted tests do not name."""
 import numpy as np
@@ -147,3 +149,57 @@ def test_random_f16_cascade_matches_oracle(i):
     G.run_cascade(dw, partition_size=ps, options=pagedkv.CallOptions(**opts))
     ref, ref_lse = G.reference(w)
     G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, "f16", desc, w=w)
+
+
+N_COMBO = 256
+
+
+def draw_combo(i: int, base=110_000):
+    """Case i of the crossed sweep: every cache dtype and block size (8 to
+    128), decode or varlen rows, windows and partition sizes, and each of
+    the five launch options set or not independently of the others (an
+    option that does not apply to the case, such as head pairs over a
+    16-bit cache, must leave the result unchanged)."""
+    rng = np.random.default_rng(base + i)
+    dtype = str(rng.choice(["f32", "bf16", "f16", "fp8"]))
+    head = 128 if dtype == "fp8" else int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32, 64, 128]))
+    hkv = int(rng.choice([1, 2, 3, 8]))
+    group = int(rng.choice([1, 3, 4, 8, 20]))
+    S = int(rng.integers(1, 11))
+    if rng.random() < 0.35:
+        L = rng.integers(0, 2500, S)
+        L[rng.random(S) < 0.15] = 0
+        w = W.make_decode(f"combo{i}", L, hkv * group, hkv, head, bs, dtype, seed=2 * base + i)
+    else:
+        ctx = rng.integers(0, 2000, S)
+        ql = np.where(rng.random(S) < 0.5, 1, rng.integers(2, 200, S))
+        empty = rng.random(S) < 0.1
+        ql[empty] = 0
+        ctx[empty] = 0
+        w = W.make_varlen(f"combo{i}", ctx, ql, hkv * group, hkv, head, bs, dtype,
+                          seed=2 * base + i, causal=bool(rng.random() < 0.7))
+    if rng.random() < 0.3:
+        w.window_left = int(rng.integers(0, 900))
+    ps = int(rng.choice([0, -1, 32, 128, 512]))
+    opts = {"decode_kernel": int(rng.integers(0, 3)), "prefill_kernel": int(rng.integers(0, 2)),
+            "fp8_head_pairs": int(rng.integers(0, 2)), "mixed_launch": int(rng.integers(0, 2)),
+            "cascade_launch": int(rng.integers(0, 2))}
+    desc = (f"combo {i}: {dtype} D{head} bs{bs} {hkv * group}/{hkv} heads, {S} seqs, "
+            f"{'decode' if w.cu_seqlens_q is None else ('varlen causal' if w.causal else 'varlen')}, "
+            f"window {w.window_left}, ps {ps}, options {opts}")
+    return w, ps, opts, desc
+
+
+@pytest.mark.parametrize("i", range(N_COMBO))
+def test_random_combined_options_match_oracle(i):
+    w, ps, opts, desc = draw_combo(i)
+    print(f"[gpu-test] {desc}", flush=True)
+    dw = G.DevWorkload(w)
+    o = pagedkv.CallOptions(**opts)
+    G.run(dw, partition_size=ps, options=o)
+    assert o.launched, desc
+    ref, ref_lse = G.reference(w)
+    tol = {"f32": "f32", "f16": "f16"}.get(w.dtype, "bf16")
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, tol, desc,
+                      w=w if tol == "f16" else None)
