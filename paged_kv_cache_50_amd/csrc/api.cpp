@@ -192,9 +192,10 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
     // e4m3 caches: a kv head's token row is 128 bytes, and whole 256-byte
     // rows gather faster (a microbenchmark of the two patterns: +7-9 %), so
     // each wave reads the rows of two adjacent kv heads when there is an
-    // even number of them and a single head chunk.  Measured: MHA decode at
-    // C2 shapes 200 -> 190 us; GQA decode at C3 shapes unchanged (twice the
-    // LDS per workgroup: two workgroups per CU instead of three).  Only for
+    // even number of them and a single head chunk.  Measured: MHA decode of
+    // 64 sequences x 32 heads 200 -> 190 us; GQA decode of 256 sequences
+    // (32 / 8 heads) unchanged (twice the LDS per workgroup: two workgroups
+    // per CU instead of three).  Only for
     // the decode kernel's own launch (the one-launch forms keep one head),
     // and a call's options may keep one head per wave (A/B runs).
     a.heads_per_wave = (two_heads_ok && is_fp8(cache) && a.head_chunks == 1 &&
@@ -323,7 +324,8 @@ pkv_status plan_seq_order(AttnArgs& a, const pkv_kv_cache* cache, void* workspac
   if (a.num_splits <= 1 || !use_mfma_decode(cache, a.num_heads / cache->num_kv_heads, ch))
     return PKV_OK;
   // with few sequences the planner's launch costs more than the order saves
-  // (C4's 8 sequences: the same step time; with a 4096-key window: 47 -> 42 us)
+  // (8 sequences of 32k-131k tokens: the same step time; with a 4096-key
+  // window: 47 -> 42 us)
   if (!multi && a.num_seqs < kPlanMinSeqs) return PKV_OK;
   int32_t* order = order_area(a, cache, workspace);
   ch.ran |= PKV_RAN_PLANNER;
@@ -351,8 +353,9 @@ int32_t device_cus() {
 // tiles: 2 over a bfloat16 cache, 3 over an fp8 one (of 1-4 tried, with
 // roles per XCD or inside each XCD).  Over an fp8 cache the prefill tiles
 // also convert their codes and the decode rows move half the bytes, so more
-// of the chip starts on prefill (C5's batch over an fp8 cache: 250 us, against
-// 262 us in two launches and 285 us with 2 XCDs in four).
+// of the chip starts on prefill (4 chunks of 512 rows beside 128 decode rows,
+// over an fp8 cache: 250 us, against 262 us in two launches and 285 us with
+// 2 XCDs in four).
 constexpr int32_t kMixedShare = 2;
 constexpr int32_t kMixedShareFp8 = 3;
 

@@ -20,8 +20,8 @@ Conventions (taken from the vLLM pages):
 Random recipe (all integer draws inclusive):
   root = SeedSequence(seed); one metadata stream drawn from root draws the
   lengths and then the block permutation; spawned child streams draw q and,
-  per sequence, that sequence's K then V values; C5 uses one more child for
-  the new tokens' K, V and q. Values are standard_normal(float32) * sigma,
+  per sequence, that sequence's K then V values; the mixed chunked-prefill
+  workloads use one more child for the new tokens' K, V and q. Values are standard_normal(float32) * sigma,
   rounded to bfloat16 (bf16 workloads) or IEEE binary16 (f16 workloads) by
   round-to-nearest-even.
 Every cache slot that holds no valid token (block 0, spare pool blocks, the
