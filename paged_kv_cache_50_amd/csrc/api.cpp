@@ -178,9 +178,6 @@ pkv_status launch_valu_z_chunks(AttnArgs a, int dtype, int head_size, int block_
   return PKV_OK;
 }
 
-// One-row attention (decode, or the one-row sequences of a varlen batch):
-// picks the kernel, the head chunking and the partitions per workgroup (left
-// in `a` for the split merge that follows), launches over all z.
 // Matrix-core decode launch geometry for gy partitions: sets head chunks,
 // partitions per workgroup and the range order in `a`; returns (gx, ranges).
 int32_t device_cus();
@@ -259,6 +256,9 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
   }
 }
 
+// One-row attention (decode, or the one-row sequences of a varlen batch):
+// picks the kernel, the head chunking and the partitions per workgroup (left
+// in `a` for the split merge that follows), launches over all z.
 pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, int64_t z_total,
                           hipStream_t st, Choice& ch) {
   const int group = a.num_heads / cache->num_kv_heads;
