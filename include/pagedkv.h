@@ -109,7 +109,10 @@ typedef struct pkv_kv_cache {
   int64_t num_blocks;    /* pool size, 1 .. INT32_MAX (block ids are int32)         */
   int32_t block_size;    /* tokens per block: 8, 16, 32, 64 or 128                  */
   int32_t num_kv_heads;  /* > 0                                                     */
-  int32_t head_size;     /* 64 or 128                                               */
+  int32_t head_size;     /* 64, 128 or 256 (256: float32, bfloat16 and binary16
+                            caches, on the VALU kernels; the capability matrix
+                            of ch. 6 "Matrice de capacités : les champs comme
+                            contrat" lists a backend of head size 256)          */
   int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value, which
                             are bfloat16 for PKV_FP8_E4M3)                          */
   int64_t block_stride;  /* elements between consecutive blocks; 0 = dense; the

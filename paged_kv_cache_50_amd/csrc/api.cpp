@@ -87,7 +87,8 @@ const char* reason(int32_t dtype, int32_t head_size, int32_t block_size, int32_t
   if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_F16 && dtype != PKV_FP8_E4M3)
     return "dtype must be PKV_F32, PKV_BF16, PKV_F16 or PKV_FP8_E4M3";
   if (dtype == PKV_FP8_E4M3 && head_size != 128) return "fp8 caches need head_size 128";
-  if (head_size != 64 && head_size != 128) return "head_size must be 64 or 128";
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return "head_size must be 64, 128 or 256";
   if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64 &&
       block_size != 128)
     return "block_size must be 8, 16, 32, 64 or 128";

@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
   constexpr int RPW = 64 / LPR;     // token rows per wave load
   constexpr int TPS = RPW * kNls;   // tokens per wave step
   static_assert(RPW <= BS && BS % RPW == 0, "a wave load must stay inside one block");
-  static_assert(LPR >= 4 && LPR <= 32, "row width");
+  static_assert(LPR >= 4 && LPR <= 64, "row width");
 
   __shared__ float s_acc[kWaves][GT][D];
   __shared__ float s_m[kWaves][GT];
@@ -372,16 +372,18 @@ static hipError_t launch_bs(const AttnArgs& a, int bs, int gt, dim3 grid, hipStr
 
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int block_size,
                             int heads_per_chunk, dim3 grid, hipStream_t stream) {
-  if (dtype == PKV_F32) {
-    if (head_size == 64) return launch_bs<float, 64>(a, block_size, heads_per_chunk, grid, stream);
-    if (head_size == 128) return launch_bs<float, 128>(a, block_size, heads_per_chunk, grid, stream);
-  } else if (dtype == PKV_BF16) {
-    if (head_size == 64) return launch_bs<uint16_t, 64>(a, block_size, heads_per_chunk, grid, stream);
-    if (head_size == 128) return launch_bs<uint16_t, 128>(a, block_size, heads_per_chunk, grid, stream);
-  } else if (dtype == PKV_F16) {
-    if (head_size == 64) return launch_bs<_Float16, 64>(a, block_size, heads_per_chunk, grid, stream);
-    if (head_size == 128) return launch_bs<_Float16, 128>(a, block_size, heads_per_chunk, grid, stream);
-  }
+  auto by_head = [&](auto elem) -> hipError_t {
+    using T = decltype(elem);
+    switch (head_size) {
+      case 64: return launch_bs<T, 64>(a, block_size, heads_per_chunk, grid, stream);
+      case 128: return launch_bs<T, 128>(a, block_size, heads_per_chunk, grid, stream);
+      case 256: return launch_bs<T, 256>(a, block_size, heads_per_chunk, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  if (dtype == PKV_F32) return by_head(float{});
+  if (dtype == PKV_BF16) return by_head(uint16_t{});
+  if (dtype == PKV_F16) return by_head(_Float16{});
   return hipErrorInvalidValue;
 }
 

@@ -141,16 +141,17 @@ constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;      // row_mirror: lane i <-> 15-i within 16
 
-// Sum over aligned groups of N lanes (N = 4, 8, 16, 32); every lane of the
+// Sum over aligned groups of N lanes (N = 4, 8, 16, 32, 64); every lane of the
 // group receives the total.  Within a row of 16 the butterfly is done with DPP.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
   x += dpp_f<kDppQuadXor1>(x);
   x += dpp_f<kDppQuadXor2>(x);
   if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
   if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
   return x;
 }
 

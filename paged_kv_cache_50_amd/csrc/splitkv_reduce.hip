@@ -157,13 +157,18 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size, hipStream_t st) {
-  const bool d64 = head_size == 64, d128 = head_size == 128;
-  if (dtype == PKV_F32 && d64) return launch_typed<float, 64>(a, st);
-  if (dtype == PKV_F32 && d128) return launch_typed<float, 128>(a, st);
-  if (dtype == PKV_BF16 && d64) return launch_typed<uint16_t, 64>(a, st);
-  if (dtype == PKV_BF16 && d128) return launch_typed<uint16_t, 128>(a, st);
-  if (dtype == PKV_F16 && d64) return launch_typed<_Float16, 64>(a, st);
-  if (dtype == PKV_F16 && d128) return launch_typed<_Float16, 128>(a, st);
+  auto by_head = [&](auto elem) -> hipError_t {
+    using T = decltype(elem);
+    switch (head_size) {
+      case 64: return launch_typed<T, 64>(a, st);
+      case 128: return launch_typed<T, 128>(a, st);
+      case 256: return launch_typed<T, 256>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  if (dtype == PKV_F32) return by_head(float{});
+  if (dtype == PKV_BF16) return by_head(uint16_t{});
+  if (dtype == PKV_F16) return by_head(_Float16{});
   return hipErrorInvalidValue;
 }
 

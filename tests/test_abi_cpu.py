@@ -54,6 +54,12 @@ def test_unsupported_reason(L):
     assert "dtype" in pagedkv.unsupported_reason(5, 128, 16, 32, 8)
     assert "dtype" in pagedkv.unsupported_reason(4, 128, 16, 32, 8)
     assert "head_size" in pagedkv.unsupported_reason(1, 96, 16, 32, 8)
+    # head size 256 on the VALU kernels: float32, bfloat16 and binary16 caches
+    for dt in (pagedkv.PKV_F32, pagedkv.PKV_BF16, pagedkv.PKV_F16):
+        assert pagedkv.unsupported_reason(dt, 256, 16, 32, 8) is None
+    assert "128" in pagedkv.unsupported_reason(pagedkv.PKV_FP8_E4M3, 256, 16, 32, 8)
+    for d in (32, 192, 512):
+        assert "head_size" in pagedkv.unsupported_reason(1, d, 16, 32, 8)
     for bs in (8, 16, 32, 64, 128):
         assert pagedkv.unsupported_reason(1, 128, bs, 32, 8) is None
     for bs in (4, 48, 96, 256):

@@ -21,6 +21,7 @@ def cascade(Lib, c, out=A16, q=A16, cu=A16, sl=A16, bt=A16, mb=400, pre=A16, S=1
 def test_cascade_error_codes(L):
     assert cascade(L, cache(dtype=0, d=128)) == 3               # fp32 cache: no prefix kernel
     assert cascade(L, cache(dtype=1, d=64)) == 3                # head 64
+    assert cascade(L, cache(dtype=1, d=256)) == 3               # head 256: VALU kernels only
     assert cascade(L, cache(), cpl=4095) == 2                   # not a whole number of blocks
     assert cascade(L, cache(), cpl=-16) == 2
     assert cascade(L, cache(), cpl=6000) == 2                   # longer than max_seq_len

@@ -1,0 +1,170 @@
+"""GPU parity at head size 256 (the VALU kernels and the split merge; the
+matrix-core kernels, fp8 caches and cascades take head size 128 only).
+
+The cache write, bit for bit. Decode over float32, bfloat16 and binary16
+caches for MHA and GQA layouts, every block size, split or not (and long
+rows whose ranges exceed the merge's one-round-trip form). Chunked prefill
+rows, causal and not, with and without sliding windows. A call that asks for
+the matrix-core kernels still runs the VALU one. A needle whose output must
+be a cached V row exactly. The no-alloc entry point. All of it is checked
+against the oracle within the dtype's tolerance."""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_50_amd import pagedkv
+from paged_kv_cache_50_amd import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+P = pagedkv
+D = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pagedkv.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _check(w, dw, what):
+    ref, ref_lse = G.reference(w)
+    tol = w.dtype if w.dtype in ("f32", "f16") else "bf16"
+    G.assert_all_rows(G.dev_to_f64(dw.out), G.dev_to_f64(dw.lse), ref, ref_lse, tol, what, w=w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_head256_kv_write_bit_exact(dtype):
+    """Rows of 8 kv heads x 256 elements land in their slots bit for bit;
+    slot -1 and rows past slot_mapping's length write nothing."""
+    torch = G.torch()
+    w = W.make_varlen("h256_write", [5, 40, 0, 17], [3, 1, 4, 2], 8, 8, D, 16, dtype, seed=3)
+    slots = w.slot_mapping.copy()
+    slots[[1, 6]] = -1
+    key, val = w.key_new.copy(), w.value_new.copy()
+    pad = np.ones((2,) + key.shape[1:], dtype=key.dtype)
+    key, val = np.concatenate([key, pad]), np.concatenate([val, pad])
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_cache_write(kc, vc, key, val, slots, w.block_size)
+    _announce(f"head 256 kv_write {dtype} T={len(slots)}")
+    dk, dv = G.np_to_dev(w.k_cache, dtype), G.np_to_dev(w.v_cache, dtype)
+    pagedkv.kv_cache_write(dk, dv, G.np_to_dev(key, dtype), G.np_to_dev(val, dtype),
+                           torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    bits = lambda x: x.view(np.uint32) if x.dtype == np.float32 else x   # NaN slots compare too
+    assert np.array_equal(bits(G.dev_to_bits(dk)), bits(kc))
+    assert np.array_equal(bits(G.dev_to_bits(dv)), bits(vc))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("hq,hkv,bs", [(8, 8, 16), (32, 8, 16), (16, 2, 8), (12, 3, 32),
+                                       (20, 1, 64), (4, 4, 128)])
+@pytest.mark.parametrize("ps", [0, -1, 128])
+def test_head256_decode(dtype, hq, hkv, bs, ps):
+    """Decode rows of lengths 0 to 1300 over MHA and GQA layouts (groups
+    1, 3, 4, 8, 20), every block size, one partition, 512-token ranges or
+    128-token partitions."""
+    lens = [1, 37, 300, 513, 1300, 777, 0]
+    w = W.make_decode("h256_decode", lens, hq, hkv, D, bs, dtype, seed=hq + 3 * hkv + bs)
+    _announce(f"head 256 decode {dtype} {hq}/{hkv} bs={bs} ps={ps}")
+    dw = G.DevWorkload(w)
+    o = P.CallOptions()
+    G.run(dw, partition_size=ps, options=o)
+    assert o.launched & P.RAN_DECODE_VALU and not o.launched & P.RAN_DECODE_MFMA, o.ran()
+    _check(w, dw, f"head 256 decode {dtype} {hq}/{hkv} bs={bs} ps={ps}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head256_long_split(dtype):
+    """Rows of 20k and 9k tokens in 128-token partitions: more ranges than
+    the merge's one-round-trip form takes, so the per-(row, head) merge runs."""
+    w = W.make_decode("h256_long", [20000, 9000, 513], 16, 4, D, 16, dtype, seed=31, sigma=0.5)
+    _announce(f"head 256 long split {dtype}")
+    dw = G.DevWorkload(w)
+    o = P.CallOptions()
+    G.run(dw, partition_size=128, options=o)
+    assert o.launched & P.RAN_SPLIT_MERGE, o.ran()
+    _check(w, dw, f"head 256 long split {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("win", [-1, 40])
+def test_head256_prefill_rows(dtype, causal, win):
+    """Chunked prefill rows (up to 150 query rows) beside decode rows and an
+    empty sequence, causal or symmetric, with or without a window."""
+    w = W.make_varlen("h256_prefill", [0, 300, 900, 5, 0], [150, 1, 64, 30, 0], 16, 4, D, 32,
+                      dtype, seed=7 + causal, causal=causal)
+    w.window_left = win
+    _announce(f"head 256 prefill {dtype} causal={causal} window={win}")
+    dw = G.DevWorkload(w)
+    o = P.CallOptions()
+    G.run(dw, options=o)
+    assert o.launched & P.RAN_PREFILL_VALU and not o.launched & P.RAN_PREFILL_MFMA, o.ran()
+    _check(w, dw, f"head 256 prefill {dtype} causal={causal} window={win}")
+
+
+def test_head256_matrix_core_request_runs_valu():
+    """Asking for the matrix-core decode kernel at head size 256 runs the
+    VALU kernel, with the same result as the library's own choice."""
+    w = W.make_decode("h256_force", [700, 64, 1500], 32, 8, D, 16, "bf16", seed=12)
+    dw = G.DevWorkload(w)
+    G.run(dw)
+    G.torch().cuda.synchronize()
+    a = G.dev_to_bits(dw.out).copy()
+    o = P.CallOptions(decode_kernel=2)
+    G.run(dw, options=o)
+    assert o.launched & P.RAN_DECODE_VALU and not o.launched & P.RAN_DECODE_MFMA, o.ran()
+    assert np.array_equal(G.dev_to_bits(dw.out), a)
+
+
+@pytest.mark.parametrize("hq,hkv,ps", [(8, 8, -1), (32, 8, 0), (32, 8, 128)])
+def test_head256_needle_exact(hq, hkv, ps):
+    """q = 64 e0 and one key = 64 e0 per sequence (bfloat16): that key's
+    logit beats every other by 256, every other probability is exactly 0 in
+    float32, and the output is the needle's V row bit for bit."""
+    lens = [300, 77, 1024]
+    w = W.make_decode("h256_needle", lens, hq, hkv, D, 16, "bf16", seed=hq + ps)
+    one = np.uint16(0x4280)                              # 64.0 in bfloat16
+    w.q[:] = 0
+    w.q[:, :, 0] = one
+    rng = np.random.default_rng(5)
+    needles = [int(rng.integers(0, L)) for L in lens]
+    for s, L in enumerate(lens):
+        for j in range(L):
+            slot = W.slots_of(w.block_tables[s], np.array([j]), w.block_size)[0]
+            b, o = divmod(int(slot), w.block_size)
+            w.k_cache[b, o][:, 0] = one if j == needles[s] else 0
+    _announce(f"head 256 needle {hq}/{hkv} ps={ps}")
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=ps)
+    got = G.dev_to_bits(dw.out)
+    g = hq // hkv
+    for s in range(len(lens)):
+        slot = W.slots_of(w.block_tables[s], np.array([needles[s]]), w.block_size)[0]
+        b, o = divmod(int(slot), w.block_size)
+        assert np.array_equal(got[s], np.repeat(w.v_cache[b, o], g, axis=0)), f"sequence {s}"
+
+
+def test_head256_noalloc_matches_decode():
+    """The no-alloc entry point at head size 256 gives the decode call's
+    result bit for bit (split partials in the library's scratch array)."""
+    torch = G.torch()
+    w = W.make_decode("h256_noalloc", [3000, 40, 1700, 900], 32, 8, D, 16, "bf16", seed=21)
+    dw = G.DevWorkload(w)
+    G.run(dw, partition_size=512)
+    torch.cuda.synchronize()
+    a = G.dev_to_bits(dw.out).copy()
+    dw.out.zero_()
+    P.paged_attention_decode_noalloc(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables,
+                                     dw.seq_lens, w.scale, int(w.max_seq_len), partition_size=512)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.dev_to_bits(dw.out), a)

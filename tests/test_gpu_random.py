@@ -155,14 +155,14 @@ N_COMBO = 256
 
 
 def draw_combo(i: int, base=110_000):
-    """Case i of the crossed sweep: every cache dtype and block size (8 to
-    128), decode or varlen rows, windows and partition sizes, and each of
+    """Case i of the crossed sweep: every cache dtype, head size (64, 128,
+    256) and block size (8 to 128), decode or varlen rows, windows and partition sizes, and each of
     the five launch options set or not independently of the others (an
     option that does not apply to the case, such as head pairs over a
     16-bit cache, must leave the result unchanged)."""
     rng = np.random.default_rng(base + i)
     dtype = str(rng.choice(["f32", "bf16", "f16", "fp8"]))
-    head = 128 if dtype == "fp8" else int(rng.choice([64, 128]))
+    head = 128 if dtype == "fp8" else int(rng.choice([64, 128, 256]))
     bs = int(rng.choice([8, 16, 32, 64, 128]))
     hkv = int(rng.choice([1, 2, 3, 8]))
     group = int(rng.choice([1, 3, 4, 8, 20]))

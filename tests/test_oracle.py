@@ -117,6 +117,30 @@ def test_oracle_matches_bruteforce(bs, causal):
             np.testing.assert_allclose(lse[cu[s]:cu[s + 1], h], np.array(bl), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_oracle_matches_bruteforce_head256(causal):
+    """The widest head the library takes (256), against the same brute
+    force: a GQA pair of query heads over one kv head."""
+    rng = np.random.default_rng(256 + causal)
+    Hq, Hkv, D, bs = 2, 1, 256, 16
+    seq_lens = [1, 9, 33]
+    qlens = [1, 4, 9] if causal else [1, 1, 1]
+    Kc, Vc, bt, Kseq, Vseq = tiny_pool(rng, seq_lens, Hkv, D, bs)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), Hq, D)).astype(np.float32)
+    scale = 1 / 16
+    out, lse = oracle.paged_attention(q, Kc, Vc, bt, np.array(seq_lens), scale, bs, "f32",
+                                      cu_seqlens_q=cu, causal=causal)
+    for s, L in enumerate(seq_lens):
+        for h in range(Hq):
+            Q = [list(map(float, q[r, h])) for r in range(cu[s], cu[s + 1])]
+            K = [list(map(float, Kseq[s][j, 0])) for j in range(L)]
+            V = [list(map(float, Vseq[s][j, 0])) for j in range(L)]
+            bo, bl = brute_attention(Q, K, V, scale, causal)
+            np.testing.assert_allclose(out[cu[s]:cu[s + 1], h], np.array(bo), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[cu[s]:cu[s + 1], h], np.array(bl), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("bs", [4, 16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window", [0, 3, 10, 100])
