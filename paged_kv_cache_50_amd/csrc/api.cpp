@@ -221,7 +221,8 @@ std::pair<unsigned, unsigned> mfma_decode_geometry(AttnArgs& a, const pkv_kv_cac
       const int P = a.partition_size;
       const int64_t span = eff_len + 31;             // the range starts at a multiple of 32
       const int64_t nparts = (span + P - 1) / P;
-      const int cus = device_cus() > 0 ? device_cus() : 256;
+      const int dev_cus = device_cus();
+      const int cus = dev_cus > 0 ? dev_cus : 256;
       const int64_t slots = (int64_t)cus * (is_fp8(cache) && a.heads_per_wave == 1 ? 3 : 2);
       int64_t best = -1;
       const int floor_tpw = tpw;
