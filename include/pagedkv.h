@@ -110,9 +110,9 @@ typedef struct pkv_kv_cache {
   int32_t block_size;    /* tokens per block: 8, 16, 32, 64 or 128                  */
   int32_t num_kv_heads;  /* > 0                                                     */
   int32_t head_size;     /* 64, 128 or 256 (256: float32, bfloat16 and binary16
-                            caches, on the VALU kernels; the capability matrix
-                            of ch. 6 "Matrice de capacités : les champs comme
-                            contrat" lists a backend of head size 256)          */
+                            caches; the capability matrix of ch. 6 "Matrice de
+                            capacités : les champs comme contrat" lists a
+                            backend of head size 256)                          */
   int32_t dtype;         /* pkv_dtype of both caches (and of q/out/key/value, which
                             are bfloat16 for PKV_FP8_E4M3)                          */
   int64_t block_stride;  /* elements between consecutive blocks; 0 = dense; the
@@ -137,7 +137,7 @@ typedef struct pkv_kv_cache {
  */
 typedef struct pkv_call_options {
   int32_t decode_kernel;   /* 0 library choice; 1 the VALU kernel; 2 the matrix-core
-                              kernel (16-bit caches with head_size 128)            */
+                              kernel (16-bit caches with head_size 128 or 256)     */
   int32_t prefill_kernel;  /* 0 library choice; 1 the VALU row kernel (16-bit)       */
   int32_t fp8_head_pairs;  /* 0 library choice; 1 one kv head per wave in fp8 decode  */
   int32_t mixed_launch;    /* 0 library choice; 1 prefill rows and decode rows of a

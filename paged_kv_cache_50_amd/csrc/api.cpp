@@ -142,7 +142,7 @@ constexpr int64_t kWgFixedTokens = 128;    // a workgroup's fixed cost in stream
 
 bool use_mfma_decode(const pkv_kv_cache* c, int group, const Choice& ch) {
   if (c->dtype == PKV_FP8_E4M3) return true;          // the only fp8 decode kernel
-  if (!is16(c->dtype) || c->head_size != 128) return false;
+  if (!is16(c->dtype) || (c->head_size != 128 && c->head_size != 256)) return false;
   if (ch.decode_kernel == 1) return false;
   if (ch.decode_kernel == 2) return true;
   return group >= kMfmaMinGroup;
@@ -270,8 +270,8 @@ pkv_status launch_one_row(AttnArgs& a, const pkv_kv_cache* cache, unsigned gy, i
     for (int64_t z0 = 0; z0 < z_total; z0 += kMaxGridZ) {
       a.z_base = (int32_t)z0;
       const unsigned gz = (unsigned)std::min<int64_t>(kMaxGridZ, z_total - z0);
-      if (pkv::launch_attn_mfma_decode(a, cache->block_size, cache->dtype, dim3(gx, gz, gparts),
-                                       st) != hipSuccess)
+      if (pkv::launch_attn_mfma_decode(a, cache->block_size, cache->head_size, cache->dtype,
+                                       dim3(gx, gz, gparts), st) != hipSuccess)
         return PKV_ERR_HIP;
     }
     a.z_base = 0;

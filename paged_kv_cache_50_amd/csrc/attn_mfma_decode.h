@@ -32,7 +32,12 @@
 // loads into the same registers, computes the logits; then does the same
 // with the V rows (in the same LDS area) and the PV product, so the next
 // tile's loads are in flight while it computes and the LDS of a workgroup
-// stays at 34 KiB (block ids run one tile further ahead).  The 4 waves merge
+// stays at 34 KiB (block ids run one tile further ahead).
+// Head size 256 (16-bit caches): tiles of 16 tokens, so that a tile is the
+// same 8 KiB and eight loads per lane; the logits take 8 k-steps of one
+// 16-token block, and the PV product is the 16 x 16 x 16 form, whose A
+// operand is a single transposed read.  The merge stages [16][256] floats
+// per wave, so the workgroup's LDS is 65 KiB (still two per CU).  The 4 waves merge
 // their softmax states through LDS at the end and write the row, or the
 // range's partial result.
 // Tokens past the partition end are loaded from an in-bounds slot of the last
@@ -40,6 +45,8 @@
 // (select, never multiply), so stale NaNs in unused cache slots cannot reach
 // the result.
 #pragma once
+
+#include <type_traits>
 
 #include "attn_common.h"
 #include "device_common.h"
@@ -51,19 +58,28 @@ namespace dec {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kD = 128;
-constexpr int kTile = 32;                 // tokens per wave step
-constexpr int kKTileBytes = kTile * kD * 2;
-constexpr int kVPitch = kD * 2 + 16;      // LDS bytes per V token row (padded)
-constexpr int kVTileBytes = kTile * kVPitch;
-// a wave stages a tile's K rows, computes the logits, then stages the V rows
-// in the same area: 8.5 KiB per wave, 34 KiB per workgroup
-constexpr int kWaveLds = kKTileBytes > kVTileBytes ? kKTileBytes : kVTileBytes;
-constexpr int kLdsBytes = kWaves * kWaveLds;
+
+// Per-wave geometry for head size D (128 or 256).  A tile is 32 tokens at
+// D = 128 and 16 at D = 256, so that it is 8 KiB of K (and of V) either way,
+// eight 16-byte loads per lane.  A wave stages a tile's K rows, computes the
+// logits, then stages the V rows in the same area; at the end the area holds
+// the wave's [16 heads][D] float32 output for the merge.
+template <int D>
+struct Geo {
+  static_assert(D == 128 || D == 256, "head size");
+  static constexpr int kTile = D == 256 ? 16 : 32;        // tokens per wave step
+  static constexpr int kVPitch = D * 2 + 16;              // LDS bytes per V token row (padded)
+  static constexpr int kKTileBytes = kTile * D * 2;
+  static constexpr int kVTileBytes = kTile * kVPitch;
+  static constexpr int kTileArea = kKTileBytes > kVTileBytes ? kKTileBytes : kVTileBytes;
+  static constexpr int kMergeBytes = 16 * D * 4;
+  // 8.5 KiB per wave (34 KiB per workgroup) at D = 128; 16 KiB (64 KiB) at 256
+  static constexpr int kWaveLds = kTileArea > kMergeBytes ? kTileArea : kMergeBytes;
+};
 // LDS of a workgroup whose waves cover HP kv heads each
-template <int HP>
-constexpr int kLdsBytesHp = HP * kLdsBytes;
-static_assert(kWaveLds >= 16 * kD * 4, "the final merge stages [16 heads][D] floats per wave");
+template <int HP, int D = 128>
+constexpr int kLdsBytesHp = HP * kWaves * Geo<D>::kWaveLds;
+constexpr int kLdsBytes = kLdsBytesHp<1>;
 
 __device__ __forceinline__ float xmax16_32(float x) {
   // max over the 4 lanes {l, l^16, l^32, l^48}: the token groups of a column
@@ -83,7 +99,8 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // LDS byte offset of 16-byte chunk c (0..15) of token row t in a K tile:
 // slots are XOR-swizzled by the row so that 16 lanes reading the same chunk
 // of 16 different rows hit 16 different bank groups.
-__device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + ((c ^ (t & 15)) << 4); }
+template <int D>
+__device__ __forceinline__ int ktile_off(int t, int c) { return t * (D * 2) + ((c ^ (t & 15)) << 4); }
 
 // FP8: the caches hold e4m3 codes with per-kv-head scales; a token row is
 // then 128 bytes, read by 8 lanes, and converted (exactly) to bfloat16 while
@@ -99,7 +116,7 @@ __device__ __forceinline__ int ktile_off(int t, int c) { return t * (kD * 2) + (
 // item zi (before the dispatch order is applied), key range bz of nz.  The
 // caller provides the LDS areas (kLdsBytesHp<HP>, 16-byte aligned, and the
 // two [kWaves][32] merge arrays).
-template <int BS, int DT, int HP>
+template <int BS, int DT, int HP, int D = 128>
 __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, int bz, int nz,
                                              char* __restrict__ s_lds, float (*s_m)[32],
                                              float (*s_l)[32]) {
@@ -109,12 +126,23 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   using H = Fmt16<DT == PKV_F16>;                    // operand format of the products
   using x8 = typename H::x8;
   static_assert(HP == 1 || (HP == 2 && FP8), "two heads per wave: e4m3 caches");
+  static_assert(D == 128 || (HP == 1 && !FP8), "head size 256: 16-bit caches");
+  constexpr int kTile = Geo<D>::kTile;
+  constexpr int kVPitch = Geo<D>::kVPitch;
+  constexpr int kWaveLds = Geo<D>::kWaveLds;
+  constexpr int kKSteps = D / 32;                    // k-steps of the logits product
+  constexpr int kTT = kTile / 16;                    // 16-token blocks of a tile (2 or 1)
+  constexpr int kNS = 4 * kTT;                       // logits of a lane per tile
+  constexpr int kDB = D / 16;                        // 16-dim blocks of the output
+  // probabilities as the B operand of the PV product: 8 values (32-token
+  // tiles, 16 x 16 x 32 products) or 4 (16-token tiles, 16 x 16 x 16)
+  using PB = std::conditional_t<kTT == 2, x8, typename H::x4>;
   // blocks a 32-token tile spans; a tile of larger blocks lies inside one
   // block (tiles start at multiples of 32 positions), at offset tbase % BS
   constexpr int kBlkPerTile = BS < kTile ? kTile / BS : 1;
   constexpr int kEB = FP8 ? 1 : 2;                   // bytes per cached element
   // bytes of one token's row as a wave reads it: HP adjacent kv heads
-  constexpr int kRowBytes = HP * kD * kEB;
+  constexpr int kRowBytes = HP * D * kEB;
   constexpr int kLanesPerRow = kRowBytes / 16;
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;    // token rows per wave load
   constexpr int kLoads = kTile / kRowsPerLoad;       // loads per tile (K and V each)
@@ -155,25 +183,25 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int pbegin = it.L_begin;                 // first visible key (sliding window)
 
   // Q^T B operands: lane (kg, n) holds q[h0+n][(4j+kg)*8 .. +8] for k-step j.
-  x8 qb[HP][4];
+  x8 qb[HP][kKSteps];
 #pragma unroll
   for (int hp = 0; hp < HP; ++hp) {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)it.row * a.num_heads + h0 + hp * group + n) * kD;
+                           ((int64_t)it.row * a.num_heads + h0 + hp * group + n) * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kKSteps; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (n < G) v = *reinterpret_cast<const u32x4*>(qrow + (4 * j + kg) * 8);
       qb[hp][j] = H::as_x8(v);
     }
   }
 
-  f32x4 o[HP][8];
+  f32x4 o[HP][kDB];
   float m[HP], lsum[HP], logit_scale[HP];
 #pragma unroll
   for (int hp = 0; hp < HP; ++hp) {
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) o[hp][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jd = 0; jd < kDB; ++jd) o[hp][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[hp] = -INFINITY;
     lsum[hp] = 0.f;
     logit_scale[hp] = a.scale_log2;
@@ -183,13 +211,14 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
   const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
   const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
-  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * kD * kEB;   // bytes
-  const uint32_t head_off = (uint32_t)kvh * kD * kEB;
+  const uint32_t tok_stride = (uint32_t)a.num_kv_heads * D * kEB;   // bytes
+  const uint32_t head_off = (uint32_t)kvh * D * kEB;
   const int64_t blk_stride = a.block_stride * kEB;
   // lane's place in a natural load: token row within the load, byte offset
   // in the row, and (fp8) which head's 128 bytes it holds
   const int lrow = lane / kLanesPerRow;
   const int lbyte = (lane % kLanesPerRow) * 16;
+  const int lchunk = lane % kLanesPerRow;             // 16-byte chunk of the row it loads
   const int lhead = FP8 ? (lane % kLanesPerRow) / 8 : 0;
   const int64_t max_blk = a.num_blocks - 1;
   const int ntiles = (pend > pstart) ? (pend - pstart + kTile - 1) / kTile : 0;
@@ -237,10 +266,10 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
         char* klds = wlds + lhead * kWaveLds;
         u32x4 k0, k1;
         e4m3x16_to_bf16x16(K[i], k0, k1);
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c)) = k0;
-        *reinterpret_cast<u32x4*>(klds + ktile_off(tok, 2 * c + 1)) = k1;
+        *reinterpret_cast<u32x4*>(klds + ktile_off<D>(tok, 2 * c)) = k0;
+        *reinterpret_cast<u32x4*>(klds + ktile_off<D>(tok, 2 * c + 1)) = k1;
       } else {
-        *reinterpret_cast<u32x4*>(wlds + ktile_off(tok, n)) = K[i];
+        *reinterpret_cast<u32x4*>(wlds + ktile_off<D>(tok, lchunk)) = K[i];
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -264,7 +293,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       } else {
         u32x4 v = V[i];
         if (dead) v = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(wlds + tok * kVPitch + n * 16) = v;
+        *reinterpret_cast<u32x4*>(wlds + tok * kVPitch + lchunk * 16) = v;
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -279,20 +308,20 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     const char* klds = wlds + hp * kWaveLds;
 
     // logits S^T: A operand = K rows (token tt*16 + n, chunk 4j + kg)
-    f32x4 sacc[2];
+    f32x4 sacc[kTT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kTT; ++tt) {
       sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(klds + ktile_off(tt * 16 + n, 4 * j + kg));
+      for (int j = 0; j < kKSteps; ++j) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(klds + ktile_off<D>(tt * 16 + n, 4 * j + kg));
         sacc[tt] = H::mfma(H::as_x8(ka), qb[hp][j], sacc[tt]);
       }
     }
     // lane holds tokens tt*16 + 4kg + i of head column n
-    float s[8];
+    float s[kNS];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tbase + tt * 16 + 4 * kg + i;
@@ -301,23 +330,23 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
       }
     float mx = s[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+    for (int e = 1; e < kNS; ++e) mx = fmaxf(mx, s[e]);
     mx = xmax16_32(mx);
     const float mn = fmaxf(m[hp], mx);
     const float mref = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = fast_exp2(m[hp] - mref);
     m[hp] = mn;
-    x8 pb;
+    PB pb;
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kNS; ++e) {
       const float p = fast_exp2(s[e] - mref);
       psum += p;
       pb[e] = (typename H::elem)p;
     }
     lsum[hp] = lsum[hp] * alpha + psum;
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) o[hp][jd] *= alpha;
+    for (int jd = 0; jd < kDB; ++jd) o[hp][jd] *= alpha;
     __asm__ volatile("" ::: "memory");
     return pb;
   };
@@ -325,17 +354,22 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   // O^T += V^T P^T for head hp of a tile whose V rows are staged, one 16-dim
   // tile at a time; the transposed reads give lane (kg, n) V[4kg + jj][16jd + n]
   // and V[16 + 4kg + jj][16jd + n].
-  auto pv = [&](const x8 pb, int hp) {
+  auto pv = [&](const PB pb, int hp) {
     {
       const int jj = n >> 2, q4 = n & 3;
       const char* r0 = wlds + hp * kWaveLds + (4 * kg + jj) * kVPitch + q4 * 8;
       const char* r1 = r0 + 16 * kVPitch;
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
+      for (int jd = 0; jd < kDB; ++jd) {
         i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r0 + jd * 32));
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r1 + jd * 32));
-        const x8 va = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[hp][jd] = H::mfma(va, pb, o[hp][jd]);
+        if constexpr (kTT == 2) {
+          i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(r1 + jd * 32));
+          const x8 va = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[hp][jd] = H::mfma(va, pb, o[hp][jd]);
+        } else {
+          // 16-token tiles: the first transposed read is the whole A operand
+          o[hp][jd] = H::mfma16(__builtin_bit_cast(typename H::x4, lo), pb, o[hp][jd]);
+        }
       }
     }
     __asm__ volatile("" ::: "memory");
@@ -371,7 +405,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     const int nt = tile + tstep;
     stage_k(kr);
     if (nt < tend) issue(kc, ids, kr);
-    x8 pb[HP];
+    PB pb[HP];
 #pragma unroll
     for (int hp = 0; hp < HP; ++hp) pb[hp] = logits(tile, hp);
     stage_v(tile, vr);
@@ -390,10 +424,10 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
   for (int hp = 0; hp < HP; ++hp) {
     lsum[hp] = xsum16_32(lsum[hp]);
-    float* so = reinterpret_cast<float*>(wlds + hp * kWaveLds);   // [16 heads][128]
+    float* so = reinterpret_cast<float*>(wlds + hp * kWaveLds);   // [16 heads][D]
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd)
-      *reinterpret_cast<f32x4*>(so + n * kD + 16 * jd + 4 * kg) = o[hp][jd];
+    for (int jd = 0; jd < kDB; ++jd)
+      *reinterpret_cast<f32x4*>(so + n * D + 16 * jd + 4 * kg) = o[hp][jd];
     if (kg == 0) {
       s_m[wave][hp * 16 + n] = m[hp];
       s_l[wave][hp * 16 + n] = lsum[hp];
@@ -401,10 +435,10 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   }
   __syncthreads();
   const int range = rz;
-  for (int idx = tid; idx < HP * G * kD; idx += kThreads) {
-    const int hp = idx / (G * kD);
-    const int h = (idx / kD) % G;
-    const int d = idx % kD;
+  for (int idx = tid; idx < HP * G * D; idx += kThreads) {
+    const int hp = idx / (G * D);
+    const int h = (idx / D) % G;
+    const int d = idx % D;
     float M = s_m[0][hp * 16 + h];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hp * 16 + h]);
@@ -413,7 +447,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(s_m[w][hp * 16 + h] - Mref);
-      O = fmaf(reinterpret_cast<const float*>(s_lds + (w * HP + hp) * kWaveLds)[h * kD + d], f, O);
+      O = fmaf(reinterpret_cast<const float*>(s_lds + (w * HP + hp) * kWaveLds)[h * D + d], f, O);
       Ls = fmaf(s_l[w][hp * 16 + h], f, Ls);
     }
     const int head = h0 + hp * group + h;
@@ -421,14 +455,14 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
     if constexpr (FP8) out_scale = a.v_scale[kvh + hp];
     if (it.nranges == 1) {
       const float v = Ls > 0.f ? O / Ls * out_scale : 0.f;
-      static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * kD + d] =
+      static_cast<uint16_t*>(a.out)[((int64_t)it.row * a.num_heads + head) * D + d] =
           static_cast<uint16_t>(H::rne(v));
       if (d == 0 && a.lse_out)
         a.lse_out[(int64_t)it.row * a.num_heads + head] =
             Ls > 0.f ? (M + acc_log2(Ls)) * kLn2 : -INFINITY;
     } else {
       const int64_t widx = ((int64_t)range * a.num_heads + head) * a.num_seqs + it.seq;
-      a.ws_o[widx * kD + d] = Ls > 0.f ? O / Ls * out_scale : 0.f;
+      a.ws_o[widx * D + d] = Ls > 0.f ? O / Ls * out_scale : 0.f;
       if (d == 0) a.ws_lse[widx] = Ls > 0.f ? M + acc_log2(Ls) : -INFINITY;
     }
   }

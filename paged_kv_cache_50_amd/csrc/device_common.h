@@ -9,8 +9,10 @@ namespace pkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -63,9 +65,15 @@ template <>
 struct Fmt16<false> {
   typedef __bf16 elem;
   typedef bf16x8_t x8;
+  typedef bf16x4_t x4;
   static __device__ __forceinline__ x8 as_x8(u32x4 v) { return __builtin_bit_cast(x8, v); }
   static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // the 16 x 16 x 16 product (K = 16: 4 operand values per lane)
+  static __device__ __forceinline__ f32x4 mfma16(x4 a, x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
@@ -76,9 +84,13 @@ template <>
 struct Fmt16<true> {
   typedef _Float16 elem;
   typedef f16x8_t x8;
+  typedef f16x4_t x4;
   static __device__ __forceinline__ x8 as_x8(u32x4 v) { return __builtin_bit_cast(x8, v); }
   static __device__ __forceinline__ f32x4 mfma(x8 a, x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(x4 a, x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
   static __device__ __forceinline__ float hi(uint32_t w) { return f16_hi(w); }

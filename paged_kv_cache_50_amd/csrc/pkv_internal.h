@@ -109,11 +109,12 @@ hipError_t launch_attn_valu(const AttnArgs& a, int dtype, int head_size, int blo
 
 // The matrix-core kernels below take the cache's pkv_dtype: PKV_BF16,
 // PKV_F16 or PKV_FP8_E4M3 (any other value: hipErrorInvalidValue).
-// Grouped-query decode on the matrix cores: head size 128, up to 16 query
-// heads per kv-head chunk (head_chunks = ceil(group / 16)).
+// Grouped-query decode on the matrix cores: head size 128 (256 over 16-bit
+// caches), up to 16 query heads per kv-head chunk (head_chunks =
+// ceil(group / 16)).
 // grid = (num_kv_heads * head_chunks, sequences, ceil(partitions / parts_per_wg)).
-hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, int dtype, dim3 grid,
-                                   hipStream_t stream);
+hipError_t launch_attn_mfma_decode(const AttnArgs& a, int block_size, int head_size, int dtype,
+                                   dim3 grid, hipStream_t stream);
 
 // Chunked prefill on the matrix cores (rows of sequences with > 1 query
 // rows): head size 128.

@@ -1,13 +1,14 @@
-"""GPU parity at head size 256 (the VALU kernels and the split merge; the
-matrix-core kernels, fp8 caches and cascades take head size 128 only).
+"""GPU parity at head size 256: the VALU kernel, grouped decode on the
+matrix cores over 16-bit caches (16-token tiles), and the split merge; fp8
+caches, the matrix-core prefill and cascades take head size 128 only.
 
 The cache write, bit for bit. Decode over float32, bfloat16 and binary16
 caches for MHA and GQA layouts, every block size, split or not (and long
-rows whose ranges exceed the merge's one-round-trip form). Chunked prefill
-rows, causal and not, with and without sliding windows. A call that asks for
-the matrix-core kernels still runs the VALU one. A needle whose output must
-be a cached V row exactly. The no-alloc entry point. All of it is checked
-against the oracle within the dtype's tolerance."""
+rows whose ranges exceed the merge's one-round-trip form), on the kernel
+the library picks and on both kernels by request. Chunked prefill rows,
+causal and not, with and without sliding windows. A needle whose output
+must be a cached V row exactly. The no-alloc entry point. All of it is
+checked against the oracle within the dtype's tolerance."""
 import numpy as np
 import pytest
 
@@ -78,7 +79,10 @@ def test_head256_decode(dtype, hq, hkv, bs, ps):
     dw = G.DevWorkload(w)
     o = P.CallOptions()
     G.run(dw, partition_size=ps, options=o)
-    assert o.launched & P.RAN_DECODE_VALU and not o.launched & P.RAN_DECODE_MFMA, o.ran()
+    mfma = dtype != "f32" and hq // hkv >= 4             # grouped decode of 16-bit caches
+    want, other = ((P.RAN_DECODE_MFMA, P.RAN_DECODE_VALU) if mfma
+                   else (P.RAN_DECODE_VALU, P.RAN_DECODE_MFMA))
+    assert o.launched & want and not o.launched & other, o.ran()
     _check(w, dw, f"head 256 decode {dtype} {hq}/{hkv} bs={bs} ps={ps}")
 
 
@@ -112,18 +116,22 @@ def test_head256_prefill_rows(dtype, causal, win):
     _check(w, dw, f"head 256 prefill {dtype} causal={causal} window={win}")
 
 
-def test_head256_matrix_core_request_runs_valu():
-    """Asking for the matrix-core decode kernel at head size 256 runs the
-    VALU kernel, with the same result as the library's own choice."""
-    w = W.make_decode("h256_force", [700, 64, 1500], 32, 8, D, 16, "bf16", seed=12)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 2), (40, 2)])
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_head256_both_decode_kernels(dtype, hq, hkv, kernel):
+    """Either decode kernel on request (the VALU one, or the matrix cores
+    with 16-token tiles) for MHA, a group of 8 and a group of 20 split
+    into head chunks, against the oracle, split into 512-token ranges."""
+    w = W.make_decode("h256_kernels", [700, 64, 1500, 2100, 0], hq, hkv, D, 16, dtype,
+                      seed=12 + hq)
+    _announce(f"head 256 decode_kernel={kernel} {dtype} {hq}/{hkv}")
     dw = G.DevWorkload(w)
-    G.run(dw)
-    G.torch().cuda.synchronize()
-    a = G.dev_to_bits(dw.out).copy()
-    o = P.CallOptions(decode_kernel=2)
-    G.run(dw, options=o)
-    assert o.launched & P.RAN_DECODE_VALU and not o.launched & P.RAN_DECODE_MFMA, o.ran()
-    assert np.array_equal(G.dev_to_bits(dw.out), a)
+    o = P.CallOptions(decode_kernel=kernel)
+    G.run(dw, partition_size=512, options=o)
+    want = P.RAN_DECODE_VALU if kernel == 1 else P.RAN_DECODE_MFMA
+    assert o.launched & want, o.ran()
+    _check(w, dw, f"head 256 decode_kernel={kernel} {dtype} {hq}/{hkv}")
 
 
 @pytest.mark.parametrize("hq,hkv,ps", [(8, 8, -1), (32, 8, 0), (32, 8, 128)])
@@ -156,7 +164,8 @@ def test_head256_needle_exact(hq, hkv, ps):
 
 def test_head256_noalloc_matches_decode():
     """The no-alloc entry point at head size 256 gives the decode call's
-    result bit for bit (split partials in the library's scratch array)."""
+    result bit for bit (split partials and the sequence order in the
+    library's scratch array; grouped decode on the matrix cores)."""
     torch = G.torch()
     w = W.make_decode("h256_noalloc", [3000, 40, 1700, 900], 32, 8, D, 16, "bf16", seed=21)
     dw = G.DevWorkload(w)
