@@ -58,6 +58,15 @@ namespace dec {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Lazy exponent reference: probabilities are formed against the running
+// reference, which is raised (with a rescale of the accumulators) only when
+// a tile's max outgrows it by more than kRescaleSlack (log2 units), so a
+// probability never exceeds 2^kRescaleSlack.  It starts at a finite stand-in
+// for -inf, far below any logit: the first visible key raises it, and a
+// column that sees no key keeps it with sum 0.
+constexpr float kRescaleSlack = 8.f;
+constexpr float kSlackSum = 256.f;              // 2^kRescaleSlack
+constexpr float kMinRef = -3.0e38f;
 
 // Per-wave geometry for head size D (128 or 256).  A tile is 32 tokens at
 // D = 128 and 16 at D = 256, so that it is 8 KiB of K (and of V) either way,
@@ -202,7 +211,7 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
   for (int hp = 0; hp < HP; ++hp) {
 #pragma unroll
     for (int jd = 0; jd < kDB; ++jd) o[hp][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[hp] = -INFINITY;
+    m[hp] = kMinRef;
     lsum[hp] = 0.f;
     logit_scale[hp] = a.scale_log2;
     if constexpr (FP8) logit_scale[hp] *= a.k_scale[kvh + hp];
@@ -328,25 +337,41 @@ __device__ __forceinline__ void decode_block(const AttnArgs& a, int bx, int zi, 
         s[tt * 4 + i] = (full || (tok < pend && tok >= pbegin)) ? sacc[tt][i] * logit_scale[hp]
                                                                 : -INFINITY;
       }
-    float mx = s[0];
-#pragma unroll
-    for (int e = 1; e < kNS; ++e) mx = fmaxf(mx, s[e]);
-    mx = xmax16_32(mx);
-    const float mn = fmaxf(m[hp], mx);
-    const float mref = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m[hp] - mref);
-    m[hp] = mn;
+    // Probabilities against the current reference.  Some lane's sum can
+    // exceed 2^slack only if its column's max outgrew the reference by more
+    // than the slack (or several of its probabilities are large); then, and
+    // only then, the wave takes the full step: the tile's column maxima, the
+    // raised references with the rescale, and the probabilities again.  The
+    // result is the same as always taking it.
     PB pb;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < kNS; ++e) {
-      const float p = fast_exp2(s[e] - mref);
+      const float p = fast_exp2(s[e] - m[hp]);
       psum += p;
       pb[e] = (typename H::elem)p;
     }
-    lsum[hp] = lsum[hp] * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSlackSum))) {
+      float mx = s[0];
 #pragma unroll
-    for (int jd = 0; jd < kDB; ++jd) o[hp][jd] *= alpha;
+      for (int e = 1; e < kNS; ++e) mx = fmaxf(mx, s[e]);
+      mx = xmax16_32(mx);                            // the same on the column's 4 lanes
+      if (mx > m[hp] + kRescaleSlack) {
+        const float alpha = fast_exp2(m[hp] - mx);
+        lsum[hp] *= alpha;
+#pragma unroll
+        for (int jd = 0; jd < kDB; ++jd) o[hp][jd] *= alpha;
+        m[hp] = mx;
+      }
+      psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < kNS; ++e) {
+        const float p = fast_exp2(s[e] - m[hp]);
+        psum += p;
+        pb[e] = (typename H::elem)p;
+      }
+    }
+    lsum[hp] += psum;
     __asm__ volatile("" ::: "memory");
     return pb;
   };
