@@ -32,7 +32,7 @@
 // loads into the same registers, computes the logits; then does the same
 // with the V rows (in the same LDS area) and the PV product, so the next
 // tile's loads are in flight while it computes and the LDS of a workgroup
-// stays at 34 KiB (block ids run one tile further ahead).
+// stays at 35 KiB (block ids run one tile further ahead).
 // Head size 256 (16-bit caches): tiles of 16 tokens, so that a tile is the
 // same 8 KiB and eight loads per lane; the logits take 8 k-steps of one
 // 16-token block, and the PV product is the 16 x 16 x 16 form, whose A
@@ -82,7 +82,8 @@ struct Geo {
   static constexpr int kVTileBytes = kTile * kVPitch;
   static constexpr int kTileArea = kKTileBytes > kVTileBytes ? kKTileBytes : kVTileBytes;
   static constexpr int kMergeBytes = 16 * D * 4;
-  // 8.5 KiB per wave (34 KiB per workgroup) at D = 128; 16 KiB (64 KiB) at 256
+  // 8.5 KiB per wave (34 KiB per workgroup, 35 KiB with the merge arrays) at
+  // D = 128; 16 KiB (64 KiB, 65 KiB) at D = 256
   static constexpr int kWaveLds = kTileArea > kMergeBytes ? kTileArea : kMergeBytes;
 };
 // LDS of a workgroup whose waves cover HP kv heads each
