@@ -325,11 +325,15 @@ pkv_status pkv_paged_attention_varlen(void* out, const void* q, const pkv_kv_cac
  *                  block_tables will do)
  *   other arguments as for pkv_paged_attention_varlen
  *   workspace      >= pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned
- * Needs a bfloat16, binary16 or fp8 (e4m3) cache with head_size 128
- * (PKV_ERR_UNSUPPORTED otherwise) and, when common_prefix_len > 0, a
- * positive scale (PKV_ERR_SHAPE otherwise) and positive fp8 k_scale entries,
- * as for the prefill rows of pkv_paged_attention_varlen: the prefix pass is
- * the prefill kernel.  common_prefix_len 0 is the plain varlen call.
+ * Takes every cache the varlen call takes.  Over bfloat16, binary16 and fp8
+ * (e4m3) caches with head_size 128 the prefix pass runs on the matrix cores;
+ * over float32 caches and other head sizes (or with the VALU row kernel
+ * requested) it runs on the VALU kernel, one query row per workgroup, and
+ * is then no faster than the plain call (pkv_cascade_reason says so).  When
+ * common_prefix_len > 0 the scale must be positive (PKV_ERR_SHAPE
+ * otherwise), and so must the fp8 k_scale entries, as for the prefill rows
+ * of pkv_paged_attention_varlen.  common_prefix_len 0 is the plain varlen
+ * call.
  * Asynchronous on `stream`.
  * The suffix result is rounded to the output dtype (bfloat16 or binary16)
  * before the merge, as the output of the pages' suffix call is; the prefix
@@ -359,7 +363,10 @@ size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t
 
 /*
  * Should a batch use cascade attention?  NULL when it is advised, else a
- * static string saying why not.  The pages' thresholds come first (ch. 6
+ * static string saying why not.  Caches whose prefix pass would run on the
+ * VALU kernel (float32, or head_size other than 128) are not advised: there
+ * the cascade measured no faster than the plain call.  Then the pages'
+ * thresholds (ch. 6
  * "Réflexion de conception": a shared prefix of at least 256 tokens, at least
  * 8 requests, no sliding window), then a rough cost model of this library
  * for the prefix's share of the work: the plain form takes the longer of

@@ -447,7 +447,7 @@ constexpr int64_t kPrefixTargetWgsFused = 128;
 // matrix-core kernel; a call's options may keep separate launches (A/B).
 bool use_cascade_launch(const pkv_kv_cache* cache, int group, const Choice& ch) {
   if (ch.cascade == 1) return false;
-  return use_mfma_decode(cache, group, ch) && device_cus() > 0;
+  return use_mfma_prefill(cache, ch) && use_mfma_decode(cache, group, ch) && device_cus() > 0;
 }
 
 // XCDs in four (by workgroup index) that start the one-launch cascade on
@@ -844,7 +844,8 @@ const char* pkv_cascade_reason(int32_t common_prefix_len, int32_t num_seqs, int3
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                                int32_t dtype, int32_t window_left) {
   if ((!is16(dtype) && dtype != PKV_FP8_E4M3) || head_size != 128)
-    return "cascade attention needs bfloat16, fp16 or fp8 caches with head_size 128";
+    return "the prefix pass would run on the VALU kernel (float32 caches or head_size other "
+           "than 128), one query row per workgroup: the plain call is as fast or faster";
   if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
     return "num_heads must be a positive multiple of num_kv_heads";
   if (window_left >= 0) return "sliding-window attention does not use the cascade";
@@ -888,8 +889,6 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
       max_seq_len > kMaxSeqLen || max_query_len < 0 || max_blocks_per_seq <= 0)
     return PKV_ERR_SHAPE;
   if (reason(cache->dtype, cache->head_size, cache->block_size, num_heads, cache->num_kv_heads))
-    return PKV_ERR_UNSUPPORTED;
-  if ((!is16(cache->dtype) && cache->dtype != PKV_FP8_E4M3) || cache->head_size != 128)
     return PKV_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   const int32_t cpl = common_prefix_len;
@@ -984,9 +983,23 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
     if (st != PKV_OK) return st;
   } else {
     ch.ran |= PKV_RAN_PREFIX;
-    if (pkv::launch_attn_mfma_prefix(p, cache->block_size, cache->dtype,
-                                     dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
-      return PKV_ERR_HIP;
+    if (use_mfma_prefill(cache, ch)) {
+      if (pkv::launch_attn_mfma_prefix(p, cache->block_size, cache->dtype,
+                                       dim3(g.qtiles, g.gy, (unsigned)g.parts), s) != hipSuccess)
+        return PKV_ERR_HIP;
+    } else {
+      // other dtypes and head sizes: the VALU kernel, one workgroup per
+      // (kv-head chunk, query row, prefix partition); its partials are
+      // indexed by row, so the launch takes num_seqs = rows
+      AttnArgs pv = p;
+      pv.num_seqs = num_tokens;
+      const int gt = heads_per_chunk(group);
+      pv.head_chunks = group / gt;
+      st = launch_valu_z_chunks(pv, cache->dtype, cache->head_size, cache->block_size, gt,
+                                (unsigned)(cache->num_kv_heads * pv.head_chunks),
+                                (unsigned)g.parts, num_tokens, s);
+      if (st != PKV_OK) return st;
+    }
     // 2. suffix pass: each row against its own keys (from the prefix end on)
     st = varlen_impl(out, q, cache, cu_seqlens_q, seq_lens, block_tables, max_blocks_per_seq,
                      num_seqs, num_tokens, num_heads, max_query_len, max_seq_len, scale, causal,
@@ -999,7 +1012,9 @@ pkv_status pkv_cascade_attention(void* out, const void* q, const pkv_kv_cache* c
   m.cu_seqlens_q = cu_seqlens_q;
   m.lse_out = lse_out;
   ch.ran |= PKV_RAN_CASCADE_MERGE;
-  if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, io_dtype(cache->dtype), s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_cascade_merge(m, lse_suffix, p.num_splits, io_dtype(cache->dtype),
+                                cache->head_size, s) != hipSuccess)
+    return PKV_ERR_HIP;
   return PKV_OK;
 }
 

@@ -51,6 +51,22 @@ struct Item {
 // Maps the workgroup to (sequence, row, key range).  Returns false when the
 // workgroup has nothing to do.  Identical logic runs in the reduce kernel.
 __device__ __forceinline__ bool resolve_item(const AttnArgs& a, int z, Item& it) {
+  if (a.mode == kModePrefix) {
+    // cascade prefix pass on the VALU kernel: query row z of the batch
+    // against the shared prefix (keys 0 .. prefix_len-1, read through
+    // block-table row 0), unmasked, one partial per partition; the partials
+    // are indexed by row (the launch passes num_seqs = rows)
+    if (z >= a.num_tokens || a.partition_size <= 0) return false;
+    it.seq = z;
+    it.row = z;
+    it.L_begin = 0;
+    it.L_end = min(max(a.prefix_len, 0), a.max_blocks_per_seq * a.block_size);
+    it.base = 0;
+    it.P = a.partition_size;
+    it.nparts = max(1, (it.L_end + it.P - 1) / it.P);
+    it.nranges = it.nparts;
+    return true;
+  }
   int seq, row, qlen = 1, qidx = 0;
   if (a.mode == kModeDecode) {
     seq = z;

@@ -175,7 +175,9 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  const int32_t* __restrict__ bt = a.block_tables + (int64_t)it.seq * a.max_blocks_per_seq;
+  // the cascade prefix pass reads every row's keys through block-table row 0
+  const int bt_row = a.mode == kModePrefix ? 0 : it.seq;
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)bt_row * a.max_blocks_per_seq;
   const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
   const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
   const int64_t tok_stride = (int64_t)a.num_kv_heads * D;            // elements between tokens
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(const AttnArgs a) {
       Ls = fmaf(s_l[w][h], f, Ls);
     }
     const int head = h0 + h;
-    if (it.nranges == 1) {
+    if (it.nranges == 1 && a.mode != kModePrefix) {
       const float v = Ls > 0.f ? O / Ls : 0.f;
       store_out<T>(a.out, ((int64_t)it.row * a.num_heads + head) * D + d, v);
       if (d == 0 && a.lse_out)

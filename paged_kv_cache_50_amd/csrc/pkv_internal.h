@@ -16,7 +16,8 @@ enum AttnMode : int32_t {
   kModeVarlenRows = 2, // z = query row; only rows of sequences with > 1 query rows, no split
   kModePrefix = 3      // cascade prefix pass: every query row of the batch against the shared
                        // prefix (keys 0 .. prefix_len-1 through block_tables row 0), no mask;
-                       // z = key partition of partition_size tokens, fp32 partials out
+                       // z = key partition of partition_size tokens, fp32 partials out (the
+                       // VALU kernel: grid.y = query row, grid.z = partition, num_seqs = rows)
 };
 
 // Arguments of the attention kernels (passed by value).
@@ -163,9 +164,10 @@ hipError_t launch_attn_mfma_prefix(const AttnArgs& a, int block_size, int dtype,
 // Cascade merge: out (the suffix result, in place) and its natural-log lse
 // `lse_suffix` [rows, heads] are combined with `num_parts` prefix partials
 // (layout of launch_attn_mfma_prefix); rows of sequences with seq_len 0 keep
-// the suffix result (zeros).  out_dtype PKV_BF16 or PKV_F16, head size 128.
+// the suffix result (zeros).  out_dtype PKV_F32, PKV_BF16 or PKV_F16; head
+// size 64, 128 or 256.
 hipError_t launch_cascade_merge(const AttnArgs& a, const float* lse_suffix, int num_parts,
-                                int out_dtype, hipStream_t stream);
+                                int out_dtype, int head_size, hipStream_t stream);
 
 // Log-sum-exp merge of split partial results (modes kModeDecode/kModeVarlenOne).
 hipError_t launch_splitkv_reduce(const AttnArgs& a, int dtype, int head_size,

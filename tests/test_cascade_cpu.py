@@ -19,9 +19,14 @@ def cascade(Lib, c, out=A16, q=A16, cu=A16, sl=A16, bt=A16, mb=400, pre=A16, S=1
 
 
 def test_cascade_error_codes(L):
-    assert cascade(L, cache(dtype=0, d=128)) == 3               # fp32 cache: no prefix kernel
-    assert cascade(L, cache(dtype=1, d=64)) == 3                # head 64
-    assert cascade(L, cache(dtype=1, d=256)) == 3               # head 256: VALU kernels only
+    # float32 caches and head sizes 64 and 256 (prefix pass on the VALU
+    # kernel) pass the capability check: a workspace one byte short is the
+    # first error
+    for dt, d in ((0, 128), (1, 64), (1, 256), (3, 64), (0, 256)):
+        need = pagedkv.cascade_workspace_bytes(16, 16, 32, 8, d, 5000, 4096)
+        assert cascade(L, cache(dtype=dt, d=d), wsb=need - 1) == 5, (dt, d)
+    assert cascade(L, cache(dtype=4)) == 3                      # no such dtype
+    assert cascade(L, cache(dtype=2, d=64)) == 3                # fp8 caches: head 128 only
     assert cascade(L, cache(), cpl=4095) == 2                   # not a whole number of blocks
     assert cascade(L, cache(), cpl=-16) == 2
     assert cascade(L, cache(), cpl=6000) == 2                   # longer than max_seq_len
@@ -92,8 +97,10 @@ def test_cascade_reason_thresholds(L):
     assert "window" in r(4096, 256, 256, 32, 8, 128, window_left=100)
     assert r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_FP8_E4M3) is None
     assert r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_F16) is None
-    assert "bfloat16" in r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_F32)
-    assert "bfloat16" in r(4096, 256, 256, 32, 8, 64)
+    # supported, but the prefix pass would run on the VALU kernel
+    assert "VALU" in r(4096, 256, 256, 32, 8, 128, dtype=pagedkv.PKV_F32)
+    assert "VALU" in r(4096, 256, 256, 32, 8, 64)
+    assert "VALU" in r(4096, 256, 256, 32, 8, 256, dtype=pagedkv.PKV_F16)
     # long prefill chunks: every row recomputes the prefix on the matrix
     # cores, and the saving (a few re-reads of the prefix) does not pay for it
     assert "cost" in r(256, 8, 8 * 4096, 32, 8, 128)
