@@ -144,7 +144,25 @@ __device__ __forceinline__ float xsum16_32(float x) {
 // DT is the cache's pkv_dtype: PKV_BF16, PKV_F16 (binary16 operands and
 // output; the unscaled probabilities stay below 2^8, well inside its range)
 // or PKV_FP8_E4M3.
-template <int BS, bool PREFIX, int DT>
+// Workgroup i of a launch runs on XCD i % 8.  The query tiles (x) of one
+// stream -- a head group (y) of one sequence or prefix partition (z) --
+// read the same keys and values.  Numbering the workgroups of a z slice so
+// that each XCD takes whole streams lets one L2 serve all of a stream's
+// tiles.  Only slices of a multiple of 8 workgroups are renumbered (then
+// workgroup l of the slice runs on XCD l % 8 whatever z is); z keeps its
+// order, since the slices of one-row sequences in a varlen launch are empty.
+__device__ __forceinline__ void xcd_stream_order(int& bx, int& by) {
+  const uint32_t X = gridDim.x, n = X * gridDim.y;
+  if (n % 8 != 0) return;
+  const uint32_t l = blockIdx.x + X * blockIdx.y;
+  const uint32_t i = (l % 8) * (n / 8) + l / 8;   // stream-major item of the slice
+  by = (int)(i / X);
+  bx = (int)(i - (uint32_t)by * X);
+}
+
+// XCD_ORDER: (bx, by) are the launch's block indices, renumbered by
+// xcd_stream_order once the workgroup is known to hold prefill rows.
+template <int BS, bool PREFIX, int DT, bool XCD_ORDER = false>
 __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by, int seq,
                                               char* __restrict__ s_lds) {
   static_assert(DT == PKV_BF16 || DT == PKV_F16 || DT == PKV_FP8_E4M3, "cache dtype");
@@ -167,6 +185,7 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     L = clamp_seq_len(load_uniform_i32(a.seq_lens, seq), a.max_seq_len, a.max_blocks_per_seq, BS);
     off = L - (qe - qs);                             // absolute position of row i = i + off
   }
+  if constexpr (XCD_ORDER) xcd_stream_order(bx, by);
   const int GC = a.head_chunks_gc;                   // query heads per column group (<= 8)
   const int R = kColTiles / GC;                      // row blocks per workgroup
   const int q0 = bx * 16 * R;

@@ -1,8 +1,9 @@
 // Chunked-prefill kernel on the matrix cores: one workgroup per (query tile,
 // head group, sequence); the work itself is pf::prefill_block.  The cascade
 // prefix pass uses the same body over (query tile of the whole batch, head
-// group, prefix key partition).  DT is the cache's pkv_dtype (bfloat16,
-// binary16 or e4m3).
+// group, prefix key partition).  Both number the workgroups of a z slice so
+// that each XCD takes whole (head group, z) streams (pf::xcd_stream_order).
+// DT is the cache's pkv_dtype (bfloat16, binary16 or e4m3).
 #include "attn_mfma_prefill.h"
 
 namespace pkv {
@@ -11,13 +12,13 @@ namespace {
 template <int BS, int DT>
 __global__ void __launch_bounds__(pf::kThreads, 2) attn_mfma_prefill_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char s_lds[pf::kLdsBytes];
-  pf::prefill_block<BS, false, DT>(a, blockIdx.x, blockIdx.y, blockIdx.z + a.z_base, s_lds);
+  pf::prefill_block<BS, false, DT, true>(a, blockIdx.x, blockIdx.y, blockIdx.z + a.z_base, s_lds);
 }
 
 template <int BS, int DT>
 __global__ void __launch_bounds__(pf::kThreads, 2) attn_mfma_prefix_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char s_lds[pf::kLdsBytes];
-  pf::prefill_block<BS, true, DT>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_lds);
+  pf::prefill_block<BS, true, DT, true>(a, blockIdx.x, blockIdx.y, blockIdx.z, s_lds);
 }
 
 template <bool PREFIX, int BS, int DT>
