@@ -352,6 +352,31 @@ def test_parity_prefill_shapes(hq, hkv, bs, causal):
     G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "prefill")
 
 
+# (hq, hkv, longest chunk): the standalone prefill launch numbers the
+# workgroups of each sequence's slice (query tiles x head groups) so that
+# each XCD takes whole (head group, sequence) streams when the slice holds a
+# multiple of 8 workgroups, and keeps the grid order otherwise.  Slices of
+# 7 x 8, 2 x 8, 1 x 8, 7 x 8 (8 query heads per group) and 2 x 4 (a stream
+# over two XCDs) are renumbered; 10 x 2 and 2 x 3 are not.
+@pytest.mark.parametrize("hq,hkv,qmax", [(32, 8, 200), (8, 8, 250), (8, 8, 100), (64, 8, 100),
+                                         (16, 4, 64), (8, 2, 300), (12, 3, 33)])
+def test_parity_prefill_launch_stream_order(hq, hkv, qmax):
+    """Prefill chunks in the prefill launch of their own (call option
+    mixed_launch = 1), one-row sequences between and after them, so that
+    the launch's empty slices sit at several positions of its z axis."""
+    ctx = [40, 0, 300, 0, 77, 5]
+    ql = [qmax, 1, qmax // 2 + 3, 1, 17, 1]
+    w = W.make_varlen("prefill_order", ctx, ql, hq, hkv, 128, 16, "bf16", seed=hq * 7 + qmax,
+                      causal=True)
+    _announce(f"prefill launch stream order hq={hq} hkv={hkv} qmax={qmax}")
+    dw = G.DevWorkload(w)
+    opts = {"mixed_launch": 1}
+    G.run(dw, options=opts)
+    ref, ref_lse = G.reference(w)
+    G.assert_close(G.dev_to_f64(dw.out), ref, "bf16", f"prefill order {hq}/{hkv} q={qmax}")
+    G.lse_close(G.dev_to_f64(dw.lse), ref_lse, "prefill order")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("ps", [0, -1])
