@@ -100,6 +100,28 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t lds_addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
   return r;
 }
+// 16-byte LDS read written as inline asm, for the same reason: the compiler
+// cannot always tell a plain read of the current stage apart from the ring's
+// direct-to-LDS loads in flight, and then waits for all of them before it
+// (inside the persistent launches it did so on every tile).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128_at(uint32_t lds_addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF) : "memory");
+  return r;
+}
+// Waits until at most N LDS operations are outstanding (they complete in
+// order), then marks the K registers written so that no use of them is
+// scheduled before the wait.
+template <int N>
+__device__ __forceinline__ void lds_k_ready(u32x4 (&r)[2][4]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(r[tt][j]));
+}
 // Waits for every outstanding LDS read, then marks the registers written so
 // that no use of them is scheduled before the wait.
 template <int N>
@@ -403,31 +425,37 @@ __device__ __forceinline__ void prefill_block(const AttnArgs& a, int bx, int by,
     const int j0 = t * kTile;
     // wholly above this wave's diagonal, or below its window
     if (MASKED && (j0 > wave_last_pos || j0 + kTile - 1 < wave_first_key)) return;
-    // every LDS read of the tile issued up front: K chunks for the A
-    // operands, then the transposed V rows (waited for before the first PV
-    // product)
+    // every LDS read of the tile issued up front: the 8 K chunks for the A
+    // operands, then the 16 transposed V rows (waited for before the first PV
+    // product).  The K chunks are waited for after the first 8 V reads
+    // (lgkmcnt counts to 15).  With the stage known at compile time the
+    // reads take its offset as an immediate.
+    constexpr int KO = SO >= 0 ? SO : 0;
+    const uint32_t lbase = SO >= 0 ? (uint32_t)(uintptr_t)(lds_void*)s_lds
+                                   : (uint32_t)(uintptr_t)(lds_void*)buf;
+    u32x4 kr[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kr[0][j] = ds_read_b128_at<KO>(lbase + koff[j]);
+      kr[1][j] = ds_read_b128_at<KO + 4096>(lbase + koff[j]);
+    }
+    u32x2 vr[8][2];
+#pragma unroll
+    for (int jd = 0; jd < 4; ++jd) {
+      vr[jd][0] = ds_read_tr16_b64<KO>(lbase + voff[jd]);
+      vr[jd][1] = ds_read_tr16_b64<KO + 16 * kD * 2>(lbase + voff[jd]);
+    }
+    lds_k_ready<8>(kr);
+#pragma unroll
+    for (int jd = 4; jd < 8; ++jd) {
+      vr[jd][0] = ds_read_tr16_b64<KO>(lbase + voff[jd]);
+      vr[jd][1] = ds_read_tr16_b64<KO + 16 * kD * 2>(lbase + voff[jd]);
+    }
     x8 ka[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ka[tt][j] = H::as_x8(*reinterpret_cast<const u32x4*>(buf + koff[j] + tt * 4096));
-    u32x2 vr[8][2];
-    if constexpr (SO >= 0) {
-      const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)s_lds;
-#pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
-        vr[jd][0] = ds_read_tr16_b64<SO>(lds0 + voff[jd]);
-        vr[jd][1] = ds_read_tr16_b64<SO + 16 * kD * 2>(lds0 + voff[jd]);
-      }
-    } else {
-      const uint32_t vbase = (uint32_t)(uintptr_t)(lds_void*)buf;
-#pragma unroll
-      for (int jd = 0; jd < 8; ++jd) {
-        vr[jd][0] = ds_read_tr16_b64<0>(vbase + voff[jd]);
-        vr[jd][1] = ds_read_tr16_b64<16 * kD * 2>(vbase + voff[jd]);
-      }
-    }
+      for (int j = 0; j < 4; ++j) ka[tt][j] = H::as_x8(kr[tt][j]);
     // S^T = K Q^T for both column tiles
     f32x4 sacc[2][2];
 #pragma unroll
