@@ -42,14 +42,18 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   const int64_t n_pre = CASCADE ? (int64_t)g.pre_x * g.pre_y * g.pre_z
                                : (int64_t)load_uniform_i32(g.pre_count, 0) * g.pre_x * g.pre_y;
   const int64_t n_dec = g.n_dec;
-  // Workgroup i runs on XCD i % 8, so its start role follows its XCD: the
-  // XCDs with i % 4 < pre_share start on the first queue, the others on the
-  // decode queue.  Whole XCDs per role keep each kind's data in its own L2s,
-  // and i % 4 spreads both kinds over the two halves of the chip (XCDs 0-3
-  // and 4-7); an uneven spread, or roles mixed inside each XCD, measured
-  // slower.  A workgroup whose queue is empty moves to the other one, and
-  // stops when both are.
-  int role = (int)(blockIdx.x & 3) < g.pre_share ? 0 : 1;
+  // Start roles.  Workgroup i runs on XCD i % 8, and workgroups i and
+  // i + 8k of one XCD fill its CUs in turn, so (i / 8) % 4 classes the CUs
+  // of every XCD in four (the two workgroups of a CU, i and i + 256 on a
+  // 256-CU chip, fall in one class).  For a mixed step, the CUs of the
+  // classes below pre_share start on prefill tiles in every XCD, and the
+  // others on decode rows: both kinds then draw on every XCD's share of HBM
+  // bandwidth, and each CU keeps one kind.  For a cascade the XCDs with
+  // i % 4 < pre_share start on prefix items (whole XCDs per role).  A
+  // workgroup whose queue is empty moves to the other one, and stops when
+  // both are.
+  int role = CASCADE ? ((int)(blockIdx.x & 3) < g.pre_share ? 0 : 1)
+                     : ((int)((blockIdx.x >> 3) & 3) < g.pre_share ? 0 : 1);
   bool switched = false;
   while (true) {
     __syncthreads();                       // the previous item's LDS use is over
