@@ -351,13 +351,11 @@ int32_t device_cus() {
   return attr;
 }
 
-// XCDs in four (by workgroup index) that start the mixed launch on prefill
-// tiles: 2 over a bfloat16 cache, 3 over an fp8 one (of 1-4 tried, with
-// roles per XCD or inside each XCD).  Over an fp8 cache the prefill tiles
-// also convert their codes and the decode rows move half the bytes, so more
-// of the chip starts on prefill (4 chunks of 512 rows beside 128 decode rows,
-// over an fp8 cache: 250 us, against 262 us in two launches and 285 us with
-// 2 XCDs in four).
+// CU classes in four (of every XCD) that start the mixed launch on prefill
+// tiles: 2 over a 16-bit cache, 3 over an fp8 one (of 1-4 tried).  Over an
+// fp8 cache the prefill tiles also convert their codes and the decode rows
+// move half the bytes, so more of the chip starts on prefill (4 chunks of
+// 512 rows beside 128 decode rows: 2 in four was 10-20 % slower there).
 constexpr int32_t kMixedShare = 2;
 constexpr int32_t kMixedShareFp8 = 3;
 

@@ -139,7 +139,8 @@ struct MixedGrid {
   int64_t n_dec;                   // decode items: dec_x * dec_y * dec_z
   int32_t pre_x, pre_y;            // prefill items per listed sequence: query tiles x head groups
   int32_t pre_z;                   // cascade: prefix partitions (items = pre_x * pre_y * pre_z)
-  int32_t pre_share;               // XCDs in four (workgroup index % 4) that start on the first queue
+  int32_t pre_share;               // in four, the CU classes ((index / 8) % 4; mixed step) or XCDs
+                                   // (index % 4; cascade) that start on the first queue
   int32_t dec_x, dec_y, dec_z;     // kv-head chunks, row items, key ranges
   int32_t workgroups;              // persistent grid size
   const int32_t* pre_list;         // [num_seqs] multi-row sequences (planner)
