@@ -55,9 +55,24 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   int role = CASCADE ? ((int)(blockIdx.x & 3) < g.pre_share ? 0 : 1)
                      : ((int)((blockIdx.x >> 3) & 3) < g.pre_share ? 0 : 1);
   bool switched = false;
+  // Mixed step: a workgroup that starts on prefill takes its first item by
+  // its rank among those workgroups (the first pre_share CU classes of every
+  // whole group of 32), so that the first round of prefill items follows
+  // the dispatch order rather than the order of arrival at the queue;
+  // later items come from the queue, offset by the number of ranked
+  // workgroups.  (A prefill-only batch: 137.9 -> 132.6 us per call.)
+  const uint32_t whole = gridDim.x / 32 * 32;
+  const int n_first = CASCADE ? 0 : (int)(whole / 32) * 8 * g.pre_share;
+  int first = -1;
+  if (!CASCADE && role == 0 && blockIdx.x < whole)
+    first = (int)(blockIdx.x / 32) * 8 * g.pre_share + (int)(blockIdx.x % 32);
   while (true) {
     __syncthreads();                       // the previous item's LDS use is over
-    if (threadIdx.x == 0) s_item = atomicAdd(&g.queues[role], 1);
+    if (threadIdx.x == 0) {
+      if (first >= 0) s_item = first;
+      else s_item = atomicAdd(&g.queues[role], 1) + (role == 0 ? n_first : 0);
+    }
+    first = -1;
     __syncthreads();
     const int64_t item = s_item;
     if (item >= (role == 0 ? n_pre : n_dec)) {
