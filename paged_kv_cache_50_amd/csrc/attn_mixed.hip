@@ -57,15 +57,24 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   bool switched = false;
   // Mixed step: a workgroup that starts on prefill takes its first item by
   // its rank among those workgroups (the first pre_share CU classes of every
-  // whole group of 32), so that the first round of prefill items follows
-  // the dispatch order rather than the order of arrival at the queue;
-  // later items come from the queue, offset by the number of ranked
-  // workgroups.  (A prefill-only batch: 137.9 -> 132.6 us per call.)
+  // whole group of 32: n_first of them, n_first / 8 on each XCD) instead of
+  // by its order of arrival at the queue; later items come from the queue,
+  // offset by n_first.  When a whole number of streams (the query tiles of
+  // one head group of one chunk) fits each XCD's share, the streams are
+  // dealt over the XCDs, whole: the tiles of a stream then share one L2,
+  // and every XCD gets streams of every chunk.  Otherwise the first items
+  // follow the ranks.
   const uint32_t whole = gridDim.x / 32 * 32;
   const int n_first = CASCADE ? 0 : (int)(whole / 32) * 8 * g.pre_share;
   int first = -1;
-  if (!CASCADE && role == 0 && blockIdx.x < whole)
-    first = (int)(blockIdx.x / 32) * 8 * g.pre_share + (int)(blockIdx.x % 32);
+  if (!CASCADE && role == 0 && blockIdx.x < whole) {
+    const int per_xcd = n_first / 8;
+    const int j = (int)(blockIdx.x / 32) * g.pre_share + (int)((blockIdx.x % 32) / 8);
+    if (per_xcd % g.pre_x == 0)
+      first = ((int)(blockIdx.x % 8) + 8 * (j / g.pre_x)) * g.pre_x + j % g.pre_x;
+    else
+      first = (int)(blockIdx.x / 32) * 8 * g.pre_share + (int)(blockIdx.x % 32);
+  }
   while (true) {
     __syncthreads();                       // the previous item's LDS use is over
     if (threadIdx.x == 0) {
