@@ -65,8 +65,25 @@ __global__ void __launch_bounds__(dec::kThreads, 2) attn_mixed_kernel(const Attn
   // and every XCD gets streams of every chunk.  Otherwise the first items
   // follow the ranks.
   const uint32_t whole = gridDim.x / 32 * 32;
-  const int n_first = CASCADE ? 0 : (int)(whole / 32) * 8 * g.pre_share;
+  int n_first = CASCADE ? 0 : (int)(whole / 32) * 8 * g.pre_share;
   int first = -1;
+  if (CASCADE && gridDim.x % 8 == 0) {
+    // Cascade: the workgroups of the XCDs that start on prefix items
+    // (x % 4 < pre_share, 2 * pre_share XCDs, gridDim.x / 8 workgroups on
+    // each) take their first item by rank in the same way, whole streams
+    // (the query tiles of one head group and prefix partition) dealt over
+    // those XCDs when they fit, else in rank order.
+    const int nx = 2 * g.pre_share;
+    const int per_xcd = (int)(gridDim.x / 8);
+    n_first = nx * per_xcd;
+    const int x = (int)(blockIdx.x % 8);
+    if ((x & 3) < g.pre_share) {
+      const int xr = (x >> 2) * g.pre_share + (x & 3);
+      const int j = (int)(blockIdx.x / 8);
+      first = per_xcd % g.pre_x == 0 ? (xr + nx * (j / g.pre_x)) * g.pre_x + j % g.pre_x
+                                     : j * nx + xr;
+    }
+  }
   if (!CASCADE && role == 0 && blockIdx.x < whole) {
     const int per_xcd = n_first / 8;
     const int j = (int)(blockIdx.x / 32) * g.pre_share + (int)((blockIdx.x % 32) / 8);
