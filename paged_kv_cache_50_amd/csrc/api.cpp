@@ -131,9 +131,13 @@ int64_t block_stride_elems(const pkv_kv_cache* c) {
 }
 
 // Decode kernel choice.  The matrix-core kernel pays off once a kv head
-// serves several query heads (a dense g x tokens contraction); with one query
-// head per kv head the work is a matrix-vector product and stays on the VALU.
-// A call's options may force either variant (A/B measurements).
+// serves several query heads (a dense g x tokens contraction).  At head size
+// 128 it is also the faster gather with one query head per kv head, where
+// the contraction is a matrix-vector product: 64 sequences x 32 heads of up
+// to 4096 tokens, bfloat16, ran in 334.7-335.2 us against 341.1-341.3 us on
+// the VALU kernel (one host, three runs each).  At head size 256 the VALU
+// kernel keeps groups below kMfmaMinGroup.  A call's options may force either
+// variant (A/B measurements).
 constexpr int kMfmaMinGroup = 4;
 constexpr int32_t kPlanMinSeqs = 64;
 constexpr int kMfmaTokensPerWg = 2048;
@@ -145,7 +149,7 @@ bool use_mfma_decode(const pkv_kv_cache* c, int group, const Choice& ch) {
   if (!is16(c->dtype) || (c->head_size != 128 && c->head_size != 256)) return false;
   if (ch.decode_kernel == 1) return false;
   if (ch.decode_kernel == 2) return true;
-  return group >= kMfmaMinGroup;
+  return group >= kMfmaMinGroup || c->head_size == 128;
 }
 
 // Prefill kernel choice: the matrix-core kernel for bfloat16, binary16 or

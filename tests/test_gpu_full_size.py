@@ -40,7 +40,7 @@ def _announce(msg):
 # apart from the split merge, which a split batch launches unless every row's
 # partitions fall to one workgroup.
 EXPECTED = {
-    2: pagedkv.RAN_DECODE_VALU,
+    2: pagedkv.RAN_PLANNER | pagedkv.RAN_DECODE_MFMA,
     3: pagedkv.RAN_PLANNER | pagedkv.RAN_DECODE_MFMA,
     4: pagedkv.RAN_DECODE_MFMA,
     5: pagedkv.RAN_PLANNER | pagedkv.RAN_MIXED,

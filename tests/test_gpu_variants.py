@@ -50,9 +50,9 @@ def _check(w, dw, opts, want, ps, what, key_span=None):
 CASES = [
     # (workload, shrink kwargs, partition_size, options, expected kernels other
     # than the split merge)
-    (2, dict(num_seqs=6, max_len=1500), 0, {}, P.RAN_DECODE_VALU),
-    (2, dict(num_seqs=6, max_len=1500), 0, dict(decode_kernel=2),
-     P.RAN_DECODE_MFMA),
+    (2, dict(num_seqs=6, max_len=1500), 0, {}, P.RAN_DECODE_MFMA),
+    (2, dict(num_seqs=6, max_len=1500), 0, dict(decode_kernel=1),
+     P.RAN_DECODE_VALU),
     (2, dict(num_seqs=6, max_len=1500), -1, dict(decode_kernel=2), P.RAN_DECODE_MFMA),
     (3, dict(num_seqs=70, max_len=1200), 0, {},
      P.RAN_PLANNER | P.RAN_DECODE_MFMA),
